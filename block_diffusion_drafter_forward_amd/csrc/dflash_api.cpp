@@ -1,0 +1,532 @@
+// Host side of the C ABI declared in include/dflash.h: argument validation (done entirely before any HIP
+// call, so every error path can be exercised without a GPU), workspace planning, the launch sequence of the
+// drafter pass and of KV injection, and optional per-kernel event timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "dflash.h"
+#include "kernels.h"
+
+using namespace df;
+
+// ---------------------------------------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------------------------------------
+static thread_local char g_err[512] = "";
+
+static int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+extern "C" const char* dflash_last_error(void) { return g_err; }
+
+#define HIP_TRY(expr)                                                                          \
+    do {                                                                                       \
+        hipError_t e_ = (expr);                                                                \
+        if (e_ != hipSuccess) return fail(DFLASH_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+// ---------------------------------------------------------------------------------------------------------
+// handle
+// ---------------------------------------------------------------------------------------------------------
+struct ProfEntry {
+    std::string name;
+    hipEvent_t start, stop;
+};
+
+struct dflash_handle {
+    dflash_config cfg;
+    dflash_weights w;
+    std::vector<dflash_layer_weights> layers;
+    RopeFreq rf;
+    bool profiling = false;
+    std::vector<hipEvent_t> event_pool;
+    std::vector<ProfEntry> pending;
+};
+
+static bool is_bf16(const dflash_config& c) { return c.dtype == DFLASH_BF16; }
+static size_t elt(const dflash_config& c) { return is_bf16(c) ? 2 : 4; }
+
+static int validate_config(const dflash_config* c) {
+    if (!c) return fail(DFLASH_E_ARG, "config is NULL");
+    if (c->n_layers < 1 || c->hidden < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 2 ||
+        c->ffn < 1 || c->vocab < 1 || c->feat_dim < 1)
+        return fail(DFLASH_E_ARG, "config sizes must be positive");
+    if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return fail(DFLASH_E_ARG, "unknown dtype %d", c->dtype);
+    if (c->n_q_heads % c->n_kv_heads) return fail(DFLASH_E_SHAPE, "n_q_heads %% n_kv_heads != 0");
+    if (c->n_q_heads / c->n_kv_heads > 8) return fail(DFLASH_E_UNSUPPORTED, "more than 8 query heads per KV head");
+    if (c->block_len < 2 || c->block_len > 16) return fail(DFLASH_E_UNSUPPORTED, "block_len must be in [2, 16]");
+    if (c->page_size != 16) return fail(DFLASH_E_UNSUPPORTED, "page_size must be 16");
+    if (!(c->rms_eps >= 0.f) || !(c->rope_theta >= 0.f)) return fail(DFLASH_E_ARG, "rms_eps and rope_theta must be >= 0");
+    const int qd = c->n_q_heads * c->head_dim;
+    if (is_bf16(*c)) {
+        if (c->head_dim != 128) return fail(DFLASH_E_UNSUPPORTED, "bf16 kernels need head_dim 128");
+        if (c->hidden % 256 || c->ffn % 256 || c->feat_dim % 256 || qd % 256)
+            return fail(DFLASH_E_UNSUPPORTED, "bf16 kernels need hidden, ffn, feat_dim, n_q*d multiples of 256");
+    } else {
+        if (c->head_dim % 2 || c->head_dim > 128) return fail(DFLASH_E_UNSUPPORTED, "f32 kernels need even head_dim <= 128");
+        if (c->hidden % 4 || c->ffn % 4 || c->feat_dim % 4 || qd % 4)
+            return fail(DFLASH_E_UNSUPPORTED, "f32 kernels need hidden, ffn, feat_dim, n_q*d multiples of 4");
+    }
+    return DFLASH_OK;
+}
+
+extern "C" int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_handle** out) {
+    if (!out) return fail(DFLASH_E_ARG, "out is NULL");
+    *out = nullptr;
+    int rc = validate_config(cfg);
+    if (rc) return rc;
+    if (!w || !w->layers) return fail(DFLASH_E_ARG, "weights or weights->layers is NULL");
+    if (!w->fc_w || !w->embed || !w->final_norm || !w->lm_head) return fail(DFLASH_E_ARG, "a global weight is NULL");
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const dflash_layer_weights& L = w->layers[l];
+        if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.uk || !L.uv || !L.ffn_norm || !L.w_gate ||
+            !L.w_up || !L.w_down)
+            return fail(DFLASH_E_ARG, "a weight of layer %d is NULL", l);
+    }
+    dflash_handle* h = new dflash_handle();
+    h->cfg = *cfg;
+    h->layers.assign(w->layers, w->layers + cfg->n_layers);
+    h->w = *w;
+    h->w.layers = h->layers.data();
+    std::memset(&h->rf, 0, sizeof(h->rf));
+    h->rf.on = cfg->rope_theta > 0.f;
+    for (int i = 0; i < cfg->head_dim / 2; ++i)
+        h->rf.inv[i] = h->rf.on ? (float)std::pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim) : 0.f;
+    *out = h;
+    return DFLASH_OK;
+}
+
+extern "C" void dflash_destroy(dflash_handle* h) {
+    if (!h) return;
+    for (auto& p : h->pending) {
+        h->event_pool.push_back(p.start);
+        h->event_pool.push_back(p.stop);
+    }
+    for (hipEvent_t e : h->event_pool) (void)hipEventDestroy(e);
+    delete h;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// profiling
+// ---------------------------------------------------------------------------------------------------------
+static hipEvent_t take_event(dflash_handle* h) {
+    if (!h->event_pool.empty()) {
+        hipEvent_t e = h->event_pool.back();
+        h->event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+struct Timed {
+    dflash_handle* h;
+    hipStream_t st;
+    ProfEntry e{};
+    bool on;
+    Timed(dflash_handle* h_, const char* name, hipStream_t s) : h(h_), st(s), on(h_ && h_->profiling) {
+        if (!on) return;
+        e.name = name;
+        e.start = take_event(h);
+        e.stop = take_event(h);
+        if (e.start) (void)hipEventRecord(e.start, st);
+    }
+    ~Timed() {
+        if (!on) return;
+        if (e.stop) (void)hipEventRecord(e.stop, st);
+        if (e.start && e.stop) h->pending.push_back(e);
+    }
+};
+
+extern "C" int dflash_profile_enable(dflash_handle* h, int on) {
+    if (!h) return fail(DFLASH_E_ARG, "handle is NULL");
+    h->profiling = on != 0;
+    return DFLASH_OK;
+}
+
+extern "C" int dflash_profile_collect(dflash_handle* h, dflash_kernel_stat* out, int max_entries) {
+    if (!h) return fail(DFLASH_E_ARG, "handle is NULL");
+    if (max_entries > 0 && !out) return fail(DFLASH_E_ARG, "out is NULL");
+    std::map<std::string, std::pair<int, double>> acc;
+    std::vector<std::string> order;
+    for (auto& p : h->pending) {
+        HIP_TRY(hipEventSynchronize(p.stop));
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, p.start, p.stop));
+        if (!acc.count(p.name)) order.push_back(p.name);
+        acc[p.name].first += 1;
+        acc[p.name].second += ms;
+        h->event_pool.push_back(p.start);
+        h->event_pool.push_back(p.stop);
+    }
+    h->pending.clear();
+    int n = 0;
+    for (auto& name : order) {
+        if (n >= max_entries) break;
+        std::memset(&out[n], 0, sizeof(out[n]));
+        std::snprintf(out[n].name, sizeof(out[n].name), "%s", name.c_str());
+        out[n].launches = acc[name].first;
+        out[n].total_ms = acc[name].second;
+        ++n;
+    }
+    return n;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// workspace planning
+// ---------------------------------------------------------------------------------------------------------
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Carve {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    }
+};
+
+struct DraftPlan {
+    int M;
+    GemmPlan qkv, oproj, gateup, down;
+    AttnPlan attn;
+    size_t err, h, u, q, kb, vbt, o, a, part, opart, ml, hpart, total;
+};
+
+static DraftPlan plan_draft(const dflash_config& c, int batch, int max_ctx) {
+    DraftPlan p{};
+    const int bf = is_bf16(c);
+    const int M = batch * c.block_len;
+    const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    const size_t E = elt(c);
+    p.M = M;
+    p.qkv = plan_gemm(bf, M, qd + 2 * kvd, c.hidden);
+    p.oproj = plan_gemm(bf, M, c.hidden, qd);
+    p.gateup = plan_gemm(bf, M, 2 * c.ffn, c.hidden);
+    p.down = plan_gemm(bf, M, c.hidden, c.ffn);
+    p.attn = plan_attention(batch, c.n_kv_heads, max_ctx);
+    size_t part = (size_t)p.qkv.splits * M * (qd + 2 * kvd);
+    part = std::max(part, (size_t)p.oproj.splits * M * c.hidden);
+    part = std::max(part, (size_t)p.gateup.splits * M * 2 * c.ffn);
+    part = std::max(part, (size_t)p.down.splits * M * c.hidden);
+    Carve cv;
+    p.err = cv.take(256);
+    p.h = cv.take((size_t)M * c.hidden * 4);
+    p.u = cv.take((size_t)M * c.hidden * E);
+    p.q = cv.take((size_t)M * qd * E);
+    p.kb = cv.take((size_t)batch * kvd * 16 * E);
+    p.vbt = cv.take((size_t)batch * kvd * 16 * E);
+    p.o = cv.take((size_t)M * qd * E);
+    p.a = cv.take((size_t)M * c.ffn * E);
+    p.part = cv.take(part * 4);
+    const size_t C1 = (size_t)p.attn.n_chunks + 1;
+    if (bf) {
+        p.opart = cv.take((size_t)batch * c.n_q_heads * C1 * 16 * c.head_dim * 4);
+        p.ml = cv.take((size_t)batch * c.n_q_heads * C1 * 16 * 2 * 4);
+    } else {
+        p.opart = cv.take((size_t)M * qd * 4);
+        p.ml = cv.take(0);
+    }
+    p.hpart = cv.take(head_partial_floats(c.vocab, M) * 4);
+    p.total = cv.off;
+    return p;
+}
+
+static bool draft_shape_ok(const dflash_config& c, int batch) {
+    const int M = batch * c.block_len;
+    return M <= 32;  // the fused LM head keeps at most 32 block rows per workgroup
+}
+
+extern "C" size_t dflash_draft_workspace_bytes(const dflash_handle* h, int max_batch, int max_ctx) {
+    if (!h || max_batch < 1 || max_ctx < 0) return 0;
+    return plan_draft(h->cfg, max_batch, max_ctx).total;
+}
+
+#define INJECT_ROWS 4096  // rows per internal chunk of dflash_inject_ctx (bounds the workspace)
+#define MAX_LAYERS_PER_KV_GEMM (DF_MAX_SEG / 2)
+
+struct InjectPlan {
+    int rows;
+    size_t err, f, part, total;
+};
+
+static InjectPlan plan_inject(const dflash_config& c, int n_rows) {
+    InjectPlan p{};
+    const int bf = is_bf16(c);
+    const int R = n_rows < INJECT_ROWS ? n_rows : INJECT_ROWS;
+    p.rows = R;
+    const int kvd = c.n_kv_heads * c.head_dim;
+    const int nl = c.n_layers < MAX_LAYERS_PER_KV_GEMM ? c.n_layers : MAX_LAYERS_PER_KV_GEMM;
+    GemmPlan fc = plan_gemm(bf, R, c.hidden, c.feat_dim);
+    GemmPlan kv = plan_gemm(bf, R, nl * 2 * kvd, c.hidden);
+    size_t part = std::max((size_t)fc.splits * R * c.hidden, (size_t)kv.splits * R * nl * 2 * kvd);
+    Carve cv;
+    p.err = cv.take(256);
+    p.f = cv.take((size_t)R * c.hidden * elt(c));
+    p.part = cv.take(part * 4);
+    p.total = cv.off;
+    return p;
+}
+
+extern "C" size_t dflash_inject_workspace_bytes(const dflash_handle* h, int max_rows) {
+    if (!h || max_rows < 1) return 0;
+    // the plan of the largest chunk bounds every chunk (smaller chunks need no more)
+    return plan_inject(h->cfg, max_rows).total;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// dflash_draft_block
+// ---------------------------------------------------------------------------------------------------------
+static Segs segs1(const void* p, int n) {
+    Segs s{};
+    s.ptr[0] = p;
+    s.start[0] = 0;
+    s.start[1] = n;
+    s.n = 1;
+    return s;
+}
+
+extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* block_tokens, const int32_t* ctx_len,
+                                  const int32_t* page_table, int max_pages, const dflash_kv* kv, int max_ctx,
+                                  int top_k, int32_t* tokens, int32_t* topk_ids, float* topk_logprobs,
+                                  const dflash_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
+    if (!h) return fail(DFLASH_E_ARG, "handle is NULL");
+    const dflash_config& c = h->cfg;
+    if (batch < 1) return fail(DFLASH_E_ARG, "batch must be >= 1");
+    if (!block_tokens || !ctx_len || !tokens || !ws) return fail(DFLASH_E_ARG, "a required pointer is NULL");
+    if (top_k < 0 || top_k > DF_TOPK) return fail(DFLASH_E_UNSUPPORTED, "top_k must be in [0, 8]");
+    if (top_k > c.vocab) return fail(DFLASH_E_ARG, "top_k exceeds the vocabulary");
+    if (top_k > 0 && (!topk_ids || !topk_logprobs)) return fail(DFLASH_E_ARG, "top-k outputs are NULL");
+    if (max_ctx < 0) return fail(DFLASH_E_ARG, "max_ctx must be >= 0");
+    if (max_ctx > 0) {
+        if (!page_table || !kv || !kv->k || !kv->v) return fail(DFLASH_E_ARG, "page table or KV pool is NULL");
+        if (max_pages < 1 || kv->n_pages < 1) return fail(DFLASH_E_ARG, "max_pages and n_pages must be >= 1");
+        if ((long long)max_ctx > (long long)max_pages * c.page_size)
+            return fail(DFLASH_E_CAPACITY, "max_ctx %d exceeds max_pages * page_size", max_ctx);
+    }
+    if (!draft_shape_ok(c, batch))
+        return fail(DFLASH_E_UNSUPPORTED, "batch * block_len = %d > 32 is not supported yet", batch * c.block_len);
+    const DraftPlan p = plan_draft(c, batch, max_ctx);
+    if (ws_bytes < p.total) return fail(DFLASH_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, p.total);
+    if (((uintptr_t)ws) & 255) return fail(DFLASH_E_ARG, "workspace must be 256-byte aligned");
+
+    hipStream_t st = (hipStream_t)stream;
+    char* W = (char*)ws;
+    uint32_t* err = (uint32_t*)(W + p.err);
+    float* hbuf = (float*)(W + p.h);
+    void* u = W + p.u;
+    void* q = W + p.q;
+    void* kb = W + p.kb;
+    void* vbt = W + p.vbt;
+    void* o = W + p.o;
+    void* a = W + p.a;
+    float* part = (float*)(W + p.part);
+    float* opart = (float*)(W + p.opart);
+    float* ml = (float*)(W + p.ml);
+    float* hpart = (float*)(W + p.hpart);
+    const int bf = is_bf16(c);
+    const int M = p.M, H = c.hidden, L = c.block_len;
+    const int nq = c.n_q_heads, nkv = c.n_kv_heads, d = c.head_dim;
+    const int qd = nq * d, kvd = nkv * d;
+    const size_t tap_stride = (size_t)M * H;
+    float* tap = dbg ? dbg->hidden : nullptr;
+    const void* kpool = kv ? kv->k : nullptr;
+    const void* vpool = kv ? kv->v : nullptr;
+    const int n_pages = kv ? kv->n_pages : 0;
+
+    {
+        Timed t(h, "embed_norm", st);
+        HIP_TRY(launch_embed_norm(bf, block_tokens, M, c.vocab, h->w.embed, h->layers[0].attn_norm, H, c.rms_eps, hbuf,
+                                  u, tap, err, st));
+    }
+    for (int l = 0; l < c.n_layers; ++l) {
+        const dflash_layer_weights& lw = h->layers[l];
+        Segs sq{};
+        sq.ptr[0] = lw.wq; sq.ptr[1] = lw.wk; sq.ptr[2] = lw.wv;
+        sq.start[0] = 0; sq.start[1] = qd; sq.start[2] = qd + kvd; sq.start[3] = qd + 2 * kvd;
+        sq.n = 3;
+        {
+            Timed t(h, gemm_kernel_name(p.qkv), st);
+            HIP_TRY(launch_gemm(p.qkv, u, H, M, sq, qd + 2 * kvd, H, part, st));
+        }
+        {
+            Timed t(h, "qkv_epilogue", st);
+            HIP_TRY(launch_qkv_epilogue(bf, part, p.qkv.splits, batch, L, nq, nkv, d, ctx_len, h->rf, q, kb, vbt, st));
+        }
+        {
+            Timed t(h, bf ? "attn_bf16" : "attn_f32", st);
+            HIP_TRY(launch_attention(bf, p.attn, batch, L, nq, nkv, d, q, kb, vbt, kpool, vpool, l, n_pages, page_table,
+                                     max_pages, ctx_len, max_ctx, opart, ml, err, st));
+        }
+        const void* attn_out = opart;
+        if (bf) {
+            Timed t(h, "attn_merge", st);
+            HIP_TRY(launch_attn_merge(bf, p.attn, batch, L, nq, d, opart, ml, o, st));
+            attn_out = o;
+        }
+        {
+            Timed t(h, gemm_kernel_name(p.oproj), st);
+            HIP_TRY(launch_gemm(p.oproj, attn_out, qd, M, segs1(lw.wo, H), H, qd, part, st));
+        }
+        {
+            Timed t(h, "resid_norm", st);
+            HIP_TRY(launch_resid_norm(bf, part, p.oproj.splits, M, H, hbuf, lw.ffn_norm, c.rms_eps, u, nullptr, st));
+        }
+        Segs sg{};
+        sg.ptr[0] = lw.w_gate; sg.ptr[1] = lw.w_up;
+        sg.start[0] = 0; sg.start[1] = c.ffn; sg.start[2] = 2 * c.ffn;
+        sg.n = 2;
+        {
+            Timed t(h, gemm_kernel_name(p.gateup), st);
+            HIP_TRY(launch_gemm(p.gateup, u, H, M, sg, 2 * c.ffn, H, part, st));
+        }
+        {
+            Timed t(h, "swiglu", st);
+            HIP_TRY(launch_swiglu(bf, part, p.gateup.splits, M, c.ffn, a, st));
+        }
+        {
+            Timed t(h, gemm_kernel_name(p.down), st);
+            HIP_TRY(launch_gemm(p.down, a, c.ffn, M, segs1(lw.w_down, H), H, c.ffn, part, st));
+        }
+        {
+            const void* next_gain = l + 1 < c.n_layers ? h->layers[l + 1].attn_norm : h->w.final_norm;
+            Timed t(h, "resid_norm", st);
+            HIP_TRY(launch_resid_norm(bf, part, p.down.splits, M, H, hbuf, next_gain, c.rms_eps, u,
+                                      tap ? tap + (l + 1) * tap_stride : nullptr, st));
+        }
+    }
+    {
+        Timed t(h, bf ? "lm_head_bf16" : "lm_head_f32", st);
+        HIP_TRY(launch_lm_head(bf, u, M, h->w.lm_head, c.vocab, H, hpart, dbg ? dbg->logits : nullptr, st));
+    }
+    {
+        Timed t(h, "head_merge", st);
+        HIP_TRY(launch_head_merge(M, c.vocab, top_k, hpart, block_tokens, tokens, topk_ids, topk_logprobs, err, st));
+    }
+    return DFLASH_OK;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// dflash_inject_ctx
+// ---------------------------------------------------------------------------------------------------------
+extern "C" int dflash_inject_ctx(dflash_handle* h, int batch, int n_rows, const void* feats, int64_t feat_row_stride,
+                                 const int32_t* row_offsets, const int32_t* start_pos, const int32_t* page_table,
+                                 int max_pages, const dflash_kv* kv, void* ws, size_t ws_bytes, void* stream) {
+    if (!h) return fail(DFLASH_E_ARG, "handle is NULL");
+    const dflash_config& c = h->cfg;
+    if (batch < 1 || n_rows < 1) return fail(DFLASH_E_ARG, "batch and n_rows must be >= 1");
+    if (!feats || !row_offsets || !start_pos || !page_table || !kv || !kv->k || !kv->v || !ws)
+        return fail(DFLASH_E_ARG, "a required pointer is NULL");
+    if (feat_row_stride < c.feat_dim) return fail(DFLASH_E_ARG, "feat_row_stride < feat_dim");
+    if (is_bf16(c) ? (feat_row_stride % 8) : (feat_row_stride % 4))
+        return fail(DFLASH_E_ARG, "feat_row_stride must keep rows 16-byte aligned");
+    if (max_pages < 1 || kv->n_pages < 1) return fail(DFLASH_E_ARG, "max_pages and n_pages must be >= 1");
+    const InjectPlan p = plan_inject(c, n_rows);
+    if (ws_bytes < p.total) return fail(DFLASH_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, p.total);
+    if (((uintptr_t)ws) & 255) return fail(DFLASH_E_ARG, "workspace must be 256-byte aligned");
+
+    hipStream_t st = (hipStream_t)stream;
+    const int bf = is_bf16(c);
+    char* W = (char*)ws;
+    uint32_t* err = (uint32_t*)(W + p.err);
+    void* f = W + p.f;
+    float* part = (float*)(W + p.part);
+    const int H = c.hidden, kvd = c.n_kv_heads * c.head_dim;
+    const size_t E = elt(c);
+    {
+        Timed t(h, "clear_err", st);
+        HIP_TRY(launch_clear_err(err, st));
+    }
+    for (int row0 = 0; row0 < n_rows; row0 += p.rows) {
+        const int R = std::min(p.rows, n_rows - row0);
+        const char* x = (const char*)feats + (size_t)row0 * feat_row_stride * E;
+        const GemmPlan fc = plan_gemm(bf, R, H, c.feat_dim);
+        {
+            Timed t(h, gemm_kernel_name(fc), st);
+            HIP_TRY(launch_gemm(fc, x, (int)feat_row_stride, R, segs1(h->w.fc_w, H), H, c.feat_dim, part, st));
+        }
+        {
+            Timed t(h, "fuse_cast", st);
+            HIP_TRY(launch_reduce_cast(bf, part, fc.splits, R, H, h->w.fc_b, f, st));
+        }
+        for (int l0 = 0; l0 < c.n_layers; l0 += MAX_LAYERS_PER_KV_GEMM) {
+            const int nl = std::min(MAX_LAYERS_PER_KV_GEMM, c.n_layers - l0);
+            Segs s{};
+            for (int i = 0; i < nl; ++i) {
+                s.ptr[2 * i] = h->layers[l0 + i].uk;
+                s.ptr[2 * i + 1] = h->layers[l0 + i].uv;
+                s.start[2 * i] = 2 * i * kvd;
+                s.start[2 * i + 1] = (2 * i + 1) * kvd;
+            }
+            s.start[2 * nl] = 2 * nl * kvd;
+            s.n = 2 * nl;
+            const GemmPlan kp = plan_gemm(bf, R, 2 * nl * kvd, H);
+            {
+                Timed t(h, gemm_kernel_name(kp), st);
+                HIP_TRY(launch_gemm(kp, f, H, R, s, 2 * nl * kvd, H, part, st));
+            }
+            {
+                Timed t(h, "kv_scatter", st);
+                HIP_TRY(launch_kv_scatter(bf, part, kp.splits, R, row0, l0, nl, c.n_kv_heads, c.head_dim, batch,
+                                          row_offsets, start_pos, page_table, max_pages, kv->n_pages, kv->k, kv->v,
+                                          h->rf, err, st));
+            }
+        }
+    }
+    return DFLASH_OK;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// dflash_accept_len, building blocks
+// ---------------------------------------------------------------------------------------------------------
+extern "C" int dflash_accept_len(int batch, int n_draft, const int32_t* draft, int64_t draft_stride,
+                                 const int32_t* target, int64_t target_stride, int32_t* tau, void* stream) {
+    if (batch < 1 || n_draft < 0) return fail(DFLASH_E_ARG, "batch must be >= 1 and n_draft >= 0");
+    if (!draft || !target || !tau) return fail(DFLASH_E_ARG, "a required pointer is NULL");
+    if (draft_stride < n_draft || target_stride < n_draft) return fail(DFLASH_E_ARG, "stride smaller than n_draft");
+    HIP_TRY(launch_accept(batch, n_draft, draft, draft_stride, target, target_stride, tau, (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
+extern "C" size_t dflash_linear_workspace_bytes(int dtype, int M, int N, int K) {
+    if ((dtype != DFLASH_F32 && dtype != DFLASH_BF16) || M < 1 || N < 1 || K < 1) return 0;
+    const GemmPlan p = plan_gemm(dtype == DFLASH_BF16, M, N, K);
+    return align256((size_t)p.splits * M * N * 4);
+}
+
+extern "C" int dflash_linear(int dtype, int M, int N, int K, const void* x, int64_t ldx, const void* w, float* y,
+                             void* ws, size_t ws_bytes, void* stream) {
+    if (dtype != DFLASH_F32 && dtype != DFLASH_BF16) return fail(DFLASH_E_ARG, "unknown dtype");
+    if (M < 1 || N < 1 || K < 1) return fail(DFLASH_E_ARG, "sizes must be positive");
+    if (!x || !w || !y || !ws) return fail(DFLASH_E_ARG, "a required pointer is NULL");
+    if (ldx < K) return fail(DFLASH_E_ARG, "ldx < K");
+    if (dtype == DFLASH_BF16 && (K % 256 || ldx % 8)) return fail(DFLASH_E_UNSUPPORTED, "bf16 needs K % 256 == 0");
+    if (dtype == DFLASH_F32 && (K % 4 || ldx % 4)) return fail(DFLASH_E_UNSUPPORTED, "f32 needs K % 4 == 0");
+    if (ws_bytes < dflash_linear_workspace_bytes(dtype, M, N, K)) return fail(DFLASH_E_CAPACITY, "workspace too small");
+    const GemmPlan p = plan_gemm(dtype == DFLASH_BF16, M, N, K);
+    hipStream_t st = (hipStream_t)stream;
+    HIP_TRY(launch_gemm(p, x, (int)ldx, M, segs1(w, N), N, K, (float*)ws, st));
+    HIP_TRY(launch_reduce_cast(0, (float*)ws, p.splits, M, N, nullptr, y, st));
+    return DFLASH_OK;
+}
+
+extern "C" int dflash_copy(void* dst, const void* src, size_t n_bytes, void* stream) {
+    if (!dst || !src) return fail(DFLASH_E_ARG, "a required pointer is NULL");
+    if ((n_bytes & 15) || (((uintptr_t)dst | (uintptr_t)src) & 15))
+        return fail(DFLASH_E_ARG, "n_bytes and pointers must be multiples of 16");
+    HIP_TRY(launch_copy(dst, src, n_bytes / 16, (hipStream_t)stream));
+    return DFLASH_OK;
+}

@@ -1,0 +1,337 @@
+// Row-wise kernels around the GEMMs: embedding + RMSNorm, split-K reduction + residual + RMSNorm, the QKV
+// epilogue (RoPE and block K/V layouts), SwiGLU, fused-feature rounding, the paged K/V scatter of the
+// injected context, and greedy acceptance.  All of them are bandwidth-trivial next to the weight streams;
+// they exist to keep every reduction in a fixed order and every stored tensor in its final layout.
+#include "common.h"
+#include "kernels.h"
+
+namespace df {
+
+// ------------------------------------------------------------------------------------------------------
+// embedding + first RMSNorm
+// ------------------------------------------------------------------------------------------------------
+// Block row m gathers its token's embedding row (the drafter shares the target's frozen embedding), keeps it
+// as the float32 residual, and writes u = RMSNorm(h) * g.  Block 0 clears the call's device error word
+// before any later kernel can set a flag; an out-of-range token reads row 0 (flagged later by head_merge).
+template <typename T>
+__global__ __launch_bounds__(256) void embed_norm(const int32_t* __restrict__ tok, int V, const T* __restrict__ embed,
+                                                  const T* __restrict__ gain, int H, float eps, float* __restrict__ h,
+                                                  T* __restrict__ u, float* __restrict__ tap, uint32_t* err) {
+    __shared__ float red[4];
+    const int m = blockIdx.x;
+    if (m == 0 && threadIdx.x == 0 && err) *err = 0u;
+    int t = tok[m];
+    if (t < 0 || t >= V) t = 0;
+    const T* e = embed + (size_t)t * H;
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < H; j += 256) {
+        float v = Act<T>::load(e + j);
+        h[(size_t)m * H + j] = v;
+        if (tap) tap[(size_t)m * H + j] = v;
+        ss += v * v;
+    }
+    ss = block_sum(ss, red);
+    const float rs = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int j = threadIdx.x; j < H; j += 256) {
+        float v = h[(size_t)m * H + j];
+        u[(size_t)m * H + j] = Act<T>::from(v * rs * Act<T>::load(gain + j));
+    }
+}
+
+hipError_t launch_embed_norm(int bf16, const int32_t* tok, int M, int V, const void* embed, const void* gain, int H,
+                             float eps, float* h, void* u, float* tap, uint32_t* err, hipStream_t st) {
+    if (bf16)
+        hipLaunchKernelGGL(embed_norm<bf16_t>, dim3(M), dim3(256), 0, st, tok, V, (const bf16_t*)embed,
+                           (const bf16_t*)gain, H, eps, h, (bf16_t*)u, tap, err);
+    else
+        hipLaunchKernelGGL(embed_norm<float>, dim3(M), dim3(256), 0, st, tok, V, (const float*)embed,
+                           (const float*)gain, H, eps, h, (float*)u, tap, err);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------------
+// residual add of a split-K product + RMSNorm
+// ------------------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void resid_norm(const float* __restrict__ part, int S, int M, int H,
+                                                  float* __restrict__ h, const T* __restrict__ gain, float eps,
+                                                  T* __restrict__ u, float* __restrict__ tap) {
+    __shared__ float red[4];
+    const int m = blockIdx.x;
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < H; j += 256) {
+        float a = 0.f;
+        for (int s = 0; s < S; ++s) a += part[((size_t)s * M + m) * H + j];
+        float v = h[(size_t)m * H + j] + a;
+        h[(size_t)m * H + j] = v;
+        if (tap) tap[(size_t)m * H + j] = v;
+        ss += v * v;
+    }
+    ss = block_sum(ss, red);
+    const float rs = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int j = threadIdx.x; j < H; j += 256) {
+        float v = h[(size_t)m * H + j];
+        u[(size_t)m * H + j] = Act<T>::from(v * rs * Act<T>::load(gain + j));
+    }
+}
+
+hipError_t launch_resid_norm(int bf16, const float* part, int S, int M, int H, float* h, const void* gain, float eps,
+                             void* u, float* tap, hipStream_t st) {
+    if (bf16)
+        hipLaunchKernelGGL(resid_norm<bf16_t>, dim3(M), dim3(256), 0, st, part, S, M, H, h, (const bf16_t*)gain, eps,
+                           (bf16_t*)u, tap);
+    else
+        hipLaunchKernelGGL(resid_norm<float>, dim3(M), dim3(256), 0, st, part, S, M, H, h, (const float*)gain, eps,
+                           (float*)u, tap);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------------
+// QKV epilogue
+// ------------------------------------------------------------------------------------------------------
+// One thread per (block row m, head, rotary pair i): sums the splits of columns i and i + d/2, applies the
+// rotation at position ctx_len[b] + row to q and k heads, rounds, and stores q row-major, the block's keys as
+// a 16-slot page [b][kv head][slot][d] and its values transposed [b][kv head][d][slot].
+__device__ __forceinline__ void rope_pair(float& a, float& b, int pos, int i, const RopeFreq& rf) {
+    if (!rf.on) return;
+    const float ang = (float)pos * rf.inv[i];
+    float sn, cs;
+    sincosf(ang, &sn, &cs);
+    const float x1 = a, x2 = b;
+    a = x1 * cs - x2 * sn;
+    b = x2 * cs + x1 * sn;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_epilogue(const float* __restrict__ part, int S, int B, int L, int nq,
+                                                    int nkv, int d, const int32_t* __restrict__ ctx_len, RopeFreq rf,
+                                                    T* __restrict__ q, T* __restrict__ kb, T* __restrict__ vbt) {
+    const int half = d >> 1;
+    const int heads = nq + 2 * nkv;
+    const int M = B * L;
+    const int N = heads * d;
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)M * heads * half) return;
+    const int i = idx % half;
+    const int hd = (idx / half) % heads;
+    const int m = idx / ((long)half * heads);
+    const int b = m / L, row = m % L;
+    const int c1 = hd * d + i, c2 = c1 + half;
+    float a = 0.f, c = 0.f;
+    for (int s = 0; s < S; ++s) {
+        a += part[((size_t)s * M + m) * N + c1];
+        c += part[((size_t)s * M + m) * N + c2];
+    }
+    const int pos = ctx_len[b] + row;
+    if (hd < nq) {
+        rope_pair(a, c, pos, i, rf);
+        q[(size_t)m * nq * d + hd * d + i] = Act<T>::from(a);
+        q[(size_t)m * nq * d + hd * d + i + half] = Act<T>::from(c);
+    } else if (hd < nq + nkv) {
+        const int kh = hd - nq;
+        rope_pair(a, c, pos, i, rf);
+        T* dst = kb + (((size_t)b * nkv + kh) * 16 + row) * d;
+        dst[i] = Act<T>::from(a);
+        dst[i + half] = Act<T>::from(c);
+    } else {
+        const int kh = hd - nq - nkv;
+        T* dst = vbt + ((size_t)b * nkv + kh) * d * 16;
+        dst[i * 16 + row] = Act<T>::from(a);
+        dst[(i + half) * 16 + row] = Act<T>::from(c);
+    }
+}
+
+hipError_t launch_qkv_epilogue(int bf16, const float* part, int S, int B, int L, int nq, int nkv, int d,
+                               const int32_t* ctx_len, const RopeFreq& rf, void* q, void* kb, void* vbt,
+                               hipStream_t st) {
+    const long n = (long)B * L * (nq + 2 * nkv) * (d / 2);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (bf16)
+        hipLaunchKernelGGL(qkv_epilogue<bf16_t>, grid, dim3(256), 0, st, part, S, B, L, nq, nkv, d, ctx_len, rf,
+                           (bf16_t*)q, (bf16_t*)kb, (bf16_t*)vbt);
+    else
+        hipLaunchKernelGGL(qkv_epilogue<float>, grid, dim3(256), 0, st, part, S, B, L, nq, nkv, d, ctx_len, rf,
+                           (float*)q, (float*)kb, (float*)vbt);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------------
+// SwiGLU and plain reduce + cast
+// ------------------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu(const float* __restrict__ part, int S, int M, int F, T* __restrict__ a) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)M * F) return;
+    const int m = idx / F, j = idx % F;
+    const size_t N = 2 * (size_t)F;
+    float g = 0.f, up = 0.f;
+    for (int s = 0; s < S; ++s) {
+        g += part[((size_t)s * M + m) * N + j];
+        up += part[((size_t)s * M + m) * N + F + j];
+    }
+    const float silu = g / (1.0f + expf(-g));
+    a[idx] = Act<T>::from(silu * up);
+}
+
+hipError_t launch_swiglu(int bf16, const float* part, int S, int M, int F, void* a, hipStream_t st) {
+    const long n = (long)M * F;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (bf16) hipLaunchKernelGGL(swiglu<bf16_t>, grid, dim3(256), 0, st, part, S, M, F, (bf16_t*)a);
+    else hipLaunchKernelGGL(swiglu<float>, grid, dim3(256), 0, st, part, S, M, F, (float*)a);
+    return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_cast(const float* __restrict__ part, int S, int M, int N,
+                                                   const T* __restrict__ bias, T* __restrict__ out) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)M * N) return;
+    const int n = idx % N;
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += part[(size_t)s * M * N + idx];
+    if (bias) v += Act<T>::load(bias + n);
+    out[idx] = Act<T>::from(v);
+}
+
+hipError_t launch_reduce_cast(int bf16, const float* part, int S, int M, int N, const void* bias, void* out,
+                              hipStream_t st) {
+    const long n = (long)M * N;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (bf16)
+        hipLaunchKernelGGL(reduce_cast<bf16_t>, grid, dim3(256), 0, st, part, S, M, N, (const bf16_t*)bias,
+                           (bf16_t*)out);
+    else
+        hipLaunchKernelGGL(reduce_cast<float>, grid, dim3(256), 0, st, part, S, M, N, (const float*)bias, (float*)out);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------------
+// injected context: RoPE + paged scatter
+// ------------------------------------------------------------------------------------------------------
+// One thread per (row, layer, kv head, rotary pair).  The row's request comes from a binary search of
+// row_offsets; its position is start_pos[r] + (row - row_offsets[r]).  A position beyond the page table or a
+// page id outside the pool is skipped and flagged.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_scatter(const float* __restrict__ part, int S, int rows, int row0,
+                                                  int layer0, int n_layers, int nkv, int d, int batch,
+                                                  const int32_t* __restrict__ off, const int32_t* __restrict__ start,
+                                                  const int32_t* __restrict__ pt, int max_pages, int n_pages,
+                                                  T* __restrict__ kpool, T* __restrict__ vpool, RopeFreq rf,
+                                                  uint32_t* err) {
+    const int half = d >> 1;
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)rows * n_layers * nkv * half) return;
+    const int i = idx % half;
+    const int kh = (idx / half) % nkv;
+    const int l = (idx / ((long)half * nkv)) % n_layers;
+    const int j = idx / ((long)half * nkv * n_layers);
+    const int R = row0 + j;
+    if (R >= off[batch]) return;  // padding rows: computed, not stored
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {  // last r with off[r] <= R
+        int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= R) lo = mid;
+        else hi = mid - 1;
+    }
+    const int r = lo;
+    if (off[r] > R || off[r + 1] <= R) {
+        if (i == 0 && kh == 0 && l == 0) set_err(err, DFLASH_DEVERR_ROWS);
+        return;
+    }
+    const int pos = start[r] + (R - off[r]);
+    const int pi = pos >> 4, slot = pos & 15;
+    if (pos < 0 || pi >= max_pages) {
+        if (i == 0 && kh == 0 && l == 0) set_err(err, DFLASH_DEVERR_POS);
+        return;
+    }
+    const int page = pt[(size_t)r * max_pages + pi];
+    if (page < 0 || page >= n_pages) {
+        if (i == 0 && kh == 0 && l == 0) set_err(err, DFLASH_DEVERR_PAGE);
+        return;
+    }
+    const int N = n_layers * 2 * nkv * d;
+    const int ck = l * 2 * nkv * d + kh * d + i;
+    const int cv = ck + nkv * d;
+    float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
+    for (int s = 0; s < S; ++s) {
+        const float* p = part + ((size_t)s * rows + j) * N;
+        k1 += p[ck];
+        k2 += p[ck + half];
+        v1 += p[cv];
+        v2 += p[cv + half];
+    }
+    rope_pair(k1, k2, pos, i, rf);
+    const size_t pg = ((size_t)(layer0 + l) * n_pages + page) * nkv + kh;
+    T* kd = kpool + (pg * 16 + slot) * d;
+    kd[i] = Act<T>::from(k1);
+    kd[i + half] = Act<T>::from(k2);
+    T* vd = vpool + pg * d * 16;
+    vd[i * 16 + slot] = Act<T>::from(v1);
+    vd[(i + half) * 16 + slot] = Act<T>::from(v2);
+}
+
+hipError_t launch_kv_scatter(int bf16, const float* part, int S, int rows, int row0, int layer0, int n_layers,
+                             int nkv, int d, int batch, const int32_t* row_offsets, const int32_t* start_pos,
+                             const int32_t* page_table, int max_pages, int n_pages, void* kpool, void* vpool,
+                             const RopeFreq& rf, uint32_t* err, hipStream_t st) {
+    const long n = (long)rows * n_layers * nkv * (d / 2);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (bf16)
+        hipLaunchKernelGGL(kv_scatter<bf16_t>, grid, dim3(256), 0, st, part, S, rows, row0, layer0, n_layers, nkv, d,
+                           batch,
+                           row_offsets, start_pos, page_table, max_pages, n_pages, (bf16_t*)kpool, (bf16_t*)vpool, rf,
+                           err);
+    else
+        hipLaunchKernelGGL(kv_scatter<float>, grid, dim3(256), 0, st, part, S, rows, row0, layer0, n_layers, nkv, d,
+                           batch,
+                           row_offsets, start_pos, page_table, max_pages, n_pages, (float*)kpool, (float*)vpool, rf,
+                           err);
+    return hipGetLastError();
+}
+
+__global__ void clear_err(uint32_t* err) { *err = 0u; }
+
+hipError_t launch_clear_err(uint32_t* err, hipStream_t st) {
+    hipLaunchKernelGGL(clear_err, dim3(1), dim3(1), 0, st, err);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------------
+// greedy acceptance
+// ------------------------------------------------------------------------------------------------------
+// tau = 1 + the length of the common prefix of the drafts and the target's tokens: the accepted drafts plus
+// the bonus token the target contributes at the first mismatch (or after the block).
+__global__ void accept_len(int batch, int n_draft, const int32_t* __restrict__ draft, int64_t ds,
+                           const int32_t* __restrict__ target, int64_t ts, int32_t* __restrict__ tau) {
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= batch) return;
+    int k = 0;
+    while (k < n_draft && draft[(size_t)r * ds + k] == target[(size_t)r * ts + k]) ++k;
+    tau[r] = k + 1;
+}
+
+hipError_t launch_accept(int batch, int n_draft, const int32_t* draft, int64_t ds, const int32_t* target, int64_t ts,
+                         int32_t* tau, hipStream_t st) {
+    hipLaunchKernelGGL(accept_len, dim3((batch + 63) / 64), dim3(64), 0, st, batch, n_draft, draft, ds, target, ts,
+                       tau);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------------
+// stream copy (bandwidth reference)
+// ------------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void copy16(u32x4* __restrict__ dst, const u32x4* __restrict__ src, size_t n) {
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (; i < n; i += stride) dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+hipError_t launch_copy(void* dst, const void* src, size_t n16, hipStream_t st) {
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks > 256 * 64) blocks = 256 * 64;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(copy16, dim3((unsigned)blocks), dim3(256), 0, st, (u32x4*)dst, (const u32x4*)src, n16);
+    return hipGetLastError();
+}
+
+}  // namespace df

@@ -1,0 +1,76 @@
+// Host-side launchers of the gfx950 kernels (one translation unit per kernel family).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace df {
+
+// ---- GEMM ------------------------------------------------------------------------------------------------
+enum GemmKind { GEMM_SKINNY1 = 0, GEMM_SKINNY2 = 1, GEMM_TILED = 2, GEMM_F32 = 3 };
+struct GemmPlan {
+    int kind;
+    int splits;  // number of float32 partial products written (grid split of K)
+    int kpw;     // skinny: k-range per wave (multiple of 256)
+    int kps;     // tiled: k-range per split (multiple of 64)
+};
+GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K);
+hipError_t launch_gemm(const GemmPlan& p, const void* x, int ldx, int M, const Segs& w, int N, int K, float* part,
+                       hipStream_t st);
+const char* gemm_kernel_name(const GemmPlan& p);
+
+// ---- row-wise kernels ------------------------------------------------------------------------------------
+// h = embed[tok]; u = RMSNorm(h) * g.  Also clears the device error word (block 0).
+hipError_t launch_embed_norm(int bf16, const int32_t* tok, int M, int V, const void* embed, const void* gain, int H,
+                             float eps, float* h, void* u, float* tap, uint32_t* err, hipStream_t st);
+// h += sum_s part[s]; u = RMSNorm(h) * g.
+hipError_t launch_resid_norm(int bf16, const float* part, int S, int M, int H, float* h, const void* gain, float eps,
+                             void* u, float* tap, hipStream_t st);
+// q/k/v from the QKV partials: RoPE at ctx_len[b] + i, rounding, block K [B][n_kv][16][d] and V^T
+// [B][n_kv][d][16] layouts.
+hipError_t launch_qkv_epilogue(int bf16, const float* part, int S, int B, int L, int nq, int nkv, int d,
+                               const int32_t* ctx_len, const RopeFreq& rf, void* q, void* kb, void* vbt,
+                               hipStream_t st);
+// a = silu(sum_s gate) * (sum_s up); partial columns [0, F) are gate, [F, 2F) up.
+hipError_t launch_swiglu(int bf16, const float* part, int S, int M, int F, void* a, hipStream_t st);
+// out[m][n] = round(sum_s part[s][m][n] + bias[n]).
+hipError_t launch_reduce_cast(int bf16, const float* part, int S, int M, int N, const void* bias, void* out,
+                              hipStream_t st);
+// Context K/V from the stacked [U_K^0; U_V^0; U_K^1; ...] partials, RoPE at each row's position, scatter into
+// the paged pool.  row0 = index of the first row of this chunk among all n_rows rows.
+// Columns of part cover layers layer0 .. layer0 + nl - 1.
+hipError_t launch_kv_scatter(int bf16, const float* part, int S, int rows, int row0, int layer0, int nl, int nkv,
+                             int d, int batch, const int32_t* row_offsets, const int32_t* start_pos,
+                             const int32_t* page_table, int max_pages, int n_pages, void* kpool, void* vpool,
+                             const RopeFreq& rf, uint32_t* err, hipStream_t st);
+hipError_t launch_clear_err(uint32_t* err, hipStream_t st);
+hipError_t launch_accept(int batch, int n_draft, const int32_t* draft, int64_t ds, const int32_t* target, int64_t ts,
+                         int32_t* tau, hipStream_t st);
+hipError_t launch_copy(void* dst, const void* src, size_t n16, hipStream_t st);
+
+// ---- attention -------------------------------------------------------------------------------------------
+struct AttnPlan {
+    int n_chunks;      // context chunks (the block itself is one more chunk)
+    int chunk_tokens;  // multiple of 32
+};
+AttnPlan plan_attention(int batch, int n_kv, int max_ctx);
+size_t attn_partial_floats(int batch, int nq, int n_chunks, int d);
+hipError_t launch_attention(int bf16, const AttnPlan& p, int B, int L, int nq, int nkv, int d, const void* q,
+                            const void* kb, const void* vbt, const void* kpool, const void* vpool, int layer,
+                            int n_pages, const int32_t* page_table, int max_pages, const int32_t* ctx_len,
+                            int max_ctx, float* opart, float* mlpart, uint32_t* err, hipStream_t st);
+hipError_t launch_attn_merge(int bf16, const AttnPlan& p, int B, int L, int nq, int d, const float* opart,
+                             const float* mlpart, void* o, hipStream_t st);
+
+// ---- LM head ---------------------------------------------------------------------------------------------
+int head_groups(int V);  // vocabulary groups of 64 columns (one workgroup each)
+size_t head_partial_floats(int V, int M);
+hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V, int K, float* hpart,
+                          float* logits_dbg, hipStream_t st);
+// Also flags block tokens outside [0, V) in the device error word.
+hipError_t launch_head_merge(int M, int V, int top_k, const float* hpart, const int32_t* block_tokens,
+                             int32_t* tokens, int32_t* topk_ids, float* topk_lp, uint32_t* err, hipStream_t st);
+
+}  // namespace df

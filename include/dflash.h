@@ -1,0 +1,205 @@
+/*
+ * dflash.h -- C ABI of the MI355X (gfx950) DFlash drafter hot path.
+ *
+ * Three operations make up one speculative-decoding cycle of a block-diffusion drafter with KV injection:
+ *
+ *   dflash_inject_ctx   fuse the target model's hidden states of newly committed tokens and write them as
+ *                       extra K/V into every drafter layer's paged cache
+ *                       ("DFlash: Block Diffusion for Flash Speculative Decoding", paper-graph summary,
+ *                        section 3.4.3, "Feature fusion" and "What KV injection means operationally";
+ *                        section 3.2, step 5: features are refreshed after every verification);
+ *   dflash_draft_block  one parallel drafter pass over the block [anchor, mask x (L-1)] of each request,
+ *                       returning per-position greedy tokens and top-k log-probabilities
+ *                       (same page, section 3.4.4 "Input structure", "Attention pattern", "Single forward
+ *                        pass prediction"; "Accelerating Speculative Decoding with Block Diffusion Draft
+ *                        Trees", paper-graph summary, section 3.4.2: per-position marginals softmax(l_i));
+ *   dflash_accept_len   greedy acceptance: accepted drafts up to the first mismatch, plus the bonus token
+ *                       (DFlash page, section 3.4.1, the bonus-token paragraph under Eq. 1).
+ *
+ * Conventions
+ *   - Every pointer marked "device" is GPU memory owned by the caller; the library never allocates, frees
+ *     or keeps device memory between calls.  Host structs are read during the call only (the handle keeps
+ *     a copy of the config and of the weight pointers).
+ *   - Matrices are row-major [out, in] ("W[n][k]"), bfloat16 (DFLASH_BF16) or float32 (DFLASH_F32).
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream) and never
+ *     synchronise.  They are safe to capture into a HIP graph (no memset or allocation is enqueued).
+ *   - Arguments are validated before anything is enqueued; on error nothing runs and a negative status is
+ *     returned, with a message available from dflash_last_error() on the calling thread.
+ *   - Device-side checks (page ids, positions, token ids) cannot fail the call; a kernel that meets a bad
+ *     value skips the access and ORs a flag into the 32-bit error word at the start of the workspace
+ *     (DFLASH_DEVERR_*).  Each call clears that word first.  Read it after synchronising.
+ *   - One handle per stream: calls on one handle must not overlap.
+ *
+ * Numerics (bfloat16 drafters): GEMMs accumulate in float32; the residual stream is float32; tensors that
+ * are stored between kernels (fused feature, cached K/V, normalised activations, q/k/v after RoPE,
+ * attention output, SwiGLU output, final normalised state) are rounded to bfloat16 (nearest, ties to
+ * even).  Logits are float32 and never written to memory except through the optional debug tap.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------------------------------- */
+#define DFLASH_OK 0
+#define DFLASH_E_ARG (-1)         /* null pointer, negative or zero size, inconsistent sizes            */
+#define DFLASH_E_SHAPE (-2)       /* config fields inconsistent with each other                          */
+#define DFLASH_E_CAPACITY (-3)    /* workspace smaller than dflash_*_workspace_bytes() for the call     */
+#define DFLASH_E_UNSUPPORTED (-4) /* a shape outside what the kernels implement (see dflash_create)       */
+#define DFLASH_E_HIP (-5)         /* a HIP runtime call failed (launch error, bad stream)                */
+
+/* ---- device error word flags (first 4 bytes of the workspace) -------------------------------------- */
+#define DFLASH_DEVERR_PAGE 1u     /* a page-table entry was outside [0, n_pages): access skipped           */
+#define DFLASH_DEVERR_POS 2u      /* a position fell beyond max_pages * page_size, or ctx_len > max_ctx    */
+#define DFLASH_DEVERR_TOKEN 4u    /* a block token id outside [0, vocab): embedding row 0 used instead    */
+#define DFLASH_DEVERR_ROWS 8u     /* inject row offsets not non-decreasing within [0, n_rows]              */
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Drafter shape.  Block row i of a request with ctx_len C sits at position C + i; context token j sits at
+ * position j.  rope_theta == 0 switches rotary embedding off (identity).                                  */
+typedef struct {
+    int n_layers;       /* drafter transformer layers (>= 1)                                               */
+    int hidden;         /* drafter hidden size H = width of the fused feature                              */
+    int n_q_heads;      /* query heads                                                                      */
+    int n_kv_heads;     /* key/value heads; n_q_heads % n_kv_heads == 0 (grouped-query attention)           */
+    int head_dim;       /* d: bf16 needs 128; f32 allows even d <= 128                                      */
+    int ffn;            /* SwiGLU width                                                                     */
+    int vocab;          /* V of the shared embedding and LM head                                            */
+    int feat_dim;       /* width of the concatenated target hidden states (n_feature_layers * H_target)     */
+    int block_len;      /* L: anchor + L-1 masks, 2 <= L <= 16                                              */
+    int page_size;      /* tokens per KV page; must be 16                                                   */
+    float rms_eps;      /* RMSNorm epsilon                                                                  */
+    float rope_theta;   /* rotary base; 0 = off                                                             */
+    int dtype;          /* dflash_dtype of weights, features, cache and activations                         */
+} dflash_config;
+
+/* Per-layer weights (device pointers, row-major [out, in]).                                               */
+typedef struct {
+    const void *attn_norm;  /* [H] RMSNorm gain before attention                                           */
+    const void *wq;         /* [n_q*d, H]                                                                   */
+    const void *wk;         /* [n_kv*d, H]                                                                  */
+    const void *wv;         /* [n_kv*d, H]                                                                  */
+    const void *wo;         /* [H, n_q*d]                                                                   */
+    const void *uk;         /* [n_kv*d, H] context-key projection of the fused feature (may alias wk)       */
+    const void *uv;         /* [n_kv*d, H] context-value projection (may alias wv)                          */
+    const void *ffn_norm;   /* [H]                                                                          */
+    const void *w_gate;     /* [ffn, H]                                                                     */
+    const void *w_up;       /* [ffn, H]                                                                     */
+    const void *w_down;     /* [H, ffn]                                                                     */
+} dflash_layer_weights;
+
+typedef struct {
+    const void *fc_w;       /* [H, feat_dim] feature-fusion projection                                     */
+    const void *fc_b;       /* [H] or NULL (zero bias)                                                      */
+    const void *embed;      /* [V, H] shared, frozen token embedding                                        */
+    const void *final_norm; /* [H]                                                                          */
+    const void *lm_head;    /* [V, H] shared, frozen LM head                                                */
+    const dflash_layer_weights *layers; /* host array [n_layers]                                            */
+} dflash_weights;
+
+/* Paged KV pool (device).  Layout, in elements of the config dtype:
+ *   k: [n_layers][n_pages][n_kv][page_size][head_dim]   (a page holds 16 consecutive keys)
+ *   v: [n_layers][n_pages][n_kv][head_dim][page_size]   (values stored transposed within the page)
+ * Position p of request r lives in page page_table[r * max_pages + p / 16], slot p % 16.                   */
+typedef struct {
+    void *k;
+    void *v;
+    int n_pages;
+} dflash_kv;
+
+/* Optional test taps (device pointers, float32; NULL = off).                                              */
+typedef struct {
+    float *logits;  /* [batch][L][V] full logits                                                           */
+    float *hidden;  /* [n_layers + 1][batch * L][H] residual stream after the embedding and each layer       */
+} dflash_debug;
+
+typedef struct dflash_handle dflash_handle;
+
+/* Create a handle for a drafter.  Validates the config (no HIP call is made).  Supported: dtype BF16 with
+ * head_dim 128, hidden/ffn/feat_dim/n_q*d multiples of 256; dtype F32 with even head_dim <= 128 and
+ * hidden/ffn/feat_dim/n_q*d multiples of 4; 2 <= L <= 16; page_size 16; n_q/n_kv <= 8.
+ * Returns DFLASH_OK and *out, or an error status (and *out = NULL).                                       */
+int dflash_create(const dflash_config *cfg, const dflash_weights *w, dflash_handle **out);
+void dflash_destroy(dflash_handle *h);
+
+/* Workspace bytes for dflash_draft_block with batch <= max_batch, context lengths <= max_ctx and
+ * top_k <= 8.  Returns 0 on invalid arguments.                                                           */
+size_t dflash_draft_workspace_bytes(const dflash_handle *h, int max_batch, int max_ctx);
+
+/* Workspace bytes for dflash_inject_ctx with n_rows <= max_rows.  Returns 0 on invalid arguments.         */
+size_t dflash_inject_workspace_bytes(const dflash_handle *h, int max_rows);
+
+/* Append context tokens.  For request r, feature rows row_offsets[r] .. row_offsets[r+1]-1 of `feats` are
+ * fused (f = W_fc x + b) and projected per layer into K = RoPE(U_K f) at positions start_pos[r] + j and
+ * V = U_V f, which are stored in the pages named by page_table.  Rows >= row_offsets[batch] are computed
+ * but not stored.  Rows of different requests are independent, so any row split gives the same cache.
+ *   feats          device [n_rows][feat_dim], row stride feat_row_stride elements (>= feat_dim)
+ *   row_offsets    device int32 [batch + 1]
+ *   start_pos      device int32 [batch]
+ *   page_table     device int32 [batch][max_pages]
+ *   ws, ws_bytes   device workspace of at least dflash_inject_workspace_bytes(h, n_rows) bytes           */
+int dflash_inject_ctx(dflash_handle *h, int batch, int n_rows, const void *feats, int64_t feat_row_stride,
+                      const int32_t *row_offsets, const int32_t *start_pos, const int32_t *page_table,
+                      int max_pages, const dflash_kv *kv, void *ws, size_t ws_bytes, void *stream);
+
+/* One drafter pass per request over block_tokens (anchor, then mask ids) against that request's first
+ * ctx_len[r] cached context tokens.  Attention is non-causal over [context ; block].
+ *   block_tokens   device int32 [batch][L]
+ *   ctx_len        device int32 [batch], each in [0, max_ctx]
+ *   page_table     device int32 [batch][max_pages]
+ *   max_ctx        host upper bound of ctx_len (sizes the split of the context across workgroups)
+ *   top_k          0..8
+ *   tokens         device int32 [batch][L]: greedy argmax per row (ties -> smaller id); the drafts are
+ *                  rows 1..L-1
+ *   topk_ids       device int32 [batch][L][top_k] ordered by (logit desc, id asc); NULL if top_k == 0
+ *   topk_logprobs  device float [batch][L][top_k]: logit - logsumexp over the full vocabulary
+ *   dbg            host struct of optional taps, or NULL
+ *   ws, ws_bytes   at least dflash_draft_workspace_bytes(h, batch, max_ctx) bytes                       */
+int dflash_draft_block(dflash_handle *h, int batch, const int32_t *block_tokens, const int32_t *ctx_len,
+                       const int32_t *page_table, int max_pages, const dflash_kv *kv, int max_ctx, int top_k,
+                       int32_t *tokens, int32_t *topk_ids, float *topk_logprobs, const dflash_debug *dbg,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* tau[r] = 1 + the number of leading j < n_draft with draft[r*draft_stride + j] == target[r*target_stride
+ * + j]; tau lies in [1, n_draft + 1].  Typical call: draft = tokens + 1 with stride L, n_draft = L - 1.
+ * All arrays are device int32.  No workspace is used.                                                     */
+int dflash_accept_len(int batch, int n_draft, const int32_t *draft, int64_t draft_stride, const int32_t *target,
+                      int64_t target_stride, int32_t *tau, void *stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none).                                */
+const char *dflash_last_error(void);
+
+/* ---- building blocks (tests, measurement) ----------------------------------------------------------- */
+
+/* y[m][n] = sum_k x[m][k] * w[n][k] for m < M, n < N, with float32 output (row stride N).  x is [M][K]
+ * (row stride ldx elements) and w [N][K], both of `dtype`.  Uses the same GEMM kernels as the drafter
+ * pass.  ws must hold dflash_linear_workspace_bytes(dtype, M, N, K) bytes.                                 */
+size_t dflash_linear_workspace_bytes(int dtype, int M, int N, int K);
+int dflash_linear(int dtype, int M, int N, int K, const void *x, int64_t ldx, const void *w, float *y, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/* Stream copy of n_bytes (multiple of 16, 16-byte aligned pointers) for measuring HBM bandwidth.           */
+int dflash_copy(void *dst, const void *src, size_t n_bytes, void *stream);
+
+/* Per-kernel timing.  When enabled, every kernel a handle launches is bracketed by HIP events.
+ * dflash_profile_collect synchronises those events, fills up to max_entries records (kernel name, number
+ * of launches, total milliseconds) accumulated since the last collect, and returns the number written.   */
+typedef struct {
+    char name[48];
+    int launches;
+    double total_ms;
+} dflash_kernel_stat;
+int dflash_profile_enable(dflash_handle *h, int on);
+int dflash_profile_collect(dflash_handle *h, dflash_kernel_stat *out, int max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

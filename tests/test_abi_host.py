@@ -1,0 +1,173 @@
+"""The C ABI library loads, exports every symbol of include/dflash.h, and rejects bad arguments before any HIP
+call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def D():
+    from block_diffusion_drafter_forward_amd import dflash
+    if not os.path.exists(dflash.LIB_PATH):
+        from block_diffusion_drafter_forward_amd.build import build
+        build()
+    dflash.lib()
+    return dflash
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(D):
+    names = _declared()
+    assert "dflash_draft_block" in names and "dflash_inject_ctx" in names and "dflash_accept_len" in names
+    lib = D.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(D.EXPORTS)
+
+
+def _shape(**kw):
+    import workloads as W
+    s = dict(W.SMALL_BF16.__dict__)
+    s.update(kw)
+    return W.DrafterShape(**s)
+
+
+def _fake_weights(shape, bad=None):
+    """Non-null dummy pointers (never dereferenced: creation makes no HIP call)."""
+    names = ["fc_w", "embed", "final_norm", "lm_head"]
+    for l in range(shape.n_layers):
+        names += [f"l{l}.{f}" for f in D_LAYER]
+    return {n: (None if n == bad else _Fake(0x1000 + 0x100 * i)) for i, n in enumerate(names)}
+
+
+D_LAYER = ["attn_norm", "wq", "wk", "wv", "wo", "uk", "uv", "ffn_norm", "w_gate", "w_up", "w_down"]
+
+
+class _Fake:
+    def __init__(self, p):
+        self.p = p
+
+    def data_ptr(self):
+        return self.p
+
+
+def _create(D, shape, bad=None):
+    return D.DraftModel(shape, _fake_weights(shape, bad))
+
+
+def test_create_accepts_supported_shapes(D):
+    import workloads as W
+    for s in (W.TINY, W.QWEN3_8B, W.LLAMA31_8B, W.SMALL_FP32, W.SMALL_GQA8):
+        m = _create(D, s)
+        assert m.handle
+        m.close()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), -4),
+    (dict(n_q_heads=7), -2),
+    (dict(n_q_heads=32, n_kv_heads=2), -4),
+    (dict(block_len=17), -4),
+    (dict(block_len=1), -4),
+    (dict(hidden=500), -4),
+    (dict(page_size=32), -4),
+    (dict(n_layers=0), -1),
+    (dict(vocab=0), -1),
+])
+def test_create_rejects_bad_configs(D, kw, code):
+    with pytest.raises(D.DFlashError) as e:
+        _create(D, _shape(**kw))
+    assert e.value.code == code
+
+
+def test_create_rejects_null_weights(D):
+    with pytest.raises(D.DFlashError) as e:
+        _create(D, _shape(), bad="l1.w_down")
+    assert e.value.code == D.DFLASH_E_ARG and "layer 1" in str(e.value)
+
+
+def _draft(D, h, **over):
+    a = dict(batch=1, block_tokens=0x10, ctx_len=0x20, page_table=0x30, max_pages=8, kv=D.dflash_kv(0x40, 0x50, 8),
+             max_ctx=100, top_k=8, tokens=0x60, topk_ids=0x70, topk_lp=0x80, dbg=None, ws=0x100000, ws_bytes=1 << 40,
+             stream=None)
+    a.update(over)
+    return D.dflash_draft_block(h, a["batch"], a["block_tokens"], a["ctx_len"], a["page_table"], a["max_pages"],
+                                a["kv"], a["max_ctx"], a["top_k"], a["tokens"], a["topk_ids"], a["topk_lp"], a["dbg"],
+                                a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(batch=0), -1),
+    (dict(block_tokens=None), -1),
+    (dict(tokens=None), -1),
+    (dict(top_k=9), -4),
+    (dict(topk_ids=None), -1),
+    (dict(max_ctx=-1), -1),
+    (dict(max_ctx=129), -3),          # beyond max_pages * 16
+    (dict(page_table=None), -1),
+    (dict(kv=None), -1),
+    (dict(ws_bytes=100), -3),
+    (dict(ws=0x100010), -1),          # misaligned workspace
+    (dict(batch=3), -4),              # 48 block rows: not supported by the fused head yet
+])
+def test_draft_block_validation(D, over, code):
+    m = _create(D, _shape())
+    try:
+        assert _draft(D, m.handle, **over) == code
+        assert D.dflash_last_error()
+    finally:
+        m.close()
+
+
+def test_draft_block_null_handle(D):
+    assert _draft(D, None) == D.DFLASH_E_ARG
+
+
+def test_workspace_sizes(D):
+    m = _create(D, _shape())
+    try:
+        a = D.dflash_draft_workspace_bytes(m.handle, 1, 100)
+        b = D.dflash_draft_workspace_bytes(m.handle, 2, 4096)
+        assert 0 < a < b and a % 256 == 0
+        assert D.dflash_draft_workspace_bytes(m.handle, 0, 100) == 0
+        assert D.dflash_inject_workspace_bytes(m.handle, 7) > 0
+        assert D.dflash_inject_workspace_bytes(m.handle, 0) == 0
+    finally:
+        m.close()
+
+
+def test_inject_validation(D):
+    m = _create(D, _shape())
+    kv = D.dflash_kv(0x40, 0x50, 8)
+    try:
+        call = lambda **o: D.dflash_inject_ctx(m.handle, o.get("batch", 1), o.get("n_rows", 4), o.get("feats", 0x10),
+                                               o.get("stride", 1536), 0x20, 0x30, 0x40, 8, o.get("kv", kv), 0x100000,
+                                               o.get("ws_bytes", 1 << 40), None)
+        assert call(batch=0) == -1
+        assert call(feats=None) == -1
+        assert call(stride=100) == -1
+        assert call(stride=1540) == -1          # rows not 16-byte aligned
+        assert call(ws_bytes=10) == -3
+        assert call(kv=D.dflash_kv(0, 0x50, 8)) == -1
+    finally:
+        m.close()
+
+
+def test_accept_and_linear_validation(D):
+    assert D.dflash_accept_len(0, 15, 0x10, 16, 0x20, 16, 0x30, None) == -1
+    assert D.dflash_accept_len(1, 15, None, 16, 0x20, 16, 0x30, None) == -1
+    assert D.dflash_accept_len(1, 15, 0x10, 8, 0x20, 16, 0x30, None) == -1
+    assert D.dflash_linear(1, 16, 64, 100, 0x10, 100, 0x20, 0x30, 0x40, 1 << 30, None) == -4
+    assert D.dflash_linear(2, 16, 64, 256, 0x10, 256, 0x20, 0x30, 0x40, 1 << 30, None) == -1
+    assert D.dflash_linear(1, 16, 64, 256, 0x10, 256, 0x20, 0x30, 0x40, 16, None) == -3
+    assert D.dflash_linear_workspace_bytes(1, 16, 4096, 4096) > 0
+    assert D.dflash_copy(0x10, 0x20, 17, None) == -1

@@ -170,6 +170,7 @@ class Workload:
     accept_p: Optional[float]       # fixed acceptance probability, or None for U[p_range]
     accept_p_range: Optional[tuple]
     top_k: int = 8
+    ctx_fixed: Optional[tuple] = None   # explicit per-request context lengths (edge cases)
 
     # ---------------- seeds ----------------
     @property
@@ -212,6 +213,8 @@ class Workload:
 
     # ---------------- requests ----------------
     def ctx_lens(self) -> np.ndarray:
+        if self.ctx_fixed is not None:
+            return np.asarray(self.ctx_fixed, dtype=np.int64)
         if self.ctx_len is not None:
             return np.full(self.batch, self.ctx_len, dtype=np.int64)
         lo, hi = self.ctx_range
@@ -306,9 +309,11 @@ SMALL_FP32 = DrafterShape(n_layers=2, hidden=128, n_q_heads=4, n_kv_heads=1, hea
 
 SMALL = [
     Workload(100, "small-bf16-b1", SMALL_BF16, 1, 100, None, False, 0.8, None),
-    Workload(101, "small-bf16-paged-b4", SMALL_BF16, 4, None, (0, 300), True, None, (0.6, 0.95)),
-    Workload(102, "small-gqa8-b3", SMALL_GQA8, 3, None, (1, 70), True, 0.7, None, top_k=5),
+    Workload(101, "small-bf16-paged-b2", SMALL_BF16, 2, None, (1, 300), True, None, (0.6, 0.95)),
+    Workload(102, "small-gqa8-b2", SMALL_GQA8, 2, None, (1, 70), True, 0.7, None, top_k=5),
     Workload(103, "small-fp32-b2", SMALL_FP32, 2, None, (0, 40), True, 0.9, None, top_k=3),
+    Workload(104, "small-bf16-edge-b2", SMALL_BF16, 2, None, None, True, 0.9, None, top_k=1, ctx_fixed=(0, 33)),
+    Workload(105, "small-bf16-long-b1", SMALL_BF16, 1, 1000, None, True, 0.8, None),
 ]
 
 
