@@ -30,11 +30,12 @@ Page names used below:
                  the cycle commits that many tokens plus the target's bonus token.
 
 Readings where the pages are silent or disagree are listed in the design notes and restated next to
-the function that applies them.  Numerics: every floating-point step is fp64.  Where the bfloat16 path
-stores a tensor (fused feature, cached K/V, normalised activations, q/k/v after RoPE, attention output,
-SwiGLU output, final normalised state) the oracle rounds the fp64 value to bfloat16 (round to nearest,
-ties to even); the residual stream and the logits are never rounded.  For float32 drafters nothing is
-rounded.
+the function that applies them.  Numerics: every floating-point step is fp64.  The pages fix no precision;
+the reading here is that a bfloat16 drafter keeps its weights, its input features and its KV cache in
+bfloat16, and nothing else: the cached K/V (the one activation tensor that persists across calls) is
+rounded to bfloat16 (round to nearest, ties to even), while every transient activation (fused feature,
+normalised inputs, q/k/v, attention output, SwiGLU output, final state, residual, logits) is carried at
+full precision.  For float32 drafters nothing is rounded.
 
 Weights are passed as numpy arrays: bfloat16 as uint16 bit patterns, or float32/float64.  They are
 converted to fp64 one matrix (or one row block) at a time, so the oracle never holds a whole drafter in
@@ -92,6 +93,7 @@ def bf16_round(x) -> np.ndarray:
 
 
 def _rounder(bf16: bool):
+    """Rounding applied to values stored in the KV cache."""
     return bf16_round if bf16 else (lambda v: np.asarray(v, dtype=np.float64))
 
 
@@ -196,12 +198,13 @@ def fuse(feats: np.ndarray, fc_w: np.ndarray, fc_b: Optional[np.ndarray], bf16: 
     """f_j = W_fc x_j (+ b) for each context token ([DF] §3.4.3 "Feature fusion").
 
     Reading: the fused width equals the drafter hidden size and no norm is applied to f (the pages
-    show only the projection of the concatenation).  f is stored, so it is rounded on the bf16 path.
+    show only the projection of the concatenation).  f is transient (only the K/V made from it are
+    cached), so it is not rounded.
     """
     f = matmul_wT(to_f64(feats), fc_w)
     if fc_b is not None:
         f = f + to_f64(fc_b)
-    return _rounder(bf16)(f)
+    return f
 
 
 def inject_layer(f: np.ndarray, uk: np.ndarray, uv: np.ndarray, positions: np.ndarray, n_kv: int,
@@ -210,7 +213,8 @@ def inject_layer(f: np.ndarray, uk: np.ndarray, uv: np.ndarray, positions: np.nd
 
     K_j = RoPE(U_K f_j) at the token's own position j, V_j = U_V f_j, one row per context token.
     Reading: the context enters as extra key/value pairs appended in the cache (not as an additive
-    bias on the block's keys), so each context key carries the rotary phase of its own position.
+    bias on the block's keys), so each context key carries the rotary phase of its own position.  These are
+    the cached values, rounded to bfloat16 on the bfloat16 path.
     Returns (K [n, n_kv, d], V [n, n_kv, d]).
     """
     rnd = _rounder(bf16)
@@ -258,7 +262,6 @@ def drafter_hidden(w: Dict[str, np.ndarray], cfg, ctx_kv_per_req: List[Sequence]
     Row-wise steps (norms, projections) run on all B*L rows at once; attention runs per request.
     Returns the final residual h [B, L, H] (and taps [B, n_layers + 1, L, H] if asked).
     """
-    rnd = _rounder(cfg.bf16)
     B, L = block_tokens.shape
     d, nq, nkv = cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads
     ctx = [ctx_kv_per_req[r][0][0].shape[0] for r in range(B)]
@@ -267,19 +270,19 @@ def drafter_hidden(w: Dict[str, np.ndarray], cfg, ctx_kv_per_req: List[Sequence]
     taps = [h.copy()]
     for l in range(cfg.n_layers):
         p = f"l{l}."
-        u = rnd(rms_norm(h, w[p + "attn_norm"], cfg.rms_eps))
-        q = rnd(rope(matmul_wT(u, w[p + "wq"]).reshape(B * L, nq, d), pos, cfg.rope_theta))
-        k = rnd(rope(matmul_wT(u, w[p + "wk"]).reshape(B * L, nkv, d), pos, cfg.rope_theta))
-        v = rnd(matmul_wT(u, w[p + "wv"]).reshape(B * L, nkv, d))
+        u = rms_norm(h, w[p + "attn_norm"], cfg.rms_eps)
+        q = rope(matmul_wT(u, w[p + "wq"]).reshape(B * L, nq, d), pos, cfg.rope_theta)
+        k = rope(matmul_wT(u, w[p + "wk"]).reshape(B * L, nkv, d), pos, cfg.rope_theta)
+        v = matmul_wT(u, w[p + "wv"]).reshape(B * L, nkv, d)
         o = np.empty((B * L, nq, d))
         for r in range(B):
             rows = slice(r * L, (r + 1) * L)
             k_ctx, v_ctx = ctx_kv_per_req[r][l]
             o[rows] = block_attention(q[rows], k_ctx, v_ctx, k[rows], v[rows])
-        o = rnd(o).reshape(B * L, nq * d)
+        o = o.reshape(B * L, nq * d)
         h = h + matmul_wT(o, w[p + "wo"])
-        u2 = rnd(rms_norm(h, w[p + "ffn_norm"], cfg.rms_eps))
-        a = rnd(silu(matmul_wT(u2, w[p + "w_gate"])) * matmul_wT(u2, w[p + "w_up"]))
+        u2 = rms_norm(h, w[p + "ffn_norm"], cfg.rms_eps)
+        a = silu(matmul_wT(u2, w[p + "w_gate"])) * matmul_wT(u2, w[p + "w_up"])
         h = h + matmul_wT(a, w[p + "w_down"])
         taps.append(h.copy())
     h = h.reshape(B, L, -1)
@@ -290,7 +293,7 @@ def drafter_hidden(w: Dict[str, np.ndarray], cfg, ctx_kv_per_req: List[Sequence]
 
 def lm_head_logits(w: Dict[str, np.ndarray], cfg, h: np.ndarray) -> np.ndarray:
     """Final RMSNorm, then the shared LM head: logits [L, V] (never rounded)."""
-    z = _rounder(cfg.bf16)(rms_norm(h, w["final_norm"], cfg.rms_eps))
+    z = rms_norm(h, w["final_norm"], cfg.rms_eps)
     return matmul_wT(z, w["lm_head"], rows_per_chunk=16384)
 
 
