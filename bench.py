@@ -180,7 +180,8 @@ def main():
                for n, c, t in stats}
 
     ab = algorithmic_bytes(s, wl.batch, int(ctx.sum()), n_new)
-    fam = {"gemm": [n for n in kernels if n.startswith("gemm_")], "attn": [n for n in kernels if n.startswith("attn_bf16") or n == "attn_f32"],
+    fam = {"gemm": [n for n in kernels if n.startswith("gemm_")],
+           "attn": [n for n in kernels if n.startswith("attn_bf16") or n == "attn_f32"],
            "lm_head": [n for n in kernels if n.startswith("lm_head")]}
     fam_time = {f: sum(kernels[n]["total_us_per_step"] for n in ns) for f, ns in fam.items()}
     dom = max(fam_time, key=fam_time.get)
@@ -190,7 +191,7 @@ def main():
     achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": ",".join(sorted(fam[dom])), "bytes_per_launch": int(bytes_per_launch),
+                "kernel": ",".join(sorted({n.split(" ")[0] for n in fam[dom]})), "bytes_per_launch": int(bytes_per_launch),
                 "avg_launch_us": round(avg_us, 2)}
 
     blocks_per_s = wl.batch * 1e3 / ms_step

@@ -14,15 +14,15 @@
 namespace df {
 
 AttnPlan plan_attention(int batch, int n_kv, int max_ctx) {
-    AttnPlan p{0, 32};
+    AttnPlan p{0, 64};
     if (max_ctx <= 0) return p;
     const int units = batch * n_kv;
     int want = (256 + units - 1) / units;
-    const int max_chunks = (max_ctx + 31) / 32;
+    const int max_chunks = (max_ctx + 127) / 128;  // at least two sub-chunks per workgroup
     if (want > max_chunks) want = max_chunks;
     if (want < 1) want = 1;
     int ct = (max_ctx + want - 1) / want;
-    ct = (ct + 31) / 32 * 32;
+    ct = (ct + 63) / 64 * 64;  // whole 64-key sub-chunks
     p.chunk_tokens = ct;
     p.n_chunks = (max_ctx + ct - 1) / ct;
     return p;
@@ -37,29 +37,46 @@ __device__ __forceinline__ uint32_t pack2(bf16_t lo, bf16_t hi) { return (uint32
 // ------------------------------------------------------------------------------------------------------
 // bfloat16 MFMA kernel (head_dim 128)
 // ------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kb,
-                                                 const bf16_t* __restrict__ vbt, const bf16_t* __restrict__ kpool,
-                                                 const bf16_t* __restrict__ vpool, int layer, int n_pages,
-                                                 const int32_t* __restrict__ pt, int max_pages,
-                                                 const int32_t* __restrict__ ctx_len, int max_ctx, int chunk_tokens,
-                                                 int n_chunks, int L, int nq, int nkv, float* __restrict__ opart,
-                                                 float* __restrict__ mlpart, uint32_t* err) {
+// Sub-chunks of 64 keys (four 16-key pages) are staged in LDS by the whole workgroup, so the G query heads
+// of a KV group read each K/V byte from HBM once.  While the waves compute on one sub-chunk, the next one is
+// already in flight into registers.  Slots past the chunk's last key and pages the table does not map are
+// staged as zeros, so uninitialised cache memory can never reach the MFMAs.
+// q and the block's own k / v are activation pairs (hi + lo bfloat16 planes); the cached K/V are plain
+// bfloat16.  The block chunk stages its hi page in page slot 0 and its lo page in slot 1 and multiplies
+// every pair of terms.
+#define AT_SUB 64
+#define AT_KLD (128 + 8)  // padded LDS row of a key (elements): 16 consecutive keys hit distinct banks
+#define AT_VLD (16 + 8)   // padded LDS row of one d within a page's transposed values
+
+template <int G>
+__global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kb,
+                                                    const bf16_t* __restrict__ vbt, const bf16_t* __restrict__ kpool,
+                                                    const bf16_t* __restrict__ vpool, int layer, int n_pages,
+                                                    const int32_t* __restrict__ pt, int max_pages,
+                                                    const int32_t* __restrict__ ctx_len, int max_ctx,
+                                                    int chunk_tokens, int n_chunks, int L, int nq, int nkv,
+                                                    float* __restrict__ opart, float* __restrict__ mlpart,
+                                                    uint32_t* err) {
     constexpr int D = 128;
+    constexpr int NT = 64 * G;
+    constexpr int PIECES = 4 * 512;  // 16-byte pieces per sub-chunk: per page 256 of K and 256 of V^T
+    constexpr int PPT = PIECES / NT;
+    __shared__ __attribute__((aligned(16))) bf16_t sk[AT_SUB * AT_KLD];
+    __shared__ __attribute__((aligned(16))) bf16_t sv[4 * D * AT_VLD];
     const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-    const int G = nq / nkv;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int h = kvh * G + w;
     const int C1 = n_chunks + 1;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+    const size_t page_elems = (size_t)16 * D;
 
-    // key range of this chunk
     int t0 = 0, t1 = 0;
-    bool block_chunk = (c == 0);
+    const bool block_chunk = (c == 0);
     if (!block_chunk) {
         int ctx = ctx_len[b];
         if (ctx > max_ctx || ctx < 0) {
-            if (c == 1 && threadIdx.x == 0) set_err(err, DFLASH_DEVERR_POS);
+            if (c == 1 && tid == 0) set_err(err, DFLASH_DEVERR_POS);
             ctx = ctx < 0 ? 0 : max_ctx;
         }
         t0 = (c - 1) * chunk_tokens;
@@ -68,13 +85,86 @@ __global__ __launch_bounds__(512) void attn_bf16(const bf16_t* __restrict__ q, c
         t1 = L;
     }
 
+    const size_t bplane = (size_t)gridDim.z * nkv * page_elems;  // hi -> lo plane of the block's k / v
+    const size_t qplane = (size_t)gridDim.z * L * nq * D;          // hi -> lo plane of q
+    // source page of page slot e of the sub-chunk starting at key ts; nullptr if unmapped
+    auto page_src = [&](int ts, int e, const bf16_t*& kp, const bf16_t*& vp) {
+        const int tp = ts + 16 * e;
+        kp = nullptr;
+        vp = nullptr;
+        if (block_chunk) {
+            if (e < 2) {
+                kp = kb + ((size_t)b * nkv + kvh) * page_elems + e * bplane;
+                vp = vbt + ((size_t)b * nkv + kvh) * page_elems + e * bplane;
+            }
+            return;
+        }
+        if (tp >= t1) return;
+        const int pi = tp >> 4;
+        if (pi >= max_pages) {
+            if (lane == 0 && w == 0) set_err(err, DFLASH_DEVERR_POS);
+            return;
+        }
+        const int page = pt[(size_t)b * max_pages + pi];
+        if (page < 0 || page >= n_pages) {
+            if (lane == 0 && w == 0) set_err(err, DFLASH_DEVERR_PAGE);
+            return;
+        }
+        const size_t pg = ((size_t)layer * n_pages + page) * nkv + kvh;
+        kp = kpool + pg * page_elems;
+        vp = vpool + pg * page_elems;
+    };
+
+    u32x4 pf[PPT];
+    auto prefetch = [&](int ts) {
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = tid + i * NT;
+            const int e = p >> 9, qq = p & 511;
+            const bf16_t *kp, *vp;
+            page_src(ts, e, kp, vp);
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (qq < 256) {
+                if (kp) v = ld16(kp + (qq >> 4) * D + (qq & 15) * 8);
+            } else if (vp) {
+                const int q2 = qq - 256, d = q2 >> 1, half = q2 & 1;
+                v = ld16(vp + d * 16 + half * 8);
+                // zero the values of slots past the last key (they may hold anything)
+                const int nvalid = block_chunk ? L : t1 - (ts + 16 * e);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s0 = half * 8 + 2 * j;
+                    uint32_t m = (s0 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
+                    v[j] &= m;
+                }
+            }
+            pf[i] = v;
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = tid + i * NT;
+            const int e = p >> 9, qq = p & 511;
+            if (qq < 256) {
+                *(u32x4*)(sk + (e * 16 + (qq >> 4)) * AT_KLD + (qq & 15) * 8) = pf[i];
+            } else {
+                const int q2 = qq - 256, d = q2 >> 1, half = q2 & 1;
+                *(u32x4*)(sv + (e * D + d) * AT_VLD + half * 8) = pf[i];
+            }
+        }
+    };
+
     // Q^T operand: lane supplies query row r (zero beyond L), eight d-values per 32-wide k-step
-    u32x4 qf[4];
+    u32x4 qf[4], ql[4];
     {
         const bool ok = r < L;
         const bf16_t* qp = q + ((size_t)(b * L + (ok ? r : 0)) * nq + h) * D + g * 8;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qf[s] = ok ? ld16(qp + s * 32) : u32x4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < 4; ++s) {
+            qf[s] = ok ? ld16(qp + s * 32) : u32x4{0u, 0u, 0u, 0u};
+            ql[s] = ok ? ld16(qp + qplane + s * 32) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
 
     f32x4 o[8];
@@ -82,74 +172,66 @@ __global__ __launch_bounds__(512) void attn_bf16(const bf16_t* __restrict__ q, c
     for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const size_t page_elems = (size_t)16 * D;
-    for (int tp = t0; tp < t1; tp += 32) {
-        // the two pages of this step (the block chunk has one)
-        const bf16_t* kp[2];
-        const bf16_t* vp[2];
-        bool pvalid[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int ts = tp + 16 * e;
-            pvalid[e] = false;
-            kp[e] = kb;
-            vp[e] = vbt;
-            if (block_chunk) {
-                if (e == 0) {
-                    kp[e] = kb + ((size_t)b * nkv + kvh) * page_elems;
-                    vp[e] = vbt + ((size_t)b * nkv + kvh) * page_elems;
-                    pvalid[e] = true;
-                }
-            } else if (ts < t1) {
-                const int pi = ts >> 4;
-                int page = pi < max_pages ? pt[(size_t)b * max_pages + pi] : -1;
-                if (pi >= max_pages) {
-                    if (lane == 0 && w == 0) set_err(err, DFLASH_DEVERR_POS);
-                } else if (page < 0 || page >= n_pages) {
-                    if (lane == 0 && w == 0) set_err(err, DFLASH_DEVERR_PAGE);
-                } else {
-                    const size_t pg = ((size_t)layer * n_pages + page) * nkv + kvh;
-                    kp[e] = kpool + pg * page_elems;
-                    vp[e] = vpool + pg * page_elems;
-                    pvalid[e] = true;
-                }
-            }
-        }
+    if (t0 < t1) prefetch(t0);
+    for (int ts = t0; ts < t1; ts += AT_SUB) {
+        __syncthreads();
+        stash();
+        __syncthreads();
+        if (ts + AT_SUB < t1) prefetch(ts + AT_SUB);
         // scores S^T[key][query]: lane holds keys 4g+i of each page for query r
-        float x[2][4];
-        bool kvalid[2][4];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        float x[4][4];
+        if (block_chunk) {
+            // the block's keys: (K_hi + K_lo)(Q_hi + Q_lo)^T, keys in page slot 0 only
             f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (pvalid[e]) {
-                const bf16_t* kr = kp[e] + (size_t)r * D + g * 8;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) sa = mfma16(ld16(kr + s * 32), qf[s], sa);
+            for (int e = 0; e < 2; ++e) {
+                const bf16_t* kr = sk + (e * 16 + r) * AT_KLD + g * 8;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const u32x4 kf = ld16(kr + s * 32);
+                    sa = mfma16(kf, qf[s], sa);
+                    sa = mfma16(kf, ql[s], sa);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = tp + 16 * e + 4 * g + i;
-                kvalid[e][i] = pvalid[e] && key < t1;
-                x[e][i] = kvalid[e][i] ? sa[i] * scale_log2 : -INFINITY;
+                x[0][i] = 4 * g + i < L ? sa[i] * scale_log2 : -INFINITY;
+                x[1][i] = x[2][i] = x[3][i] = -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
+                const bf16_t* kr = sk + (e * 16 + r) * AT_KLD + g * 8;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const u32x4 kf = ld16(kr + s * 32);
+                    sa = mfma16(kf, qf[s], sa);
+                    sa = mfma16(kf, ql[s], sa);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = ts + 16 * e + 4 * g + i;
+                    x[e][i] = key < t1 ? sa[i] * scale_log2 : -INFINITY;
+                }
             }
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[e][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run, mx);
-        // no branch around the MFMAs: while every key so far is masked, use 0 as the reference so that
-        // alpha and p evaluate to 0 instead of exp2(-inf + inf)
+        // while every key so far is masked use 0 as reference: alpha and p become 0, not exp2(-inf + inf)
         const float m_ref = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = exp2f(m_run - m_ref);
         m_run = m_new;
-        float p[2][4];
+        float p[4][4];
         float psum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 p[e][i] = exp2f(x[e][i] - m_ref);
@@ -160,38 +242,45 @@ __global__ __launch_bounds__(512) void attn_bf16(const bf16_t* __restrict__ q, c
         for (int dt = 0; dt < 8; ++dt) {
             o[dt][0] *= alpha; o[dt][1] *= alpha; o[dt][2] *= alpha; o[dt][3] *= alpha;
         }
-        // P^T operand, split into two bfloat16 terms
-        bf16_t hi[8], lo[8];
+        // O^T += V^T P^T over the two 32-key halves; P enters as two bfloat16 terms (hi + lo)
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
+        for (int hk = 0; hk < 2; ++hk) {
+            if (ts + 32 * hk >= t1) break;  // uniform: the rest of the sub-chunk is masked
+            bf16_t hi[8], lo[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = p[e][i];
+            for (int j = 0; j < 8; ++j) {
+                const float v = p[2 * hk + (j >> 2)][j & 3];
                 const bf16_t hb = f2bf(v);
-                hi[4 * e + i] = hb;
-                lo[4 * e + i] = f2bf(v - bf2f(hb));
+                hi[j] = hb;
+                lo[j] = f2bf(v - bf2f(hb));
             }
-        const u32x4 phi = u32x4{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])};
-        const u32x4 plo = u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])};
-        // V^T operand: lane row d = 16 dt + r, keys 4g..4g+3 of each page (masked keys read as zero)
+            const u32x4 phi = u32x4{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])};
+            const u32x4 plo = u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])};
+            if (block_chunk) {
+                // (V_hi + V_lo)^T over the block's keys (page slot 0 of the operand; slot 1 holds the lo plane)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            u32x2 va = u32x2{0u, 0u}, vb2 = u32x2{0u, 0u};
-            const int d = dt * 16 + r;
-            if (pvalid[0]) va = *(const u32x2*)(vp[0] + (size_t)d * 16 + 4 * g);
-            if (pvalid[1]) vb2 = *(const u32x2*)(vp[1] + (size_t)d * 16 + 4 * g);
-            uint32_t a0 = va.x, a1 = va.y, b0 = vb2.x, b1 = vb2.y;
-            if (!kvalid[0][0]) a0 &= 0xFFFF0000u;
-            if (!kvalid[0][1]) a0 &= 0x0000FFFFu;
-            if (!kvalid[0][2]) a1 &= 0xFFFF0000u;
-            if (!kvalid[0][3]) a1 &= 0x0000FFFFu;
-            if (!kvalid[1][0]) b0 &= 0xFFFF0000u;
-            if (!kvalid[1][1]) b0 &= 0x0000FFFFu;
-            if (!kvalid[1][2]) b1 &= 0xFFFF0000u;
-            if (!kvalid[1][3]) b1 &= 0x0000FFFFu;
-            const u32x4 vf = u32x4{a0, a1, b0, b1};
-            o[dt] = mfma16(vf, phi, o[dt]);
-            o[dt] = mfma16(vf, plo, o[dt]);
+                for (int dt = 0; dt < 8; ++dt) {
+                    const int d = dt * 16 + r;
+                    const u32x2 vh = *(const u32x2*)(sv + (0 * D + d) * AT_VLD + 4 * g);
+                    const u32x2 vl = *(const u32x2*)(sv + (1 * D + d) * AT_VLD + 4 * g);
+                    const u32x4 fh = u32x4{vh[0], vh[1], 0u, 0u};
+                    const u32x4 fl = u32x4{vl[0], vl[1], 0u, 0u};
+                    o[dt] = mfma16(fh, phi, o[dt]);
+                    o[dt] = mfma16(fh, plo, o[dt]);
+                    o[dt] = mfma16(fl, phi, o[dt]);
+                    o[dt] = mfma16(fl, plo, o[dt]);
+                }
+                break;
+            }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const int d = dt * 16 + r;
+                const u32x2 va = *(const u32x2*)(sv + ((2 * hk) * D + d) * AT_VLD + 4 * g);
+                const u32x2 vb = *(const u32x2*)(sv + ((2 * hk + 1) * D + d) * AT_VLD + 4 * g);
+                const u32x4 vf = u32x4{va[0], va[1], vb[0], vb[1]};
+                o[dt] = mfma16(vf, phi, o[dt]);
+                o[dt] = mfma16(vf, plo, o[dt]);
+            }
         }
     }
 
@@ -212,27 +301,47 @@ __global__ __launch_bounds__(512) void attn_bf16(const bf16_t* __restrict__ q, c
 // ------------------------------------------------------------------------------------------------------
 // merge of the chunk partials -> o (rounded), and the float32 attention kernel
 // ------------------------------------------------------------------------------------------------------
+// One wave per (request, query head, block row): lanes first combine the chunks' (m, l) in the log2 domain,
+// then each lane accumulates two of the 128 output columns over the chunks in a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ opart, const float* __restrict__ mlpart,
                                                   int B, int L, int nq, int d, int C1, T* __restrict__ o) {
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (long)B * L * nq * d) return;
-    const int dd = idx % d;
-    const int h = (idx / d) % nq;
-    const int row = (idx / ((long)d * nq)) % L;
-    const int b = idx / ((long)d * nq * L);
+    __shared__ float wsh[4][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int item = blockIdx.x * 4 + w;  // (b, row, h)
+    if (item >= B * L * nq) return;
+    const int h = item % nq;
+    const int row = (item / nq) % L;
+    const int b = item / (nq * L);
     const size_t base = ((size_t)b * nq + h) * C1;
     float M = -INFINITY;
-    for (int c = 0; c < C1; ++c) M = fmaxf(M, mlpart[((base + c) * 16 + row) * 2]);
-    float lsum = 0.f, acc = 0.f;
-    for (int c = 0; c < C1; ++c) {
-        const float mc = mlpart[((base + c) * 16 + row) * 2];
-        if (mc == -INFINITY) continue;
-        const float wgt = exp2f(mc - M);
-        lsum += wgt * mlpart[((base + c) * 16 + row) * 2 + 1];
-        acc += wgt * opart[((base + c) * 16 + row) * d + dd];
+    for (int c = lane; c < C1; c += 64) M = fmaxf(M, mlpart[((base + c) * 16 + row) * 2]);
+    M = wave_max(M);
+    float lsum = 0.f, acc0 = 0.f, acc1 = 0.f;
+    for (int c0 = 0; c0 < C1; c0 += 64) {
+        const int c = c0 + lane;
+        float wgt = 0.f;
+        if (c < C1) {
+            const float mc = mlpart[((base + c) * 16 + row) * 2];
+            wgt = mc == -INFINITY ? 0.f : exp2f(mc - M);
+            lsum += wgt * mlpart[((base + c) * 16 + row) * 2 + 1];
+        }
+        wsh[w][lane] = wgt;
+        __builtin_amdgcn_wave_barrier();
+        const int cn = min(64, C1 - c0);
+        const float* op = opart + ((base + c0) * 16 + row) * d;
+#pragma unroll 4
+        for (int i = 0; i < cn; ++i) {
+            const float wi = wsh[w][i];
+            acc0 += wi * op[(size_t)i * 16 * d + lane];
+            acc1 += wi * op[(size_t)i * 16 * d + lane + 64];
+        }
+        __builtin_amdgcn_wave_barrier();
     }
-    o[((size_t)(b * L + row) * nq + h) * d + dd] = Act<T>::from(acc / lsum);
+    lsum = wave_sum(lsum);
+    const size_t base_o = ((size_t)(b * L + row) * nq + h) * d, plane = (size_t)B * L * nq * d;
+    put_act(o, plane, base_o + lane, acc0 / lsum);
+    put_act(o, plane, base_o + lane + 64, acc1 / lsum);
 }
 
 // Float32 drafters: one wave per (block row, query head, request); lanes take keys round-robin with their
@@ -312,10 +421,19 @@ hipError_t launch_attention(int bf16, const AttnPlan& p, int B, int L, int nq, i
                             int max_ctx, float* opart, float* mlpart, uint32_t* err, hipStream_t st) {
     if (bf16) {
         const int G = nq / nkv;
-        hipLaunchKernelGGL(attn_bf16, dim3(p.n_chunks + 1, nkv, B), dim3(64 * G), 0, st, (const bf16_t*)q,
-                           (const bf16_t*)kb, (const bf16_t*)vbt, (const bf16_t*)kpool, (const bf16_t*)vpool, layer,
-                           n_pages, page_table, max_pages, ctx_len, max_ctx, p.chunk_tokens, p.n_chunks, L, nq, nkv,
-                           opart, mlpart, err);
+        const dim3 grid(p.n_chunks + 1, nkv, B);
+#define DF_ATTN(GG)                                                                                                \
+    hipLaunchKernelGGL(attn_bf16<GG>, grid, dim3(64 * GG), 0, st, (const bf16_t*)q, (const bf16_t*)kb,            \
+                       (const bf16_t*)vbt, (const bf16_t*)kpool, (const bf16_t*)vpool, layer, n_pages, page_table, \
+                       max_pages, ctx_len, max_ctx, p.chunk_tokens, p.n_chunks, L, nq, nkv, opart, mlpart, err)
+        switch (G) {
+            case 1: DF_ATTN(1); break;
+            case 2: DF_ATTN(2); break;
+            case 4: DF_ATTN(4); break;
+            case 8: DF_ATTN(8); break;
+            default: return hipErrorInvalidValue;
+        }
+#undef DF_ATTN
     } else {
         // writes o (float32) straight into opart's storage; no merge step
         hipLaunchKernelGGL(attn_f32, dim3(L, nq, B), dim3(64), 0, st, (const float*)q, (const float*)kb,
@@ -327,8 +445,8 @@ hipError_t launch_attention(int bf16, const AttnPlan& p, int B, int L, int nq, i
 
 hipError_t launch_attn_merge(int bf16, const AttnPlan& p, int B, int L, int nq, int d, const float* opart,
                              const float* mlpart, void* o, hipStream_t st) {
-    const long n = (long)B * L * nq * d;
-    const dim3 grid((unsigned)((n + 255) / 256));
+    const long n = (long)B * L * nq;  // one wave each (d == 128)
+    const dim3 grid((unsigned)((n + 3) / 4));
     if (bf16)
         hipLaunchKernelGGL(attn_merge<bf16_t>, grid, dim3(256), 0, st, opart, mlpart, B, L, nq, d, p.n_chunks + 1,
                            (bf16_t*)o);

@@ -25,7 +25,7 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
     return (bf16_t)(u >> 16);
 }
 
-// Storage type of activations: bfloat16 bits or float32.
+// Storage type of weights and cached values: bfloat16 bits or float32.
 template <typename T> struct Act;
 template <> struct Act<bf16_t> {
     static __device__ __forceinline__ float load(const bf16_t* p) { return bf2f(*p); }
@@ -35,6 +35,21 @@ template <> struct Act<float> {
     static __device__ __forceinline__ float load(const float* p) { return *p; }
     static __device__ __forceinline__ float from(float f) { return f; }
 };
+
+// Transient activations of a bfloat16 drafter are kept at float32 precision as two bfloat16 planes,
+// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi) (relative error <= 2^-17), so that they can enter the
+// bfloat16 MFMAs exactly enough: a product with hi + lo costs two MFMAs.  `plane` is the element distance
+// from the hi plane to the lo plane.  Float32 drafters store the value itself (plane unused).
+__device__ __forceinline__ void put_act(bf16_t* p, size_t plane, size_t i, float v) {
+    const bf16_t h = f2bf(v);
+    p[i] = h;
+    p[i + plane] = f2bf(v - bf2f(h));
+}
+__device__ __forceinline__ void put_act(float* p, size_t, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ float get_act(const bf16_t* p, size_t plane, size_t i) {
+    return bf2f(p[i]) + bf2f(p[i + plane]);
+}
+__device__ __forceinline__ float get_act(const float* p, size_t, size_t i) { return p[i]; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes = eight bfloat16 MFMA operands
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

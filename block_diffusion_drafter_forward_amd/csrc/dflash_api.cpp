@@ -57,6 +57,8 @@ struct dflash_handle {
 
 static bool is_bf16(const dflash_config& c) { return c.dtype == DFLASH_BF16; }
 static size_t elt(const dflash_config& c) { return is_bf16(c) ? 2 : 4; }
+// Transient activations: a pair of bfloat16 planes (bfloat16 drafters) or float32 -- 4 bytes per element.
+static const size_t ACT = 4;
 
 static int validate_config(const dflash_config* c) {
     if (!c) return fail(DFLASH_E_ARG, "config is NULL");
@@ -65,9 +67,14 @@ static int validate_config(const dflash_config* c) {
         return fail(DFLASH_E_ARG, "config sizes must be positive");
     if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return fail(DFLASH_E_ARG, "unknown dtype %d", c->dtype);
     if (c->n_q_heads % c->n_kv_heads) return fail(DFLASH_E_SHAPE, "n_q_heads %% n_kv_heads != 0");
-    if (c->n_q_heads / c->n_kv_heads > 8) return fail(DFLASH_E_UNSUPPORTED, "more than 8 query heads per KV head");
+    {
+        const int G = c->n_q_heads / c->n_kv_heads;
+        if (G != 1 && G != 2 && G != 4 && G != 8)
+            return fail(DFLASH_E_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8");
+    }
     if (c->block_len < 2 || c->block_len > 16) return fail(DFLASH_E_UNSUPPORTED, "block_len must be in [2, 16]");
     if (c->page_size != 16) return fail(DFLASH_E_UNSUPPORTED, "page_size must be 16");
+    if (c->hidden > 16384) return fail(DFLASH_E_UNSUPPORTED, "hidden must be <= 16384");
     if (!(c->rms_eps >= 0.f) || !(c->rope_theta >= 0.f)) return fail(DFLASH_E_ARG, "rms_eps and rope_theta must be >= 0");
     const int qd = c->n_q_heads * c->head_dim;
     if (is_bf16(*c)) {
@@ -137,9 +144,11 @@ struct Timed {
     hipStream_t st;
     ProfEntry e{};
     bool on;
-    Timed(dflash_handle* h_, const char* name, hipStream_t s) : h(h_), st(s), on(h_ && h_->profiling) {
+    Timed(dflash_handle* h_, const char* name, hipStream_t s, int N = 0, int K = 0)
+        : h(h_), st(s), on(h_ && h_->profiling) {
         if (!on) return;
         e.name = name;
+        if (N > 0) e.name += " N=" + std::to_string(N) + " K=" + std::to_string(K);
         e.start = take_event(h);
         e.stop = take_event(h);
         if (e.start) (void)hipEventRecord(e.start, st);
@@ -211,7 +220,6 @@ static DraftPlan plan_draft(const dflash_config& c, int batch, int max_ctx) {
     const int bf = is_bf16(c);
     const int M = batch * c.block_len;
     const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
-    const size_t E = elt(c);
     p.M = M;
     p.qkv = plan_gemm(bf, M, qd + 2 * kvd, c.hidden);
     p.oproj = plan_gemm(bf, M, c.hidden, qd);
@@ -225,12 +233,12 @@ static DraftPlan plan_draft(const dflash_config& c, int batch, int max_ctx) {
     Carve cv;
     p.err = cv.take(256);
     p.h = cv.take((size_t)M * c.hidden * 4);
-    p.u = cv.take((size_t)M * c.hidden * E);
-    p.q = cv.take((size_t)M * qd * E);
-    p.kb = cv.take((size_t)batch * kvd * 16 * E);
-    p.vbt = cv.take((size_t)batch * kvd * 16 * E);
-    p.o = cv.take((size_t)M * qd * E);
-    p.a = cv.take((size_t)M * c.ffn * E);
+    p.u = cv.take((size_t)M * c.hidden * ACT);
+    p.q = cv.take((size_t)M * qd * ACT);
+    p.kb = cv.take((size_t)batch * kvd * 16 * ACT);
+    p.vbt = cv.take((size_t)batch * kvd * 16 * ACT);
+    p.o = cv.take((size_t)M * qd * ACT);
+    p.a = cv.take((size_t)M * c.ffn * ACT);
     p.part = cv.take(part * 4);
     const size_t C1 = (size_t)p.attn.n_chunks + 1;
     if (bf) {
@@ -240,14 +248,14 @@ static DraftPlan plan_draft(const dflash_config& c, int batch, int max_ctx) {
         p.opart = cv.take((size_t)M * qd * 4);
         p.ml = cv.take(0);
     }
-    p.hpart = cv.take(head_partial_floats(c.vocab, M) * 4);
+    p.hpart = cv.take(head_partial_floats(bf, c.vocab, M) * 4);
     p.total = cv.off;
     return p;
 }
 
 static bool draft_shape_ok(const dflash_config& c, int batch) {
     const int M = batch * c.block_len;
-    return M <= 32;  // the fused LM head keeps at most 32 block rows per workgroup
+    return is_bf16(c) || M <= 32;  // the float32 LM head keeps at most 32 block rows per workgroup
 }
 
 extern "C" size_t dflash_draft_workspace_bytes(const dflash_handle* h, int max_batch, int max_ctx) {
@@ -275,7 +283,7 @@ static InjectPlan plan_inject(const dflash_config& c, int n_rows) {
     size_t part = std::max((size_t)fc.splits * R * c.hidden, (size_t)kv.splits * R * nl * 2 * kvd);
     Carve cv;
     p.err = cv.take(256);
-    p.f = cv.take((size_t)R * c.hidden * elt(c));
+    p.f = cv.take((size_t)R * c.hidden * ACT);
     p.part = cv.take(part * 4);
     p.total = cv.off;
     return p;
@@ -318,7 +326,8 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
             return fail(DFLASH_E_CAPACITY, "max_ctx %d exceeds max_pages * page_size", max_ctx);
     }
     if (!draft_shape_ok(c, batch))
-        return fail(DFLASH_E_UNSUPPORTED, "batch * block_len = %d > 32 is not supported yet", batch * c.block_len);
+        return fail(DFLASH_E_UNSUPPORTED, "float32 drafters support batch * block_len <= 32 (got %d)",
+                    batch * c.block_len);
     const DraftPlan p = plan_draft(c, batch, max_ctx);
     if (ws_bytes < p.total) return fail(DFLASH_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, p.total);
     if (((uintptr_t)ws) & 255) return fail(DFLASH_E_ARG, "workspace must be 256-byte aligned");
@@ -359,8 +368,8 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
         sq.start[0] = 0; sq.start[1] = qd; sq.start[2] = qd + kvd; sq.start[3] = qd + 2 * kvd;
         sq.n = 3;
         {
-            Timed t(h, gemm_kernel_name(p.qkv), st);
-            HIP_TRY(launch_gemm(p.qkv, u, H, M, sq, qd + 2 * kvd, H, part, st));
+            Timed t(h, gemm_kernel_name(p.qkv), st, qd + 2 * kvd, H);
+            HIP_TRY(launch_gemm(p.qkv, u, H, bf ? (size_t)M * H : 0, M, sq, qd + 2 * kvd, H, part, st));
         }
         {
             Timed t(h, "qkv_epilogue", st);
@@ -378,8 +387,8 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
             attn_out = o;
         }
         {
-            Timed t(h, gemm_kernel_name(p.oproj), st);
-            HIP_TRY(launch_gemm(p.oproj, attn_out, qd, M, segs1(lw.wo, H), H, qd, part, st));
+            Timed t(h, gemm_kernel_name(p.oproj), st, H, qd);
+            HIP_TRY(launch_gemm(p.oproj, attn_out, qd, bf ? (size_t)M * qd : 0, M, segs1(lw.wo, H), H, qd, part, st));
         }
         {
             Timed t(h, "resid_norm", st);
@@ -390,16 +399,16 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
         sg.start[0] = 0; sg.start[1] = c.ffn; sg.start[2] = 2 * c.ffn;
         sg.n = 2;
         {
-            Timed t(h, gemm_kernel_name(p.gateup), st);
-            HIP_TRY(launch_gemm(p.gateup, u, H, M, sg, 2 * c.ffn, H, part, st));
+            Timed t(h, gemm_kernel_name(p.gateup), st, 2 * c.ffn, H);
+            HIP_TRY(launch_gemm(p.gateup, u, H, bf ? (size_t)M * H : 0, M, sg, 2 * c.ffn, H, part, st));
         }
         {
             Timed t(h, "swiglu", st);
             HIP_TRY(launch_swiglu(bf, part, p.gateup.splits, M, c.ffn, a, st));
         }
         {
-            Timed t(h, gemm_kernel_name(p.down), st);
-            HIP_TRY(launch_gemm(p.down, a, c.ffn, M, segs1(lw.w_down, H), H, c.ffn, part, st));
+            Timed t(h, gemm_kernel_name(p.down), st, H, c.ffn);
+            HIP_TRY(launch_gemm(p.down, a, c.ffn, bf ? (size_t)M * c.ffn : 0, M, segs1(lw.w_down, H), H, c.ffn, part, st));
         }
         {
             const void* next_gain = l + 1 < c.n_layers ? h->layers[l + 1].attn_norm : h->w.final_norm;
@@ -414,7 +423,7 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
     }
     {
         Timed t(h, "head_merge", st);
-        HIP_TRY(launch_head_merge(M, c.vocab, top_k, hpart, block_tokens, tokens, topk_ids, topk_logprobs, err, st));
+        HIP_TRY(launch_head_merge(bf, M, c.vocab, top_k, hpart, block_tokens, tokens, topk_ids, topk_logprobs, err, st));
     }
     return DFLASH_OK;
 }
@@ -455,8 +464,8 @@ extern "C" int dflash_inject_ctx(dflash_handle* h, int batch, int n_rows, const 
         const char* x = (const char*)feats + (size_t)row0 * feat_row_stride * E;
         const GemmPlan fc = plan_gemm(bf, R, H, c.feat_dim);
         {
-            Timed t(h, gemm_kernel_name(fc), st);
-            HIP_TRY(launch_gemm(fc, x, (int)feat_row_stride, R, segs1(h->w.fc_w, H), H, c.feat_dim, part, st));
+            Timed t(h, gemm_kernel_name(fc), st, H, c.feat_dim);
+            HIP_TRY(launch_gemm(fc, x, (int)feat_row_stride, 0, R, segs1(h->w.fc_w, H), H, c.feat_dim, part, st));
         }
         {
             Timed t(h, "fuse_cast", st);
@@ -475,8 +484,8 @@ extern "C" int dflash_inject_ctx(dflash_handle* h, int batch, int n_rows, const 
             s.n = 2 * nl;
             const GemmPlan kp = plan_gemm(bf, R, 2 * nl * kvd, H);
             {
-                Timed t(h, gemm_kernel_name(kp), st);
-                HIP_TRY(launch_gemm(kp, f, H, R, s, 2 * nl * kvd, H, part, st));
+                Timed t(h, gemm_kernel_name(kp), st, 2 * nl * kvd, H);
+                HIP_TRY(launch_gemm(kp, f, H, bf ? (size_t)R * H : 0, R, s, 2 * nl * kvd, H, part, st));
             }
             {
                 Timed t(h, "kv_scatter", st);
@@ -518,7 +527,7 @@ extern "C" int dflash_linear(int dtype, int M, int N, int K, const void* x, int6
     if (ws_bytes < dflash_linear_workspace_bytes(dtype, M, N, K)) return fail(DFLASH_E_CAPACITY, "workspace too small");
     const GemmPlan p = plan_gemm(dtype == DFLASH_BF16, M, N, K);
     hipStream_t st = (hipStream_t)stream;
-    HIP_TRY(launch_gemm(p, x, (int)ldx, M, segs1(w, N), N, K, (float*)ws, st));
+    HIP_TRY(launch_gemm(p, x, (int)ldx, 0, M, segs1(w, N), N, K, (float*)ws, st));
     HIP_TRY(launch_reduce_cast(0, (float*)ws, p.splits, M, N, nullptr, y, st));
     return DFLASH_OK;
 }

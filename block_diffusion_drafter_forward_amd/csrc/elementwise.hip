@@ -8,81 +8,119 @@
 namespace df {
 
 // ------------------------------------------------------------------------------------------------------
-// embedding + first RMSNorm
+// row kernels: 1024 threads per block row, four consecutive columns per thread and pass (H <= 16384)
 // ------------------------------------------------------------------------------------------------------
+#define ROW_THREADS 1024
+#define ROW_PASSES 4
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ void st4(float* p, float4 v) { *(float4*)p = v; }
+__device__ __forceinline__ float4 ld4(const bf16_t* p) {
+    const uint2 b = *(const uint2*)p;
+    return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u), __uint_as_float(b.y << 16),
+                       __uint_as_float(b.y & 0xFFFF0000u));
+}
+// four consecutive activations: a pair of bfloat16 planes, or float32
+__device__ __forceinline__ void st4_act(bf16_t* p, size_t plane, float4 v) {
+    uint2 hb, lb;
+    const bf16_t h0 = f2bf(v.x), h1 = f2bf(v.y), h2 = f2bf(v.z), h3 = f2bf(v.w);
+    hb.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    hb.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
+    lb.x = (uint32_t)f2bf(v.x - bf2f(h0)) | ((uint32_t)f2bf(v.y - bf2f(h1)) << 16);
+    lb.y = (uint32_t)f2bf(v.z - bf2f(h2)) | ((uint32_t)f2bf(v.w - bf2f(h3)) << 16);
+    *(uint2*)p = hb;
+    *(uint2*)(p + plane) = lb;
+}
+__device__ __forceinline__ void st4_act(float* p, size_t, float4 v) { *(float4*)p = v; }
+__device__ __forceinline__ float4 add4(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+__device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
+
+// u = RMSNorm(v) * g for the row values held in registers (u stored as an activation pair)
+template <typename T>
+__device__ __forceinline__ void norm_store(const float4 (&v)[ROW_PASSES], float ss, int H, const T* __restrict__ gain,
+                                           float eps, T* __restrict__ urow, size_t plane, float* red) {
+    ss = block_sum(ss, red);
+    const float rs = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+    for (int q = 0; q < ROW_PASSES; ++q) {
+        const int j = (threadIdx.x + q * ROW_THREADS) * 4;
+        if (j >= H) break;
+        const float4 g = ld4(gain + j);
+        st4_act(urow + j, plane,
+                make_float4(v[q].x * rs * g.x, v[q].y * rs * g.y, v[q].z * rs * g.z, v[q].w * rs * g.w));
+    }
+}
+
 // Block row m gathers its token's embedding row (the drafter shares the target's frozen embedding), keeps it
 // as the float32 residual, and writes u = RMSNorm(h) * g.  Block 0 clears the call's device error word
 // before any later kernel can set a flag; an out-of-range token reads row 0 (flagged later by head_merge).
 template <typename T>
-__global__ __launch_bounds__(256) void embed_norm(const int32_t* __restrict__ tok, int V, const T* __restrict__ embed,
-                                                  const T* __restrict__ gain, int H, float eps, float* __restrict__ h,
-                                                  T* __restrict__ u, float* __restrict__ tap, uint32_t* err) {
-    __shared__ float red[4];
+__global__ __launch_bounds__(ROW_THREADS) void embed_norm(const int32_t* __restrict__ tok, int V,
+                                                          const T* __restrict__ embed, const T* __restrict__ gain, int H,
+                                                          float eps, float* __restrict__ h, T* __restrict__ u,
+                                                          float* __restrict__ tap, uint32_t* err) {
+    __shared__ float red[ROW_THREADS / 64];
     const int m = blockIdx.x;
     if (m == 0 && threadIdx.x == 0 && err) *err = 0u;
     int t = tok[m];
     if (t < 0 || t >= V) t = 0;
     const T* e = embed + (size_t)t * H;
+    float4 v[ROW_PASSES];
     float ss = 0.f;
-    for (int j = threadIdx.x; j < H; j += 256) {
-        float v = Act<T>::load(e + j);
-        h[(size_t)m * H + j] = v;
-        if (tap) tap[(size_t)m * H + j] = v;
-        ss += v * v;
+#pragma unroll
+    for (int q = 0; q < ROW_PASSES; ++q) {
+        const int j = (threadIdx.x + q * ROW_THREADS) * 4;
+        if (j >= H) break;
+        v[q] = ld4(e + j);
+        st4(h + (size_t)m * H + j, v[q]);
+        if (tap) st4(tap + (size_t)m * H + j, v[q]);
+        ss += dot4(v[q]);
     }
-    ss = block_sum(ss, red);
-    const float rs = 1.0f / sqrtf(ss / (float)H + eps);
-    for (int j = threadIdx.x; j < H; j += 256) {
-        float v = h[(size_t)m * H + j];
-        u[(size_t)m * H + j] = Act<T>::from(v * rs * Act<T>::load(gain + j));
-    }
+    norm_store(v, ss, H, gain, eps, u + (size_t)m * H, (size_t)gridDim.x * H, red);
 }
 
 hipError_t launch_embed_norm(int bf16, const int32_t* tok, int M, int V, const void* embed, const void* gain, int H,
                              float eps, float* h, void* u, float* tap, uint32_t* err, hipStream_t st) {
     if (bf16)
-        hipLaunchKernelGGL(embed_norm<bf16_t>, dim3(M), dim3(256), 0, st, tok, V, (const bf16_t*)embed,
+        hipLaunchKernelGGL(embed_norm<bf16_t>, dim3(M), dim3(ROW_THREADS), 0, st, tok, V, (const bf16_t*)embed,
                            (const bf16_t*)gain, H, eps, h, (bf16_t*)u, tap, err);
     else
-        hipLaunchKernelGGL(embed_norm<float>, dim3(M), dim3(256), 0, st, tok, V, (const float*)embed,
+        hipLaunchKernelGGL(embed_norm<float>, dim3(M), dim3(ROW_THREADS), 0, st, tok, V, (const float*)embed,
                            (const float*)gain, H, eps, h, (float*)u, tap, err);
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------------------------------------------------
-// residual add of a split-K product + RMSNorm
-// ------------------------------------------------------------------------------------------------------
+// h += sum over splits of a GEMM product (fixed order), then u = RMSNorm(h) * g.
 template <typename T>
-__global__ __launch_bounds__(256) void resid_norm(const float* __restrict__ part, int S, int M, int H,
-                                                  float* __restrict__ h, const T* __restrict__ gain, float eps,
-                                                  T* __restrict__ u, float* __restrict__ tap) {
-    __shared__ float red[4];
+__global__ __launch_bounds__(ROW_THREADS) void resid_norm(const float* __restrict__ part, int S, int M, int H,
+                                                          float* __restrict__ h, const T* __restrict__ gain, float eps,
+                                                          T* __restrict__ u, float* __restrict__ tap) {
+    __shared__ float red[ROW_THREADS / 64];
     const int m = blockIdx.x;
+    float4 v[ROW_PASSES];
     float ss = 0.f;
-    for (int j = threadIdx.x; j < H; j += 256) {
-        float a = 0.f;
-        for (int s = 0; s < S; ++s) a += part[((size_t)s * M + m) * H + j];
-        float v = h[(size_t)m * H + j] + a;
-        h[(size_t)m * H + j] = v;
-        if (tap) tap[(size_t)m * H + j] = v;
-        ss += v * v;
+#pragma unroll
+    for (int q = 0; q < ROW_PASSES; ++q) {
+        const int j = (threadIdx.x + q * ROW_THREADS) * 4;
+        if (j >= H) break;
+        float4 a = ld4(part + (size_t)m * H + j);
+        for (int s = 1; s < S; ++s) a = add4(a, ld4(part + ((size_t)s * M + m) * H + j));
+        v[q] = add4(ld4(h + (size_t)m * H + j), a);
+        st4(h + (size_t)m * H + j, v[q]);
+        if (tap) st4(tap + (size_t)m * H + j, v[q]);
+        ss += dot4(v[q]);
     }
-    ss = block_sum(ss, red);
-    const float rs = 1.0f / sqrtf(ss / (float)H + eps);
-    for (int j = threadIdx.x; j < H; j += 256) {
-        float v = h[(size_t)m * H + j];
-        u[(size_t)m * H + j] = Act<T>::from(v * rs * Act<T>::load(gain + j));
-    }
+    norm_store(v, ss, H, gain, eps, u + (size_t)m * H, (size_t)M * H, red);
 }
 
 hipError_t launch_resid_norm(int bf16, const float* part, int S, int M, int H, float* h, const void* gain, float eps,
                              void* u, float* tap, hipStream_t st) {
     if (bf16)
-        hipLaunchKernelGGL(resid_norm<bf16_t>, dim3(M), dim3(256), 0, st, part, S, M, H, h, (const bf16_t*)gain, eps,
-                           (bf16_t*)u, tap);
+        hipLaunchKernelGGL(resid_norm<bf16_t>, dim3(M), dim3(ROW_THREADS), 0, st, part, S, M, H, h, (const bf16_t*)gain,
+                           eps, (bf16_t*)u, tap);
     else
-        hipLaunchKernelGGL(resid_norm<float>, dim3(M), dim3(256), 0, st, part, S, M, H, h, (const float*)gain, eps,
-                           (float*)u, tap);
+        hipLaunchKernelGGL(resid_norm<float>, dim3(M), dim3(ROW_THREADS), 0, st, part, S, M, H, h, (const float*)gain,
+                           eps, (float*)u, tap);
     return hipGetLastError();
 }
 
@@ -123,21 +161,23 @@ __global__ __launch_bounds__(256) void qkv_epilogue(const float* __restrict__ pa
         c += part[((size_t)s * M + m) * N + c2];
     }
     const int pos = ctx_len[b] + row;
+    const size_t qplane = (size_t)M * nq * d, bplane = (size_t)B * nkv * 16 * d;
     if (hd < nq) {
         rope_pair(a, c, pos, i, rf);
-        q[(size_t)m * nq * d + hd * d + i] = Act<T>::from(a);
-        q[(size_t)m * nq * d + hd * d + i + half] = Act<T>::from(c);
+        const size_t o = (size_t)m * nq * d + hd * d + i;
+        put_act(q, qplane, o, a);
+        put_act(q, qplane, o + half, c);
     } else if (hd < nq + nkv) {
         const int kh = hd - nq;
         rope_pair(a, c, pos, i, rf);
-        T* dst = kb + (((size_t)b * nkv + kh) * 16 + row) * d;
-        dst[i] = Act<T>::from(a);
-        dst[i + half] = Act<T>::from(c);
+        const size_t o = (((size_t)b * nkv + kh) * 16 + row) * d + i;
+        put_act(kb, bplane, o, a);
+        put_act(kb, bplane, o + half, c);
     } else {
         const int kh = hd - nq - nkv;
-        T* dst = vbt + ((size_t)b * nkv + kh) * d * 16;
-        dst[i * 16 + row] = Act<T>::from(a);
-        dst[(i + half) * 16 + row] = Act<T>::from(c);
+        const size_t o = ((size_t)b * nkv + kh) * d * 16 + row;
+        put_act(vbt, bplane, o + (size_t)i * 16, a);
+        put_act(vbt, bplane, o + (size_t)(i + half) * 16, c);
     }
 }
 
@@ -170,7 +210,7 @@ __global__ __launch_bounds__(256) void swiglu(const float* __restrict__ part, in
         up += part[((size_t)s * M + m) * N + F + j];
     }
     const float silu = g / (1.0f + expf(-g));
-    a[idx] = Act<T>::from(silu * up);
+    put_act(a, (size_t)M * F, idx, silu * up);
 }
 
 hipError_t launch_swiglu(int bf16, const float* part, int S, int M, int F, void* a, hipStream_t st) {
@@ -190,7 +230,7 @@ __global__ __launch_bounds__(256) void reduce_cast(const float* __restrict__ par
     float v = 0.f;
     for (int s = 0; s < S; ++s) v += part[(size_t)s * M * N + idx];
     if (bias) v += Act<T>::load(bias + n);
-    out[idx] = Act<T>::from(v);
+    put_act(out, (size_t)M * N, idx, v);
 }
 
 hipError_t launch_reduce_cast(int bf16, const float* part, int S, int M, int N, const void* bias, void* out,

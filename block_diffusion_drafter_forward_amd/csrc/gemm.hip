@@ -9,6 +9,7 @@
 // consumer of the product (an epilogue kernel) sums the splits in a fixed order, so results are
 // deterministic.
 #include "common.h"
+#include "gemm_core.h"
 #include "kernels.h"
 
 namespace df {
@@ -20,9 +21,11 @@ namespace df {
 // [k0 + w * kpw, k0 + (w + 1) * kpw) of the workgroup's split.  Per 256-wide k-chunk a lane loads, for each
 // n-tile, eight 16-byte pieces of one weight row (A operand: row = lane % 16, k = 32 j + 8 (lane / 16)) and
 // the matching eight pieces of its activation row (B operand), then issues 8 MFMAs per (n-tile, m-tile).
-template <int MT>
-__global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict__ x, int ldx, int M, Segs w,
-                                                        int N, int K, int kpw, float* __restrict__ part) {
+// With SPLIT the activation is a pair of bfloat16 planes (x = hi + lo, lo plane at x + xplane) and every
+// weight fragment meets both: two MFMAs, one weight load.
+template <int MT, bool SPLIT>
+__global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict__ x, int ldx, size_t xplane, int M,
+                                                        Segs w, int N, int K, int kpw, float* __restrict__ part) {
     constexpr int NT = 4;
     __shared__ f32x4 red[4][NT * MT][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -51,21 +54,28 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict
     for (int kc = kb; kc < ke; kc += 256) {
         u32x4 wf[NT][8];
         u32x4 xf[MT][8];
+        u32x4 xl[SPLIT ? MT : 1][8];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int j = 0; j < 8; ++j) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                wf[nt][j] = ld16_nt(wrow[nt] + kc + j * 32);
+            for (int nt = 0; nt < NT; ++nt) wf[nt][j] = ld16_nt(wrow[nt] + kc + j * 32);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) xf[mt][j] = ld16(xrow[mt] + kc + j * 32);
+            for (int mt = 0; mt < MT; ++mt) {
+                xf[mt][j] = ld16(xrow[mt] + kc + j * 32);
+                if (SPLIT) xl[SPLIT ? mt : 0][j] = ld16(xrow[mt] + xplane + kc + j * 32);
+            }
+        }
+        // issue every load of the chunk before the first MFMA: 32 KB of weights in flight per wave
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = mfma16(wf[nt][j], xf[mt][j], acc[nt][mt]);
+                for (int mt = 0; mt < MT; ++mt) {
+                    acc[nt][mt] = mfma16(wf[nt][j], xf[mt][j], acc[nt][mt]);
+                    if (SPLIT) acc[nt][mt] = mfma16(wf[nt][j], xl[SPLIT ? mt : 0][j], acc[nt][mt]);
+                }
     }
 
 #pragma unroll
@@ -96,81 +106,20 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict
 }
 
 // ------------------------------------------------------------------------------------------------------
-// LDS-tiled MFMA GEMM (bfloat16) for large M
+// LDS-tiled MFMA GEMM (bfloat16) for large M; the main loop lives in gemm_core.h (shared with the LM head)
 // ------------------------------------------------------------------------------------------------------
-// Tile 128 (n) x 128 (m) x 64 (k); 4 waves in a 2 x 2 grid, each owning 64 x 64 = 4 x 4 MFMA tiles.  The
-// next k-tile is fetched into registers while the current one is consumed from LDS (one barrier pair per
-// k-tile).  Rows are padded to 72 elements in LDS to spread the 16-byte reads over the banks.
-#define TL_BN 128
-#define TL_BM 128
-#define TL_BK 64
-#define TL_LD (TL_BK + 8)
-
-__global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict__ x, int ldx, int M, Segs w,
-                                                       int N, int K, int kps, float* __restrict__ part) {
+template <bool SPLIT>
+__global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict__ x, int ldx, size_t xplane, int M,
+                                                       Segs w, int N, int K, int kps, float* __restrict__ part) {
     __shared__ __attribute__((aligned(16))) bf16_t sw[TL_BN * TL_LD];
-    __shared__ __attribute__((aligned(16))) bf16_t sx[TL_BM * TL_LD];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ __attribute__((aligned(16))) bf16_t sx[(SPLIT ? 2 : 1) * TL_BM * TL_LD];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int wn = wave >> 1, wm = wave & 1;
     const int n0 = blockIdx.x * TL_BN, m0 = blockIdx.y * TL_BM, s = blockIdx.z;
     const int kb = s * kps, ke = min(K, kb + kps);
-
-    // global -> register staging: each thread moves 4 pieces of 16 bytes of W and of x per k-tile
-    const bf16_t* wsrc[4];
-    const bf16_t* xsrc[4];
-    int lrow[4], lcol[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int c = tid + 256 * i;
-        lrow[i] = c >> 3;
-        lcol[i] = (c & 7) * 8;
-        wsrc[i] = (const bf16_t*)seg_row(w, min(n0 + lrow[i], N - 1), K, 2) + lcol[i];
-        xsrc[i] = x + (size_t)min(m0 + lrow[i], M - 1) * ldx + lcol[i];
-    }
-    u32x4 pw[4], px[4];
-    auto fetch = [&](int k) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pw[i] = ld16_nt(wsrc[i] + k);
-            px[i] = ld16(xsrc[i] + k);
-        }
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *(u32x4*)(sw + lrow[i] * TL_LD + lcol[i]) = pw[i];
-            *(u32x4*)(sx + lrow[i] * TL_LD + lcol[i]) = px[i];
-        }
-    };
-
     f32x4 acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (kb < ke) fetch(kb);
-    for (int k = kb; k < ke; k += TL_BK) {
-        __syncthreads();
-        stash();
-        __syncthreads();
-        if (k + TL_BK < ke) fetch(k + TL_BK);
-#pragma unroll
-        for (int ks = 0; ks < TL_BK / 32; ++ks) {
-            u32x4 af[4], bfr[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                af[t] = ld16(sw + (wn * 64 + t * 16 + r) * TL_LD + ks * 32 + g * 8);
-                bfr[t] = ld16(sx + (wm * 64 + t * 16 + r) * TL_LD + ks * 32 + g * 8);
-            }
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = mfma16(af[a], bfr[b], acc[a][b]);
-        }
-    }
-
+    tiled_mainloop<SPLIT>(x, ldx, xplane, M, w, N, K, n0, m0, kb, ke, sw, sx, acc);
     // D lane l: n = 4 (l / 16) + i, m = l % 16 within each 16 x 16 tile
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -234,14 +183,14 @@ GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K) {
     }
     if (M <= 32) {
         p.kind = M <= 16 ? GEMM_SKINNY1 : GEMM_SKINNY2;
+        // Each wave streams kpw of K for 64 columns (32 KB of weights per 256-wide chunk).  Measured on
+        // MI355X at the drafter's shapes: one chunk per wave is best unless a longer range still leaves
+        // enough workgroups to cover the chip (>= ~700 for two chunks, >= ~2000 for four).
         const int groups = (N + 63) / 64;
-        const int chunks = (K + 255) / 256;             // 256-wide k-chunks
-        // aim for >= 512 workgroups (2 per CU, 8 waves per CU) with at least one chunk per wave
-        int want = (512 + groups - 1) / groups;
-        int max_splits = (chunks + 3) / 4;
-        int splits = want < 1 ? 1 : (want > max_splits ? max_splits : want);
-        int kpw_chunks = (chunks + 4 * splits - 1) / (4 * splits);
-        p.kpw = kpw_chunks * 256;
+        auto wgs = [&](int kpw) { return groups * ((K + 4 * kpw - 1) / (4 * kpw)); };
+        p.kpw = 256;
+        if (K % 1024 == 0 && wgs(1024) >= 2000) p.kpw = 1024;
+        else if (K % 512 == 0 && wgs(512) >= 700) p.kpw = 512;
         p.splits = (K + 4 * p.kpw - 1) / (4 * p.kpw);
         return p;
     }
@@ -256,20 +205,30 @@ GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K) {
     return p;
 }
 
-hipError_t launch_gemm(const GemmPlan& p, const void* x, int ldx, int M, const Segs& w, int N, int K, float* part,
-                       hipStream_t st) {
+hipError_t launch_gemm(const GemmPlan& p, const void* x, int ldx, size_t xplane, int M, const Segs& w, int N, int K,
+                       float* part, hipStream_t st) {
+    const bool split = xplane != 0;
+    const dim3 gs((N + 63) / 64, p.splits);
+    const dim3 gt((N + TL_BN - 1) / TL_BN, (M + TL_BM - 1) / TL_BM, p.splits);
+    const bf16_t* xb = (const bf16_t*)x;
     switch (p.kind) {
         case GEMM_SKINNY1:
-            hipLaunchKernelGGL(gemm_skinny_bf16<1>, dim3((N + 63) / 64, p.splits), dim3(256), 0, st,
-                               (const bf16_t*)x, ldx, M, w, N, K, p.kpw, part);
+            if (split)
+                hipLaunchKernelGGL((gemm_skinny_bf16<1, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kpw, part);
+            else
+                hipLaunchKernelGGL((gemm_skinny_bf16<1, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kpw, part);
             break;
         case GEMM_SKINNY2:
-            hipLaunchKernelGGL(gemm_skinny_bf16<2>, dim3((N + 63) / 64, p.splits), dim3(256), 0, st,
-                               (const bf16_t*)x, ldx, M, w, N, K, p.kpw, part);
+            if (split)
+                hipLaunchKernelGGL((gemm_skinny_bf16<2, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kpw, part);
+            else
+                hipLaunchKernelGGL((gemm_skinny_bf16<2, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kpw, part);
             break;
         case GEMM_TILED:
-            hipLaunchKernelGGL(gemm_tiled_bf16, dim3((N + TL_BN - 1) / TL_BN, (M + TL_BM - 1) / TL_BM, p.splits),
-                               dim3(256), 0, st, (const bf16_t*)x, ldx, M, w, N, K, p.kps, part);
+            if (split)
+                hipLaunchKernelGGL((gemm_tiled_bf16<true>), gt, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kps, part);
+            else
+                hipLaunchKernelGGL((gemm_tiled_bf16<false>), gt, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kps, part);
             break;
         case GEMM_F32:
             hipLaunchKernelGGL(gemm_f32, dim3((N + 3) / 4), dim3(256), 0, st, (const float*)x, ldx, M, w, N, K, part);

@@ -1,0 +1,90 @@
+// Main loop of the LDS-tiled MFMA GEMM, shared by the large-M projection kernel and the large-M LM head.
+#pragma once
+
+#include "common.h"
+
+// ------------------------------------------------------------------------------------------------------
+// LDS-tiled MFMA GEMM (bfloat16) for large M
+// ------------------------------------------------------------------------------------------------------
+// Tile 128 (n) x 128 (m) x 64 (k); 4 waves in a 2 x 2 grid, each owning 64 x 64 = 4 x 4 MFMA tiles.  The
+// next k-tile is fetched into registers while the current one is consumed from LDS (one barrier pair per
+// k-tile).  Rows are padded to 72 elements in LDS to spread the 16-byte reads over the banks.
+#define TL_BN 128
+#define TL_BM 128
+#define TL_BK 64
+#define TL_LD (TL_BK + 8)
+
+// Main loop of the tiled kernel: acc[a][b] (n-tile a, m-tile b of this wave's 64 x 64 block) for the k-range
+// [kb, ke).  sw / sx are LDS staging buffers of TL_BN * TL_LD and TL_BM * TL_LD elements.
+// With SPLIT the activation is a pair of bfloat16 planes (lo plane at x + xplane): sx holds both planes
+// (2 * TL_BM * TL_LD elements) and every weight fragment meets hi and lo.
+template <bool SPLIT>
+static __device__ __forceinline__ void tiled_mainloop(const bf16_t* __restrict__ x, int ldx, size_t xplane, int M,
+                                                      const Segs& w, int N, int K, int n0, int m0, int kb, int ke,
+                                                      bf16_t* sw, bf16_t* sx, f32x4 (&acc)[4][4]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int wn = wave >> 1, wm = wave & 1;
+    // global -> register staging: each thread moves 4 pieces of 16 bytes of W and of x per k-tile
+    const bf16_t* wsrc[4];
+    const bf16_t* xsrc[4];
+    int lrow[4], lcol[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = tid + 256 * i;
+        lrow[i] = c >> 3;
+        lcol[i] = (c & 7) * 8;
+        wsrc[i] = (const bf16_t*)seg_row(w, min(n0 + lrow[i], N - 1), K, 2) + lcol[i];
+        xsrc[i] = x + (size_t)min(m0 + lrow[i], M - 1) * ldx + lcol[i];
+    }
+    constexpr int XP = SPLIT ? 2 : 1;
+    u32x4 pw[4], px[XP][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (kb < ke) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pw[i] = ld16_nt(wsrc[i] + kb);
+#pragma unroll
+            for (int pl = 0; pl < XP; ++pl) px[pl][i] = ld16(xsrc[i] + pl * xplane + kb);
+        }
+    }
+    for (int k = kb; k < ke; k += TL_BK) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *(u32x4*)(sw + lrow[i] * TL_LD + lcol[i]) = pw[i];
+#pragma unroll
+            for (int pl = 0; pl < XP; ++pl) *(u32x4*)(sx + (pl * TL_BM + lrow[i]) * TL_LD + lcol[i]) = px[pl][i];
+        }
+        __syncthreads();
+        if (k + TL_BK < ke) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pw[i] = ld16_nt(wsrc[i] + k + TL_BK);
+#pragma unroll
+                for (int pl = 0; pl < XP; ++pl) px[pl][i] = ld16(xsrc[i] + pl * xplane + k + TL_BK);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < TL_BK / 32; ++ks) {
+            u32x4 af[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) af[t] = ld16(sw + (wn * 64 + t * 16 + r) * TL_LD + ks * 32 + g * 8);
+#pragma unroll
+            for (int pl = 0; pl < XP; ++pl) {
+                u32x4 bfr[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    bfr[t] = ld16(sx + (pl * TL_BM + wm * 64 + t * 16 + r) * TL_LD + ks * 32 + g * 8);
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) acc[a][b] = mfma16(af[a], bfr[b], acc[a][b]);
+            }
+        }
+    }
+}
+

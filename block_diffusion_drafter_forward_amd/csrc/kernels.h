@@ -17,8 +17,9 @@ struct GemmPlan {
     int kps;     // tiled: k-range per split (multiple of 64)
 };
 GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K);
-hipError_t launch_gemm(const GemmPlan& p, const void* x, int ldx, int M, const Segs& w, int N, int K, float* part,
-                       hipStream_t st);
+// xplane != 0: x is an activation pair of bfloat16 planes (lo plane xplane elements after hi).
+hipError_t launch_gemm(const GemmPlan& p, const void* x, int ldx, size_t xplane, int M, const Segs& w, int N, int K,
+                       float* part, hipStream_t st);
 const char* gemm_kernel_name(const GemmPlan& p);
 
 // ---- row-wise kernels ------------------------------------------------------------------------------------
@@ -53,7 +54,7 @@ hipError_t launch_copy(void* dst, const void* src, size_t n16, hipStream_t st);
 // ---- attention -------------------------------------------------------------------------------------------
 struct AttnPlan {
     int n_chunks;      // context chunks (the block itself is one more chunk)
-    int chunk_tokens;  // multiple of 32
+    int chunk_tokens;  // multiple of 64
 };
 AttnPlan plan_attention(int batch, int n_kv, int max_ctx);
 size_t attn_partial_floats(int batch, int nq, int n_chunks, int d);
@@ -65,12 +66,13 @@ hipError_t launch_attn_merge(int bf16, const AttnPlan& p, int B, int L, int nq, 
                              const float* mlpart, void* o, hipStream_t st);
 
 // ---- LM head ---------------------------------------------------------------------------------------------
-int head_groups(int V);  // vocabulary groups of 64 columns (one workgroup each)
-size_t head_partial_floats(int V, int M);
+int head_group_width(int bf16, int M);  // vocabulary columns per record group (64 or 128)
+int head_groups(int V, int width);
+size_t head_partial_floats(int bf16, int V, int M);
 hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V, int K, float* hpart,
                           float* logits_dbg, hipStream_t st);
 // Also flags block tokens outside [0, V) in the device error word.
-hipError_t launch_head_merge(int M, int V, int top_k, const float* hpart, const int32_t* block_tokens,
+hipError_t launch_head_merge(int bf16, int M, int V, int top_k, const float* hpart, const int32_t* block_tokens,
                              int32_t* tokens, int32_t* topk_ids, float* topk_lp, uint32_t* err, hipStream_t st);
 
 }  // namespace df

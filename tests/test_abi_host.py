@@ -117,13 +117,21 @@ def _draft(D, h, **over):
     (dict(kv=None), -1),
     (dict(ws_bytes=100), -3),
     (dict(ws=0x100010), -1),          # misaligned workspace
-    (dict(batch=3), -4),              # 48 block rows: not supported by the fused head yet
 ])
 def test_draft_block_validation(D, over, code):
     m = _create(D, _shape())
     try:
         assert _draft(D, m.handle, **over) == code
         assert D.dflash_last_error()
+    finally:
+        m.close()
+
+
+def test_float32_drafter_limits_block_rows(D):
+    import workloads as W
+    m = _create(D, W.SMALL_FP32)                      # block_len 5: 7 requests = 35 rows > 32
+    try:
+        assert _draft(D, m.handle, batch=7, max_ctx=40) == D.DFLASH_E_UNSUPPORTED
     finally:
         m.close()
 

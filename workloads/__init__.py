@@ -314,6 +314,9 @@ SMALL = [
     Workload(103, "small-fp32-b2", SMALL_FP32, 2, None, (0, 40), True, 0.9, None, top_k=3),
     Workload(104, "small-bf16-edge-b2", SMALL_BF16, 2, None, None, True, 0.9, None, top_k=1, ctx_fixed=(0, 33)),
     Workload(105, "small-bf16-long-b1", SMALL_BF16, 1, 1000, None, True, 0.8, None),
+    # more than 32 block rows: tiled GEMMs and the tiled LM head (two row tiles, ragged)
+    Workload(106, "small-bf16-serve9", SMALL_BF16, 9, None, (0, 400), True, None, (0.6, 0.95)),
+    Workload(107, "small-gqa8-b3", SMALL_GQA8, 3, None, (1, 70), True, 0.7, None, top_k=5),
 ]
 
 
