@@ -36,30 +36,88 @@ def parse():
     p.add_argument("--workload", default="qwen3-8b-shape")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-s", type=float, default=30.0, help="cap on CPU oracle work (seconds)")
+    p.add_argument("--graph", type=int, default=1,
+                   help="1: also time the step replayed as a captured HIP graph (reported beside the eager value)")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run the library's stream-copy kernel on 1 GiB (HBM-counter calibration)")
     return p.parse_args()
 
 
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None if there is
+    none or the kernel's source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256_16"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    csrc = os.path.join(ROOT, "block_diffusion_drafter_forward_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    if fields.get("source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
+def copy_probe():
+    """Copy 1 GiB with dflash_copy 10 times: known bytes for calibrating FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    from block_diffusion_drafter_forward_amd import dflash as D
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    st = torch.cuda.current_stream()
+    for _ in range(2):
+        D.check(D.dflash_copy(b.data_ptr(), a.data_ptr(), n, st.cuda_stream), "copy")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(10):
+        D.check(D.dflash_copy(b.data_ptr(), a.data_ptr(), n, st.cuda_stream), "copy")
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
+                      "gbs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
+
+
 def algorithmic_bytes(s, batch, ctx_total, n_new):
-    """Bytes one step must move at least once, per kernel family (weights read once, context K/V read once,
-    activations counted where they are read or written)."""
+    """Bytes one step must move at least once: weights read once, context K/V read once, activations
+    counted where they are read (as hi/lo pairs, 4 bytes per element) or written (float32 products)."""
     E = 2 if s.bf16 else 4
     H, qd, kvd, F, V = s.hidden, s.q_dim, s.kv_dim, s.ffn, s.vocab
     M = batch * s.block_len
-    per = {}
-    gemm = 0
-    # inject: fc over n_new rows, then all layers' U_K / U_V
-    gemm += H * s.feat_dim * E + n_new * s.feat_dim * E + n_new * H * 4
-    gemm += s.n_layers * 2 * kvd * H * E + n_new * H * E + n_new * s.n_layers * 2 * kvd * 4
+    gemms = [(H, s.feat_dim, n_new, E), (s.n_layers * 2 * kvd, H, n_new, 4)]
     for _ in range(s.n_layers):
-        gemm += (qd + 2 * kvd) * H * E + M * H * E + M * (qd + 2 * kvd) * 4     # QKV
-        gemm += H * qd * E + M * qd * E + M * H * 4                               # O
-        gemm += 2 * F * H * E + M * H * E + M * 2 * F * 4                         # gate/up
-        gemm += H * F * E + M * F * E + M * H * 4                                 # down
-    per["gemm"] = gemm
-    per["attn"] = s.n_layers * (ctx_total * 2 * kvd * E + M * (qd + 2 * kvd) * E + M * qd * 4)
-    per["lm_head"] = V * H * E + M * H * E
-    per["total"] = sum(per.values())
-    return per
+        gemms += [(qd + 2 * kvd, H, M, 4), (H, qd, M, 4), (2 * F, H, M, 4), (H, F, M, 4)]
+    total = sum(N * K * E + m * K * xe + m * N * 4 for N, K, m, xe in gemms)
+    total += s.n_layers * (ctx_total * 2 * kvd * E + M * (qd + 2 * kvd) * 4 + M * qd * 4)
+    total += V * H * E + M * H * 4
+    return total
+
+
+def launch_bytes(name, s, batch, ctx_total):
+    """Algorithmic bytes of one launch of a profiled kernel (0 for kernels outside the roofline)."""
+    E = 2 if s.bf16 else 4
+    M = batch * s.block_len
+    if name.startswith("gemm_"):
+        parts = dict(kv.split("=") for kv in name.split()[1:])
+        N, K = int(parts["N"]), int(parts["K"])
+        pair = name.split()[0].endswith("_pair")
+        # the two inject GEMMs (fusion, stacked U_K/U_V) run on the newly committed rows only
+        m = N_NEW * batch if (K == s.feat_dim or N == s.n_layers * 2 * s.kv_dim) else M
+        return N * K * E + m * K * (4 if pair else E) + m * N * 4
+    if name.startswith("attn_bf16") or name == "attn_f32":
+        return ctx_total * 2 * s.kv_dim * E + M * (s.q_dim + 2 * s.kv_dim) * 4 + M * s.q_dim * 4
+    if name.startswith("lm_head"):
+        return s.vocab * s.hidden * E + M * s.hidden * 4
+    return 0
 
 
 def cpu_baseline(wl, weights, n_new, cap_s):
@@ -95,6 +153,9 @@ def cpu_baseline(wl, weights, n_new, cap_s):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -154,7 +215,34 @@ def main():
         step()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step_eager = e0.elapsed_time(e1) / args.steps
+    ms_step = ms_step_eager
+    ms_step_graph = None
+    if args.graph:
+        # one step captured as a HIP graph (the library enqueues no memset or allocation), replayed per step
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                g.model.inject(feats_d, offs_d, start_d, g.page_table, g.kv, inj_ws, stream=cap)
+                g.draft(stream=cap)
+                g.accept(target, stream=cap)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        ref_tokens = g.tokens.clone()
+        e0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_step_graph = e0.elapsed_time(e1) / args.steps
+        step()  # eager step: the replays must leave the same drafts as eager execution
+        torch.cuda.synchronize()
+        assert torch.equal(ref_tokens, g.tokens), "graph replay and eager drafts differ"
 
     # the drafter pass alone
     for _ in range(3):
@@ -179,20 +267,26 @@ def main():
     kernels = {n: {"launches_per_step": c / prof_steps, "avg_us": 1e3 * t / c, "total_us_per_step": 1e3 * t / prof_steps}
                for n, c, t in stats}
 
-    ab = algorithmic_bytes(s, wl.batch, int(ctx.sum()), n_new)
-    fam = {"gemm": [n for n in kernels if n.startswith("gemm_")],
-           "attn": [n for n in kernels if n.startswith("attn_bf16") or n == "attn_f32"],
-           "lm_head": [n for n in kernels if n.startswith("lm_head")]}
-    fam_time = {f: sum(kernels[n]["total_us_per_step"] for n in ns) for f, ns in fam.items()}
-    dom = max(fam_time, key=fam_time.get)
-    launches = sum(kernels[n]["launches_per_step"] for n in fam[dom])
-    bytes_per_launch = ab[dom] / launches
-    avg_us = fam_time[dom] / launches
-    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    total_bytes = algorithmic_bytes(s, wl.batch, int(ctx.sum()), n_new)
+    groups = {}
+    for n, d in kernels.items():
+        nb = launch_bytes(n, s, wl.batch, int(ctx.sum()))
+        if nb == 0:
+            continue
+        gname = n.split(" ")[0]
+        gsum = groups.setdefault(gname, {"bytes": 0.0, "us": 0.0, "launches": 0.0})
+        gsum["bytes"] += nb * d["launches_per_step"]
+        gsum["us"] += d["total_us_per_step"]
+        gsum["launches"] += d["launches_per_step"]
+    dom = max(groups, key=lambda k: groups[k]["us"])
+    gd = groups[dom]
+    achieved = gd["bytes"] / (gd["us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": ",".join(sorted({n.split(" ")[0] for n in fam[dom]})), "bytes_per_launch": int(bytes_per_launch),
-                "avg_launch_us": round(avg_us, 2)}
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(dom, wl.name), "kernel": dom,
+                "bytes_per_launch": int(gd["bytes"] / gd["launches"]),
+                "avg_launch_us": round(gd["us"] / gd["launches"], 2), "launches_per_step": gd["launches"]}
+    per_kernel_roofline = {k: {"gbs": round(v["bytes"] / (v["us"] * 1e-6) / 1e9, 1), "us_per_step": round(v["us"], 1)}
+                           for k, v in groups.items()}
 
     blocks_per_s = wl.batch * 1e3 / ms_step
     out = {
@@ -212,11 +306,13 @@ def main():
                    "ctx_len": int(ctx.max()), "n_new_per_step": n_new, "layers": s.n_layers, "hidden": s.hidden,
                    "vocab": s.vocab, "top_k": wl.top_k},
         "us_per_step": round(ms_step * 1e3, 1),
+        "us_per_step_graph_replay": round(ms_step_graph * 1e3, 1) if ms_step_graph is not None else None,
         "draft_block_us": round(ms_draft * 1e3, 1),
-        "step_algorithmic_bytes": int(ab["total"]),
-        "step_hbm_gbs": round(ab["total"] / (ms_step * 1e-3) / 1e9, 1),
-        "step_frac_of_peak": round(ab["total"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "step_algorithmic_bytes": int(total_bytes),
+        "step_hbm_gbs": round(total_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_frac_of_peak": round(total_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "roofline": roofline,
+        "kernel_hbm_gbs": per_kernel_roofline,
         "kernels": {n: {k: round(v, 2) for k, v in d.items()} for n, d in kernels.items()},
         "setup_s": round(setup_s, 1),
     }

@@ -368,7 +368,7 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
         sq.start[0] = 0; sq.start[1] = qd; sq.start[2] = qd + kvd; sq.start[3] = qd + 2 * kvd;
         sq.n = 3;
         {
-            Timed t(h, gemm_kernel_name(p.qkv), st, qd + 2 * kvd, H);
+            Timed t(h, gemm_kernel_name(p.qkv, bf), st, qd + 2 * kvd, H);
             HIP_TRY(launch_gemm(p.qkv, u, H, bf ? (size_t)M * H : 0, M, sq, qd + 2 * kvd, H, part, st));
         }
         {
@@ -387,7 +387,7 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
             attn_out = o;
         }
         {
-            Timed t(h, gemm_kernel_name(p.oproj), st, H, qd);
+            Timed t(h, gemm_kernel_name(p.oproj, bf), st, H, qd);
             HIP_TRY(launch_gemm(p.oproj, attn_out, qd, bf ? (size_t)M * qd : 0, M, segs1(lw.wo, H), H, qd, part, st));
         }
         {
@@ -399,7 +399,7 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
         sg.start[0] = 0; sg.start[1] = c.ffn; sg.start[2] = 2 * c.ffn;
         sg.n = 2;
         {
-            Timed t(h, gemm_kernel_name(p.gateup), st, 2 * c.ffn, H);
+            Timed t(h, gemm_kernel_name(p.gateup, bf), st, 2 * c.ffn, H);
             HIP_TRY(launch_gemm(p.gateup, u, H, bf ? (size_t)M * H : 0, M, sg, 2 * c.ffn, H, part, st));
         }
         {
@@ -407,7 +407,7 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
             HIP_TRY(launch_swiglu(bf, part, p.gateup.splits, M, c.ffn, a, st));
         }
         {
-            Timed t(h, gemm_kernel_name(p.down), st, H, c.ffn);
+            Timed t(h, gemm_kernel_name(p.down, bf), st, H, c.ffn);
             HIP_TRY(launch_gemm(p.down, a, c.ffn, bf ? (size_t)M * c.ffn : 0, M, segs1(lw.w_down, H), H, c.ffn, part, st));
         }
         {
@@ -464,7 +464,7 @@ extern "C" int dflash_inject_ctx(dflash_handle* h, int batch, int n_rows, const 
         const char* x = (const char*)feats + (size_t)row0 * feat_row_stride * E;
         const GemmPlan fc = plan_gemm(bf, R, H, c.feat_dim);
         {
-            Timed t(h, gemm_kernel_name(fc), st, H, c.feat_dim);
+            Timed t(h, gemm_kernel_name(fc, false), st, H, c.feat_dim);
             HIP_TRY(launch_gemm(fc, x, (int)feat_row_stride, 0, R, segs1(h->w.fc_w, H), H, c.feat_dim, part, st));
         }
         {
@@ -484,7 +484,7 @@ extern "C" int dflash_inject_ctx(dflash_handle* h, int batch, int n_rows, const 
             s.n = 2 * nl;
             const GemmPlan kp = plan_gemm(bf, R, 2 * nl * kvd, H);
             {
-                Timed t(h, gemm_kernel_name(kp), st, 2 * nl * kvd, H);
+                Timed t(h, gemm_kernel_name(kp, bf), st, 2 * nl * kvd, H);
                 HIP_TRY(launch_gemm(kp, f, H, bf ? (size_t)R * H : 0, R, s, 2 * nl * kvd, H, part, st));
             }
             {

@@ -237,11 +237,11 @@ hipError_t launch_gemm(const GemmPlan& p, const void* x, int ldx, size_t xplane,
     return hipGetLastError();
 }
 
-const char* gemm_kernel_name(const GemmPlan& p) {
+const char* gemm_kernel_name(const GemmPlan& p, bool pair) {
     switch (p.kind) {
-        case GEMM_SKINNY1: return "gemm_skinny_bf16_m16";
-        case GEMM_SKINNY2: return "gemm_skinny_bf16_m32";
-        case GEMM_TILED: return "gemm_tiled_bf16";
+        case GEMM_SKINNY1: return pair ? "gemm_skinny_bf16_m16_pair" : "gemm_skinny_bf16_m16";
+        case GEMM_SKINNY2: return pair ? "gemm_skinny_bf16_m32_pair" : "gemm_skinny_bf16_m32";
+        case GEMM_TILED: return pair ? "gemm_tiled_bf16_pair" : "gemm_tiled_bf16";
         default: return "gemm_f32";
     }
 }

@@ -20,7 +20,7 @@ GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K);
 // xplane != 0: x is an activation pair of bfloat16 planes (lo plane xplane elements after hi).
 hipError_t launch_gemm(const GemmPlan& p, const void* x, int ldx, size_t xplane, int M, const Segs& w, int N, int K,
                        float* part, hipStream_t st);
-const char* gemm_kernel_name(const GemmPlan& p);
+const char* gemm_kernel_name(const GemmPlan& p, bool pair);
 
 // ---- row-wise kernels ------------------------------------------------------------------------------------
 // h = embed[tok]; u = RMSNorm(h) * g.  Also clears the device error word (block 0).

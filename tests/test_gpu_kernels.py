@@ -118,3 +118,38 @@ def test_device_error_word_flags_bad_pages_positions_and_tokens():
     g.draft()
     torch.cuda.synchronize()
     assert g.error_word() == 0
+
+
+def test_graph_replay_matches_eager():
+    """The drafter pass captured as a HIP graph and replayed several times, with eager calls and
+    synchronisations in between, reproduces the eager outputs bit for bit every time."""
+    torch, D, S = _mods()
+    wl = W.by_name("small-bf16-paged-b2")
+    g = S.GpuWorkload(wl)
+    g.prefill()
+    lg = torch.zeros((wl.batch, wl.shape.block_len, wl.shape.vocab), dtype=torch.float32, device="cuda")
+    g.draft(logits=lg)
+    torch.cuda.synchronize()
+    ref_tok, ref_lg, ref_lp = g.tokens.clone(), lg.clone(), g.topk_lp.clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            g.draft(logits=lg, stream=cap)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    other = g.block_tokens.clone()
+    for it in range(3):
+        g.tokens.zero_()
+        lg.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g.tokens, ref_tok), it
+        assert torch.equal(lg.view(torch.int32), ref_lg.view(torch.int32)), it
+        assert torch.equal(g.topk_lp.view(torch.int32), ref_lp.view(torch.int32)), it
+        # eager work between replays: a pass on different anchors, then restore
+        g.block_tokens[:, 0] = (other[:, 0] + 7 + it) % wl.shape.vocab
+        g.draft()
+        torch.cuda.synchronize()
+        g.block_tokens.copy_(other)
