@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "dflash.h"
+#include "gemm_core.h"
 #include "kernels.h"
 
 using namespace df;
@@ -45,11 +46,41 @@ struct ProfEntry {
     hipEvent_t start, stop;
 };
 
+// Element offsets of every projection matrix in the packed weight store of a bfloat16 drafter (layout of one
+// matrix: gemm_core.h).  Matrices that one GEMM stacks along N are adjacent: [wq; wk; wv], [w_gate; w_up],
+// and [uk; uv] of consecutive layers.
+struct PackLayout {
+    std::vector<size_t> qkv, o, gu, down;  // per layer
+    size_t kv = 0, kv_stride = 0;          // layer l's [uk; uv] at kv + l * kv_stride
+    size_t fc = 0, lm = 0, total = 0;
+};
+
+static PackLayout pack_layout(const dflash_config& c) {
+    PackLayout pl;
+    const int H = c.hidden, F = c.ffn, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    size_t off = 0;
+    auto take = [&](size_t n) { size_t o = off; off += n; return o; };
+    for (int l = 0; l < c.n_layers; ++l) {
+        pl.qkv.push_back(take(packed_elems(qd, H) + 2 * packed_elems(kvd, H)));
+        pl.o.push_back(take(packed_elems(H, qd)));
+        pl.gu.push_back(take(2 * packed_elems(F, H)));
+        pl.down.push_back(take(packed_elems(H, F)));
+    }
+    pl.kv_stride = 2 * packed_elems(kvd, H);
+    pl.kv = take((size_t)c.n_layers * pl.kv_stride);
+    pl.fc = take(packed_elems(H, c.feat_dim));
+    pl.lm = take(packed_elems(c.vocab, H));
+    pl.total = off;
+    return pl;
+}
+
 struct dflash_handle {
     dflash_config cfg;
     dflash_weights w;
     std::vector<dflash_layer_weights> layers;
     RopeFreq rf;
+    PackLayout pl;
+    const bf16_t* packed = nullptr;  // packed store (bfloat16 drafters), set by dflash_pack_weights
     bool profiling = false;
     std::vector<hipEvent_t> event_pool;
     std::vector<ProfEntry> pending;
@@ -111,7 +142,49 @@ extern "C" int dflash_create(const dflash_config* cfg, const dflash_weights* w, 
     h->rf.on = cfg->rope_theta > 0.f;
     for (int i = 0; i < cfg->head_dim / 2; ++i)
         h->rf.inv[i] = h->rf.on ? (float)std::pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim) : 0.f;
+    if (is_bf16(*cfg)) h->pl = pack_layout(*cfg);
     *out = h;
+    return DFLASH_OK;
+}
+
+extern "C" size_t dflash_packed_weight_bytes(const dflash_handle* h) {
+    if (!h || !is_bf16(h->cfg)) return 0;
+    return h->pl.total * 2;
+}
+
+extern "C" int dflash_pack_weights(dflash_handle* h, void* dst, size_t dst_bytes, void* stream) {
+    if (!h) return fail(DFLASH_E_ARG, "handle is NULL");
+    const dflash_config& c = h->cfg;
+    if (!is_bf16(c)) return DFLASH_OK;  // float32 drafters stream the row-major matrices
+    if (!dst) return fail(DFLASH_E_ARG, "dst is NULL");
+    if (((uintptr_t)dst) & 255) return fail(DFLASH_E_ARG, "dst must be 256-byte aligned");
+    if (dst_bytes < h->pl.total * 2) return fail(DFLASH_E_CAPACITY, "dst %zu < %zu bytes", dst_bytes, h->pl.total * 2);
+    {
+        uintptr_t a = (uintptr_t)h->w.fc_w | (uintptr_t)h->w.lm_head;
+        for (const dflash_layer_weights& w : h->layers)
+            a |= (uintptr_t)w.wq | (uintptr_t)w.wk | (uintptr_t)w.wv | (uintptr_t)w.wo | (uintptr_t)w.w_gate |
+                 (uintptr_t)w.w_up | (uintptr_t)w.w_down | (uintptr_t)w.uk | (uintptr_t)w.uv;
+        if (a & 15) return fail(DFLASH_E_ARG, "projection matrices must be 16-byte aligned");
+    }
+    hipStream_t st = (hipStream_t)stream;
+    bf16_t* P = (bf16_t*)dst;
+    const int H = c.hidden, F = c.ffn, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    const PackLayout& pl = h->pl;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const dflash_layer_weights& w = h->layers[l];
+        HIP_TRY(launch_pack(w.wq, qd, H, P + pl.qkv[l], st));
+        HIP_TRY(launch_pack(w.wk, kvd, H, P + pl.qkv[l] + packed_elems(qd, H), st));
+        HIP_TRY(launch_pack(w.wv, kvd, H, P + pl.qkv[l] + packed_elems(qd, H) + packed_elems(kvd, H), st));
+        HIP_TRY(launch_pack(w.wo, H, qd, P + pl.o[l], st));
+        HIP_TRY(launch_pack(w.w_gate, F, H, P + pl.gu[l], st));
+        HIP_TRY(launch_pack(w.w_up, F, H, P + pl.gu[l] + packed_elems(F, H), st));
+        HIP_TRY(launch_pack(w.w_down, H, F, P + pl.down[l], st));
+        HIP_TRY(launch_pack(w.uk, kvd, H, P + pl.kv + l * pl.kv_stride, st));
+        HIP_TRY(launch_pack(w.uv, kvd, H, P + pl.kv + l * pl.kv_stride + packed_elems(kvd, H), st));
+    }
+    HIP_TRY(launch_pack(h->w.fc_w, H, c.feat_dim, P + pl.fc, st));
+    HIP_TRY(launch_pack(h->w.lm_head, c.vocab, H, P + pl.lm, st));
+    h->packed = P;
     return DFLASH_OK;
 }
 
@@ -307,6 +380,14 @@ static Segs segs1(const void* p, int n) {
     return s;
 }
 
+// One projection: bfloat16 drafters stream the packed matrix at element offset `packed_off` of the store,
+// float32 drafters the row-major segments `rows`.
+static hipError_t project(const dflash_handle* h, const GemmPlan& p, const void* x, int ldx, size_t xplane, int M,
+                          size_t packed_off, const Segs& rows, int N, int K, float* part, hipStream_t st) {
+    if (is_bf16(h->cfg)) return launch_gemm_bf16(p, x, ldx, xplane, M, h->packed + packed_off, N, K, part, st);
+    return launch_gemm_f32((const float*)x, ldx, M, rows, N, K, part, st);
+}
+
 extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* block_tokens, const int32_t* ctx_len,
                                   const int32_t* page_table, int max_pages, const dflash_kv* kv, int max_ctx,
                                   int top_k, int32_t* tokens, int32_t* topk_ids, float* topk_logprobs,
@@ -331,6 +412,7 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
     const DraftPlan p = plan_draft(c, batch, max_ctx);
     if (ws_bytes < p.total) return fail(DFLASH_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, p.total);
     if (((uintptr_t)ws) & 255) return fail(DFLASH_E_ARG, "workspace must be 256-byte aligned");
+    if (is_bf16(c) && !h->packed) return fail(DFLASH_E_ARG, "bfloat16 weights are not packed (dflash_pack_weights)");
 
     hipStream_t st = (hipStream_t)stream;
     char* W = (char*)ws;
@@ -369,7 +451,8 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
         sq.n = 3;
         {
             Timed t(h, gemm_kernel_name(p.qkv, bf), st, qd + 2 * kvd, H);
-            HIP_TRY(launch_gemm(p.qkv, u, H, bf ? (size_t)M * H : 0, M, sq, qd + 2 * kvd, H, part, st));
+            HIP_TRY(project(h, p.qkv, u, H, bf ? (size_t)M * H : 0, M, bf ? h->pl.qkv[l] : 0, sq, qd + 2 * kvd, H,
+                            part, st));
         }
         {
             Timed t(h, "qkv_epilogue", st);
@@ -388,7 +471,8 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
         }
         {
             Timed t(h, gemm_kernel_name(p.oproj, bf), st, H, qd);
-            HIP_TRY(launch_gemm(p.oproj, attn_out, qd, bf ? (size_t)M * qd : 0, M, segs1(lw.wo, H), H, qd, part, st));
+            HIP_TRY(project(h, p.oproj, attn_out, qd, bf ? (size_t)M * qd : 0, M, bf ? h->pl.o[l] : 0, segs1(lw.wo, H),
+                            H, qd, part, st));
         }
         {
             Timed t(h, "resid_norm", st);
@@ -400,7 +484,8 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
         sg.n = 2;
         {
             Timed t(h, gemm_kernel_name(p.gateup, bf), st, 2 * c.ffn, H);
-            HIP_TRY(launch_gemm(p.gateup, u, H, bf ? (size_t)M * H : 0, M, sg, 2 * c.ffn, H, part, st));
+            HIP_TRY(project(h, p.gateup, u, H, bf ? (size_t)M * H : 0, M, bf ? h->pl.gu[l] : 0, sg, 2 * c.ffn, H,
+                            part, st));
         }
         {
             Timed t(h, "swiglu", st);
@@ -408,7 +493,8 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
         }
         {
             Timed t(h, gemm_kernel_name(p.down, bf), st, H, c.ffn);
-            HIP_TRY(launch_gemm(p.down, a, c.ffn, bf ? (size_t)M * c.ffn : 0, M, segs1(lw.w_down, H), H, c.ffn, part, st));
+            HIP_TRY(project(h, p.down, a, c.ffn, bf ? (size_t)M * c.ffn : 0, M, bf ? h->pl.down[l] : 0,
+                            segs1(lw.w_down, H), H, c.ffn, part, st));
         }
         {
             const void* next_gain = l + 1 < c.n_layers ? h->layers[l + 1].attn_norm : h->w.final_norm;
@@ -419,7 +505,8 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
     }
     {
         Timed t(h, bf ? "lm_head_bf16" : "lm_head_f32", st);
-        HIP_TRY(launch_lm_head(bf, u, M, h->w.lm_head, c.vocab, H, hpart, dbg ? dbg->logits : nullptr, st));
+        const void* wlm = bf ? (const void*)(h->packed + h->pl.lm) : h->w.lm_head;
+        HIP_TRY(launch_lm_head(bf, u, M, wlm, c.vocab, H, hpart, dbg ? dbg->logits : nullptr, st));
     }
     {
         Timed t(h, "head_merge", st);
@@ -446,6 +533,7 @@ extern "C" int dflash_inject_ctx(dflash_handle* h, int batch, int n_rows, const 
     const InjectPlan p = plan_inject(c, n_rows);
     if (ws_bytes < p.total) return fail(DFLASH_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, p.total);
     if (((uintptr_t)ws) & 255) return fail(DFLASH_E_ARG, "workspace must be 256-byte aligned");
+    if (is_bf16(c) && !h->packed) return fail(DFLASH_E_ARG, "bfloat16 weights are not packed (dflash_pack_weights)");
 
     hipStream_t st = (hipStream_t)stream;
     const int bf = is_bf16(c);
@@ -465,7 +553,8 @@ extern "C" int dflash_inject_ctx(dflash_handle* h, int batch, int n_rows, const 
         const GemmPlan fc = plan_gemm(bf, R, H, c.feat_dim);
         {
             Timed t(h, gemm_kernel_name(fc, false), st, H, c.feat_dim);
-            HIP_TRY(launch_gemm(fc, x, (int)feat_row_stride, 0, R, segs1(h->w.fc_w, H), H, c.feat_dim, part, st));
+            HIP_TRY(project(h, fc, x, (int)feat_row_stride, 0, R, h->pl.fc, segs1(h->w.fc_w, H), H, c.feat_dim, part,
+                            st));
         }
         {
             Timed t(h, "fuse_cast", st);
@@ -485,7 +574,8 @@ extern "C" int dflash_inject_ctx(dflash_handle* h, int batch, int n_rows, const 
             const GemmPlan kp = plan_gemm(bf, R, 2 * nl * kvd, H);
             {
                 Timed t(h, gemm_kernel_name(kp, bf), st, 2 * nl * kvd, H);
-                HIP_TRY(launch_gemm(kp, f, H, bf ? (size_t)R * H : 0, R, s, 2 * nl * kvd, H, part, st));
+                HIP_TRY(project(h, kp, f, H, bf ? (size_t)R * H : 0, R, h->pl.kv + l0 * h->pl.kv_stride, s,
+                                2 * nl * kvd, H, part, st));
             }
             {
                 Timed t(h, "kv_scatter", st);
@@ -510,10 +600,16 @@ extern "C" int dflash_accept_len(int batch, int n_draft, const int32_t* draft, i
     return DFLASH_OK;
 }
 
-extern "C" size_t dflash_linear_workspace_bytes(int dtype, int M, int N, int K) {
-    if ((dtype != DFLASH_F32 && dtype != DFLASH_BF16) || M < 1 || N < 1 || K < 1) return 0;
+// Workspace of dflash_linear: the float32 split partials, then (bfloat16) the packed image of w.
+static size_t linear_part_bytes(int dtype, int M, int N, int K) {
     const GemmPlan p = plan_gemm(dtype == DFLASH_BF16, M, N, K);
     return align256((size_t)p.splits * M * N * 4);
+}
+
+extern "C" size_t dflash_linear_workspace_bytes(int dtype, int M, int N, int K) {
+    if ((dtype != DFLASH_F32 && dtype != DFLASH_BF16) || M < 1 || N < 1 || K < 1) return 0;
+    const size_t part = linear_part_bytes(dtype, M, N, K);
+    return dtype == DFLASH_BF16 ? part + align256(packed_elems(N, K) * 2) : part;
 }
 
 extern "C" int dflash_linear(int dtype, int M, int N, int K, const void* x, int64_t ldx, const void* w, float* y,
@@ -525,9 +621,17 @@ extern "C" int dflash_linear(int dtype, int M, int N, int K, const void* x, int6
     if (dtype == DFLASH_BF16 && (K % 256 || ldx % 8)) return fail(DFLASH_E_UNSUPPORTED, "bf16 needs K % 256 == 0");
     if (dtype == DFLASH_F32 && (K % 4 || ldx % 4)) return fail(DFLASH_E_UNSUPPORTED, "f32 needs K % 4 == 0");
     if (ws_bytes < dflash_linear_workspace_bytes(dtype, M, N, K)) return fail(DFLASH_E_CAPACITY, "workspace too small");
+    if ((((uintptr_t)x) | ((uintptr_t)w) | ((uintptr_t)ws)) & 15)
+        return fail(DFLASH_E_ARG, "x, w and the workspace must be 16-byte aligned");
     const GemmPlan p = plan_gemm(dtype == DFLASH_BF16, M, N, K);
     hipStream_t st = (hipStream_t)stream;
-    HIP_TRY(launch_gemm(p, x, (int)ldx, 0, M, segs1(w, N), N, K, (float*)ws, st));
+    if (dtype == DFLASH_BF16) {
+        void* wpk = (char*)ws + linear_part_bytes(dtype, M, N, K);
+        HIP_TRY(launch_pack(w, N, K, wpk, st));
+        HIP_TRY(launch_gemm_bf16(p, x, (int)ldx, 0, M, wpk, N, K, (float*)ws, st));
+    } else {
+        HIP_TRY(launch_gemm_f32((const float*)x, (int)ldx, M, segs1(w, N), N, K, (float*)ws, st));
+    }
     HIP_TRY(launch_reduce_cast(0, (float*)ws, p.splits, M, N, nullptr, y, st));
     return DFLASH_OK;
 }

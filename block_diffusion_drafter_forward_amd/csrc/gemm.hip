@@ -15,18 +15,49 @@
 namespace df {
 
 // ------------------------------------------------------------------------------------------------------
-// skinny MFMA GEMM (bfloat16), M <= 16 * MT
+// weight packing (once per weight matrix, into the fragment-major layout of gemm_core.h)
+// ------------------------------------------------------------------------------------------------------
+// One thread per 16-byte lane piece of the packed image: piece c is lane c % 64 of fragment c / 64.
+__global__ __launch_bounds__(256) void pack_frag(const bf16_t* __restrict__ src, int N, int K, bf16_t* __restrict__ dst,
+                                                 size_t pieces) {
+    const int KS = K / 32;
+    for (size_t c = (size_t)blockIdx.x * 256 + threadIdx.x; c < pieces; c += (size_t)gridDim.x * 256) {
+        const size_t f = c >> 6;
+        const int l = (int)(c & 63);
+        const size_t t = f / KS;
+        const int s = (int)(f % KS);
+        const size_t n = t * 16 + (l & 15);
+        const int k = s * 32 + (l >> 4) * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (n < (size_t)N) v = ld16(src + n * K + k);
+        *(u32x4*)(dst + c * 8) = v;
+    }
+}
+
+hipError_t launch_pack(const void* src, int N, int K, void* dst, hipStream_t st) {
+    const size_t pieces = packed_elems(N, K) / 8;
+    const size_t blocks = (pieces + 255) / 256;
+    hipLaunchKernelGGL(pack_frag, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, st,
+                       (const bf16_t*)src, N, K, (bf16_t*)dst, pieces);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------------
+// skinny MFMA GEMM (bfloat16), M <= 16 * MT, packed weights
 // ------------------------------------------------------------------------------------------------------
 // Workgroup = 4 waves on the same 64 output columns (4 n-tiles of 16); wave w takes the k-range
-// [k0 + w * kpw, k0 + (w + 1) * kpw) of the workgroup's split.  Per 256-wide k-chunk a lane loads, for each
-// n-tile, eight 16-byte pieces of one weight row (A operand: row = lane % 16, k = 32 j + 8 (lane / 16)) and
-// the matching eight pieces of its activation row (B operand), then issues 8 MFMAs per (n-tile, m-tile).
-// With SPLIT the activation is a pair of bfloat16 planes (x = hi + lo, lo plane at x + xplane) and every
-// weight fragment meets both: two MFMAs, one weight load.
+// [k0 + w * kpw, k0 + (w + 1) * kpw) of the workgroup's split.  Per 256-wide k-chunk a wave loads, for each
+// n-tile, eight packed weight fragments (one coalesced 1 KB load each: the A operand, row = lane % 16,
+// k = 32 j + 8 (lane / 16)) and the matching eight 16-byte pieces of its activation row (B operand), then
+// issues 8 MFMAs per (n-tile, m-tile).  With SPLIT the activation is a pair of bfloat16 planes (x = hi + lo,
+// lo plane at x + xplane) and every weight fragment meets both: two MFMAs, one weight load; at one m-tile
+// the hi and lo products go to separate accumulators so that the two MFMAs do not wait on each other.
 template <int MT, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict__ x, int ldx, size_t xplane, int M,
-                                                        Segs w, int N, int K, int kpw, float* __restrict__ part) {
+                                                        const bf16_t* __restrict__ wp, int N, int K, int kpw,
+                                                        float* __restrict__ part) {
     constexpr int NT = 4;
+    constexpr bool SEP = SPLIT && MT == 1;
     __shared__ f32x4 red[4][NT * MT][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -34,22 +65,23 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict
     const int s = blockIdx.y;
     const int kb = s * 4 * kpw + wave * kpw;
     const int ke = min(K, kb + kpw);
+    const int KS = K / 32, tiles = (N + 15) / 16;
 
-    const bf16_t* wrow[NT];
+    const bf16_t* wt[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        int n = min(n0 + nt * 16 + r, N - 1);
-        wrow[nt] = (const bf16_t*)seg_row(w, n, K, 2) + g * 8;
-    }
+    for (int nt = 0; nt < NT; ++nt)
+        wt[nt] = wp + (size_t)min(blockIdx.x * NT + nt, tiles - 1) * KS * DF_FRAG + lane * 8;
     const bf16_t* xrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) xrow[mt] = x + (size_t)min(mt * 16 + r, M - 1) * ldx + g * 8;
 
-    f32x4 acc[NT][MT];
+    f32x4 acc[NT][MT], acl[SEP ? NT : 1];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (SEP) acl[SEP ? nt : 0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     for (int kc = kb; kc < ke; kc += 256) {
         u32x4 wf[NT][8];
@@ -58,7 +90,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) wf[nt][j] = ld16_nt(wrow[nt] + kc + j * 32);
+            for (int nt = 0; nt < NT; ++nt) wf[nt][j] = ld16_nt(wt[nt] + (size_t)(kc / 32 + j) * DF_FRAG);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 xf[mt][j] = ld16(xrow[mt] + kc + j * 32);
@@ -74,14 +106,22 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     acc[nt][mt] = mfma16(wf[nt][j], xf[mt][j], acc[nt][mt]);
-                    if (SPLIT) acc[nt][mt] = mfma16(wf[nt][j], xl[SPLIT ? mt : 0][j], acc[nt][mt]);
+                    if (SEP) acl[SEP ? nt : 0] = mfma16(wf[nt][j], xl[0][j], acl[SEP ? nt : 0]);
+                    else if (SPLIT) acc[nt][mt] = mfma16(wf[nt][j], xl[SPLIT ? mt : 0][j], acc[nt][mt]);
                 }
     }
 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) red[wave][nt * MT + mt][lane] = acc[nt][mt];
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4 v = acc[nt][mt];
+            if (SEP) {
+                const f32x4 u = acl[SEP ? nt : 0];
+                v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
+            }
+            red[wave][nt * MT + mt][lane] = v;
+        }
     __syncthreads();
 
     for (int e = threadIdx.x; e < NT * MT * 64; e += 256) {
@@ -110,8 +150,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict
 // ------------------------------------------------------------------------------------------------------
 template <bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict__ x, int ldx, size_t xplane, int M,
-                                                       Segs w, int N, int K, int kps, float* __restrict__ part) {
-    __shared__ __attribute__((aligned(16))) bf16_t sw[TL_BN * TL_LD];
+                                                       const bf16_t* __restrict__ wp, int N, int K, int kps,
+                                                       float* __restrict__ part) {
+    __shared__ __attribute__((aligned(16))) bf16_t sw[TL_SW];
     __shared__ __attribute__((aligned(16))) bf16_t sx[(SPLIT ? 2 : 1) * TL_BM * TL_LD];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -119,7 +160,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict_
     const int n0 = blockIdx.x * TL_BN, m0 = blockIdx.y * TL_BM, s = blockIdx.z;
     const int kb = s * kps, ke = min(K, kb + kps);
     f32x4 acc[4][4];
-    tiled_mainloop<SPLIT>(x, ldx, xplane, M, w, N, K, n0, m0, kb, ke, sw, sx, acc);
+    tiled_mainloop<SPLIT>(x, ldx, xplane, M, wp, N, K, n0, m0, kb, ke, sw, sx, acc);
     // D lane l: n = 4 (l / 16) + i, m = l % 16 within each 16 x 16 tile
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -183,14 +224,14 @@ GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K) {
     }
     if (M <= 32) {
         p.kind = M <= 16 ? GEMM_SKINNY1 : GEMM_SKINNY2;
-        // Each wave streams kpw of K for 64 columns (32 KB of weights per 256-wide chunk).  Measured on
-        // MI355X at the drafter's shapes: one chunk per wave is best unless a longer range still leaves
-        // enough workgroups to cover the chip (>= ~700 for two chunks, >= ~2000 for four).
+        // Each wave streams kpw of K for 64 columns (32 KB of packed weights per 256-wide chunk).  Measured
+        // on MI355X at the drafter's shapes (4096 x 4096 up to 24576 x 4096 and 4096 x 12288): one chunk per
+        // wave is best; only vocabulary-sized N (>= ~2000 workgroups even with four chunks) gains from
+        // longer ranges.
         const int groups = (N + 63) / 64;
         auto wgs = [&](int kpw) { return groups * ((K + 4 * kpw - 1) / (4 * kpw)); };
         p.kpw = 256;
         if (K % 1024 == 0 && wgs(1024) >= 2000) p.kpw = 1024;
-        else if (K % 512 == 0 && wgs(512) >= 700) p.kpw = 512;
         p.splits = (K + 4 * p.kpw - 1) / (4 * p.kpw);
         return p;
     }
@@ -205,35 +246,40 @@ GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K) {
     return p;
 }
 
-hipError_t launch_gemm(const GemmPlan& p, const void* x, int ldx, size_t xplane, int M, const Segs& w, int N, int K,
-                       float* part, hipStream_t st) {
+hipError_t launch_gemm_bf16(const GemmPlan& p, const void* x, int ldx, size_t xplane, int M, const void* wpacked,
+                            int N, int K, float* part, hipStream_t st) {
     const bool split = xplane != 0;
     const dim3 gs((N + 63) / 64, p.splits);
     const dim3 gt((N + TL_BN - 1) / TL_BN, (M + TL_BM - 1) / TL_BM, p.splits);
     const bf16_t* xb = (const bf16_t*)x;
+    const bf16_t* wp = (const bf16_t*)wpacked;
     switch (p.kind) {
         case GEMM_SKINNY1:
             if (split)
-                hipLaunchKernelGGL((gemm_skinny_bf16<1, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kpw, part);
+                hipLaunchKernelGGL((gemm_skinny_bf16<1, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
             else
-                hipLaunchKernelGGL((gemm_skinny_bf16<1, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kpw, part);
+                hipLaunchKernelGGL((gemm_skinny_bf16<1, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
             break;
         case GEMM_SKINNY2:
             if (split)
-                hipLaunchKernelGGL((gemm_skinny_bf16<2, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kpw, part);
+                hipLaunchKernelGGL((gemm_skinny_bf16<2, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
             else
-                hipLaunchKernelGGL((gemm_skinny_bf16<2, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kpw, part);
+                hipLaunchKernelGGL((gemm_skinny_bf16<2, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
             break;
         case GEMM_TILED:
             if (split)
-                hipLaunchKernelGGL((gemm_tiled_bf16<true>), gt, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kps, part);
+                hipLaunchKernelGGL((gemm_tiled_bf16<true>), gt, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kps, part);
             else
-                hipLaunchKernelGGL((gemm_tiled_bf16<false>), gt, dim3(256), 0, st, xb, ldx, xplane, M, w, N, K, p.kps, part);
+                hipLaunchKernelGGL((gemm_tiled_bf16<false>), gt, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kps, part);
             break;
-        case GEMM_F32:
-            hipLaunchKernelGGL(gemm_f32, dim3((N + 3) / 4), dim3(256), 0, st, (const float*)x, ldx, M, w, N, K, part);
-            break;
+        default:
+            return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const float* x, int ldx, int M, const Segs& w, int N, int K, float* part, hipStream_t st) {
+    hipLaunchKernelGGL(gemm_f32, dim3((N + 3) / 4), dim3(256), 0, st, x, ldx, M, w, N, K, part);
     return hipGetLastError();
 }
 

@@ -1,40 +1,58 @@
-// Main loop of the LDS-tiled MFMA GEMM, shared by the large-M projection kernel and the large-M LM head.
+// Packed weight layout and the main loop of the LDS-tiled MFMA GEMM, shared by the large-M projection
+// kernel and the large-M LM head.
 #pragma once
 
 #include "common.h"
+
+// ------------------------------------------------------------------------------------------------------
+// packed ("fragment-major") weights
+// ------------------------------------------------------------------------------------------------------
+// A bfloat16 matrix W[N][K] (K a multiple of 32) is stored as ceil(N / 16) x (K / 32) fragments of 16 rows x
+// 32 k-values, fragment (t, s) at element offset (t * (K / 32) + s) * 512.  Inside a fragment, lane l of a
+// wave owns the 16 bytes at offset 8 l: row 16 t + (l % 16), k = 32 s + 8 (l / 16) .. + 7 -- exactly the
+// A operand of one 16x16x32 MFMA, so a wave fetches a whole fragment with one fully coalesced 1 KB load.
+// Rows past N (the last fragment row of a ragged N) are zero.  Stacking matrices along N (q/k/v, gate/up,
+// the per-layer K/V projections) is concatenation of their packed images when every N is a multiple of 16.
+#define DF_FRAG 512  // elements per fragment
+__host__ __device__ inline size_t packed_elems(int N, int K) { return (size_t)((N + 15) / 16) * (size_t)K * 16; }
 
 // ------------------------------------------------------------------------------------------------------
 // LDS-tiled MFMA GEMM (bfloat16) for large M
 // ------------------------------------------------------------------------------------------------------
 // Tile 128 (n) x 128 (m) x 64 (k); 4 waves in a 2 x 2 grid, each owning 64 x 64 = 4 x 4 MFMA tiles.  The
 // next k-tile is fetched into registers while the current one is consumed from LDS (one barrier pair per
-// k-tile).  Rows are padded to 72 elements in LDS to spread the 16-byte reads over the banks.
+// k-tile).  The weight tile is 16 packed fragments, copied to LDS as they are (conflict-free 1 KB reads per
+// MFMA operand); activation rows are padded to 72 elements in LDS to spread the 16-byte reads over the banks.
 #define TL_BN 128
 #define TL_BM 128
 #define TL_BK 64
 #define TL_LD (TL_BK + 8)
+#define TL_SW (16 * DF_FRAG)  // elements of the LDS weight tile
 
 // Main loop of the tiled kernel: acc[a][b] (n-tile a, m-tile b of this wave's 64 x 64 block) for the k-range
-// [kb, ke).  sw / sx are LDS staging buffers of TL_BN * TL_LD and TL_BM * TL_LD elements.
-// With SPLIT the activation is a pair of bfloat16 planes (lo plane at x + xplane): sx holds both planes
-// (2 * TL_BM * TL_LD elements) and every weight fragment meets hi and lo.
+// [kb, ke).  wp is the packed weight matrix (N x K); sw / sx are LDS staging buffers of TL_SW and
+// TL_BM * TL_LD elements.  With SPLIT the activation is a pair of bfloat16 planes (lo plane at x + xplane):
+// sx holds both planes (2 * TL_BM * TL_LD elements) and every weight fragment meets hi and lo.
 template <bool SPLIT>
 static __device__ __forceinline__ void tiled_mainloop(const bf16_t* __restrict__ x, int ldx, size_t xplane, int M,
-                                                      const Segs& w, int N, int K, int n0, int m0, int kb, int ke,
-                                                      bf16_t* sw, bf16_t* sx, f32x4 (&acc)[4][4]) {
+                                                      const bf16_t* __restrict__ wp, int N, int K, int n0, int m0,
+                                                      int kb, int ke, bf16_t* sw, bf16_t* sx, f32x4 (&acc)[4][4]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int wn = wave >> 1, wm = wave & 1;
-    // global -> register staging: each thread moves 4 pieces of 16 bytes of W and of x per k-tile
+    const int KS = K / 32, tiles = (N + 15) / 16;
+    // global -> register staging: each thread moves 4 pieces of 16 bytes of W and of x per k-tile.  Weight
+    // piece c = tid + 256 i is lane (c % 64) of fragment c / 64 = (n-tile, k-step) = ((c / 64) / 2, (c / 64) % 2).
     const bf16_t* wsrc[4];
     const bf16_t* xsrc[4];
     int lrow[4], lcol[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        int c = tid + 256 * i;
+        const int c = tid + 256 * i, f = c >> 6;
+        const int t = min(n0 / 16 + (f >> 1), tiles - 1);
+        wsrc[i] = wp + ((size_t)t * KS + (f & 1)) * DF_FRAG + (c & 63) * 8;
         lrow[i] = c >> 3;
         lcol[i] = (c & 7) * 8;
-        wsrc[i] = (const bf16_t*)seg_row(w, min(n0 + lrow[i], N - 1), K, 2) + lcol[i];
         xsrc[i] = x + (size_t)min(m0 + lrow[i], M - 1) * ldx + lcol[i];
     }
     constexpr int XP = SPLIT ? 2 : 1;
@@ -46,7 +64,7 @@ static __device__ __forceinline__ void tiled_mainloop(const bf16_t* __restrict__
     if (kb < ke) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pw[i] = ld16_nt(wsrc[i] + kb);
+            pw[i] = ld16_nt(wsrc[i] + (size_t)(kb / 32) * DF_FRAG);
 #pragma unroll
             for (int pl = 0; pl < XP; ++pl) px[pl][i] = ld16(xsrc[i] + pl * xplane + kb);
         }
@@ -55,7 +73,7 @@ static __device__ __forceinline__ void tiled_mainloop(const bf16_t* __restrict__
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            *(u32x4*)(sw + lrow[i] * TL_LD + lcol[i]) = pw[i];
+            *(u32x4*)(sw + (tid + 256 * i) * 8) = pw[i];
 #pragma unroll
             for (int pl = 0; pl < XP; ++pl) *(u32x4*)(sx + (pl * TL_BM + lrow[i]) * TL_LD + lcol[i]) = px[pl][i];
         }
@@ -63,7 +81,7 @@ static __device__ __forceinline__ void tiled_mainloop(const bf16_t* __restrict__
         if (k + TL_BK < ke) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pw[i] = ld16_nt(wsrc[i] + k + TL_BK);
+                pw[i] = ld16_nt(wsrc[i] + (size_t)((k + TL_BK) / 32) * DF_FRAG);
 #pragma unroll
                 for (int pl = 0; pl < XP; ++pl) px[pl][i] = ld16(xsrc[i] + pl * xplane + k + TL_BK);
             }
@@ -72,7 +90,7 @@ static __device__ __forceinline__ void tiled_mainloop(const bf16_t* __restrict__
         for (int ks = 0; ks < TL_BK / 32; ++ks) {
             u32x4 af[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) af[t] = ld16(sw + (wn * 64 + t * 16 + r) * TL_LD + ks * 32 + g * 8);
+            for (int t = 0; t < 4; ++t) af[t] = ld16(sw + (((wn * 4 + t) * 2 + ks) * 64 + lane) * 8);
 #pragma unroll
             for (int pl = 0; pl < XP; ++pl) {
                 u32x4 bfr[4];
@@ -87,4 +105,3 @@ static __device__ __forceinline__ void tiled_mainloop(const bf16_t* __restrict__
         }
     }
 }
-

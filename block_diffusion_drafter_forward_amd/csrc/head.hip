@@ -101,7 +101,8 @@ __device__ void head_epilogue(const float (*lg)[C + 1], float (*st)[HEAD_REC], i
 // ------------------------------------------------------------------------------------------------------
 // bfloat16 MFMA LM head: the GEMM core of the skinny kernel with the reductions as epilogue
 // ------------------------------------------------------------------------------------------------------
-// z is an activation pair of bfloat16 planes (lo plane at z + zplane): two MFMAs per weight fragment.
+// W is the packed (fragment-major) V x K matrix; z is an activation pair of bfloat16 planes (lo plane at
+// z + zplane): two MFMAs per weight fragment.
 template <int MT>
 __global__ __launch_bounds__(256) void lm_head_bf16(const bf16_t* __restrict__ z, size_t zplane, int M,
                                                     const bf16_t* __restrict__ W, int V, int K,
@@ -116,18 +117,22 @@ __global__ __launch_bounds__(256) void lm_head_bf16(const bf16_t* __restrict__ z
     const int chunks = K / 256;
     const int kb = (wave * chunks / 4) * 256, ke = ((wave + 1) * chunks / 4) * 256;
 
-    const bf16_t* wrow[NT];
+    const int KS = K / 32, tiles = (V + 15) / 16;
+    const bf16_t* wt[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) wrow[nt] = W + (size_t)min(n0 + nt * 16 + r, V - 1) * K + g * 8;
+    for (int nt = 0; nt < NT; ++nt) wt[nt] = W + (size_t)min(blockIdx.x * NT + nt, tiles - 1) * KS * DF_FRAG + lane * 8;
     const bf16_t* zrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) zrow[mt] = z + (size_t)min(mt * 16 + r, M - 1) * K + g * 8;
 
-    f32x4 acc[NT][MT];
+    constexpr bool SEP = MT == 1;  // separate hi / lo accumulators at one m-tile
+    f32x4 acc[NT][MT], acl[SEP ? NT : 1];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (SEP) acl[SEP ? nt : 0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     for (int kc = kb; kc < ke; kc += 256) {
         u32x4 wf[NT][8];
@@ -135,7 +140,7 @@ __global__ __launch_bounds__(256) void lm_head_bf16(const bf16_t* __restrict__ z
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) wf[nt][j] = ld16_nt(wrow[nt] + kc + j * 32);
+            for (int nt = 0; nt < NT; ++nt) wf[nt][j] = ld16_nt(wt[nt] + (size_t)(kc / 32 + j) * DF_FRAG);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 zf[mt][j] = ld16(zrow[mt] + kc + j * 32);
@@ -150,13 +155,21 @@ __global__ __launch_bounds__(256) void lm_head_bf16(const bf16_t* __restrict__ z
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     acc[nt][mt] = mfma16(wf[nt][j], zf[mt][j], acc[nt][mt]);
-                    acc[nt][mt] = mfma16(wf[nt][j], zl[mt][j], acc[nt][mt]);
+                    if (SEP) acl[SEP ? nt : 0] = mfma16(wf[nt][j], zl[0][j], acl[SEP ? nt : 0]);
+                    else acc[nt][mt] = mfma16(wf[nt][j], zl[mt][j], acc[nt][mt]);
                 }
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) red[wave][nt * MT + mt][lane] = acc[nt][mt];
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4 v = acc[nt][mt];
+            if (SEP) {
+                const f32x4 u = acl[SEP ? nt : 0];
+                v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
+            }
+            red[wave][nt * MT + mt][lane] = v;
+        }
     __syncthreads();
     for (int e = threadIdx.x; e < NT * MT * 64; e += 256) {
         const int t = e >> 6, l = e & 63;
@@ -211,23 +224,18 @@ __global__ __launch_bounds__(256) void lm_head_f32(const float* __restrict__ z, 
 __global__ __launch_bounds__(256) void lm_head_tiled_bf16(const bf16_t* __restrict__ z, size_t zplane, int M,
                                                           const bf16_t* __restrict__ W, int V, int K,
                                                           float* __restrict__ hpart, float* __restrict__ logits_dbg) {
-    static_assert(TH_LG_BYTES >= 3 * TL_BN * TL_LD * 2, "logits tile must cover the staging buffers");
+    static_assert(TH_LG_BYTES >= (TL_SW + 2 * TL_BM * TL_LD) * 2, "logits tile must cover the staging buffers");
     __shared__ __attribute__((aligned(16))) char smem[TH_LG_BYTES + TH_ST_BYTES];
     bf16_t* sw = (bf16_t*)smem;
-    bf16_t* sx = sw + TL_BN * TL_LD;
+    bf16_t* sx = sw + TL_SW;
     float(*lg)[129] = (float(*)[129])smem;
     float(*st)[HEAD_REC] = (float(*)[HEAD_REC])(smem + TH_LG_BYTES);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int wn = wave >> 1, wm = wave & 1;
     const int n0 = blockIdx.x * TL_BN, m0 = blockIdx.y * TL_BM;
-    Segs w;
-    w.ptr[0] = W;
-    w.start[0] = 0;
-    w.start[1] = V;
-    w.n = 1;
     f32x4 acc[4][4];
-    tiled_mainloop<true>(z, K, zplane, M, w, V, K, n0, m0, 0, K, sw, sx, acc);
+    tiled_mainloop<true>(z, K, zplane, M, W, V, K, n0, m0, 0, K, sw, sx, acc);
     __syncthreads();  // staging buffers are dead from here on: reuse them for the logits tile
 #pragma unroll
     for (int a = 0; a < 4; ++a)

@@ -17,9 +17,15 @@ struct GemmPlan {
     int kps;     // tiled: k-range per split (multiple of 64)
 };
 GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K);
-// xplane != 0: x is an activation pair of bfloat16 planes (lo plane xplane elements after hi).
-hipError_t launch_gemm(const GemmPlan& p, const void* x, int ldx, size_t xplane, int M, const Segs& w, int N, int K,
-                       float* part, hipStream_t st);
+// Packs the row-major bfloat16 matrix src[N][K] (K a multiple of 32) into the fragment-major image of
+// gemm_core.h at dst (packed_elems(N, K) elements).
+hipError_t launch_pack(const void* src, int N, int K, void* dst, hipStream_t st);
+// bfloat16: wpacked is the packed N x K matrix.  xplane != 0: x is an activation pair of bfloat16 planes
+// (lo plane xplane elements after hi).
+hipError_t launch_gemm_bf16(const GemmPlan& p, const void* x, int ldx, size_t xplane, int M, const void* wpacked,
+                            int N, int K, float* part, hipStream_t st);
+// float32: row-major weight segments.
+hipError_t launch_gemm_f32(const float* x, int ldx, int M, const Segs& w, int N, int K, float* part, hipStream_t st);
 const char* gemm_kernel_name(const GemmPlan& p, bool pair);
 
 // ---- row-wise kernels ------------------------------------------------------------------------------------
@@ -69,6 +75,7 @@ hipError_t launch_attn_merge(int bf16, const AttnPlan& p, int B, int L, int nq, 
 int head_group_width(int bf16, int M);  // vocabulary columns per record group (64 or 128)
 int head_groups(int V, int width);
 size_t head_partial_floats(int bf16, int V, int M);
+// bfloat16: wlm is the packed V x K matrix; float32: row-major.
 hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V, int K, float* hpart,
                           float* logits_dbg, hipStream_t st);
 // Also flags block tokens outside [0, V) in the device error word.

@@ -64,6 +64,8 @@ _SIGS = {
     "dflash_create": (ctypes.c_int, [ctypes.POINTER(dflash_config), ctypes.POINTER(dflash_weights),
                                      ctypes.POINTER(ctypes.c_void_p)]),
     "dflash_destroy": (None, [ctypes.c_void_p]),
+    "dflash_packed_weight_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
+    "dflash_pack_weights": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "dflash_draft_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]),
     "dflash_inject_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int]),
     "dflash_inject_ctx": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -127,6 +129,14 @@ def dflash_create(cfg: dflash_config, w: dflash_weights) -> int:
 
 def dflash_destroy(h: int) -> None:
     lib().dflash_destroy(h)
+
+
+def dflash_packed_weight_bytes(h: int) -> int:
+    return lib().dflash_packed_weight_bytes(h)
+
+
+def dflash_pack_weights(h: int, dst, dst_bytes: int, stream) -> int:
+    return lib().dflash_pack_weights(h, dst, dst_bytes, stream)
 
 
 def dflash_draft_workspace_bytes(h: int, max_batch: int, max_ctx: int) -> int:
@@ -201,10 +211,11 @@ class DraftModel:
 
     weights: dict name -> torch tensor on the GPU, names as in the header (fc_w, fc_b, embed, final_norm,
     lm_head, and per layer "l{i}.attn_norm", "l{i}.wq", ...).  bfloat16 tensors may be given as int16/uint16
-    bit patterns or torch.bfloat16; float32 as torch.float32.
+    bit patterns or torch.bfloat16; float32 as torch.float32.  pack=False skips the packed weight store
+    (argument-validation tests without a GPU; such a bfloat16 handle cannot run a pass).
     """
 
-    def __init__(self, shape, weights: Dict[str, "object"]):
+    def __init__(self, shape, weights: Dict[str, "object"], pack: bool = True):
         self.shape = shape
         self.weights = weights
         s = shape
@@ -218,6 +229,13 @@ class DraftModel:
         self.w = dflash_weights(_ptr(weights["fc_w"]), _ptr(weights.get("fc_b")), _ptr(weights["embed"]),
                                 _ptr(weights["final_norm"]), _ptr(weights["lm_head"]), self._layers)
         self.handle = dflash_create(self.cfg, self.w)
+        # bfloat16 drafters stream a fragment-ordered copy of the projection matrices (made once, on device)
+        self.packed = None
+        n = dflash_packed_weight_bytes(self.handle)
+        if n and pack:
+            import torch
+            self.packed = torch.empty(n, dtype=torch.uint8, device="cuda")
+            check(dflash_pack_weights(self.handle, self.packed.data_ptr(), n, _stream()), "dflash_pack_weights")
 
     def close(self):
         if self.handle:

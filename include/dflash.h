@@ -128,6 +128,20 @@ typedef struct dflash_handle dflash_handle;
 int dflash_create(const dflash_config *cfg, const dflash_weights *w, dflash_handle **out);
 void dflash_destroy(dflash_handle *h);
 
+/* Packed weight store.  A BF16 handle streams every projection matrix (wq, wk, wv, wo, w_gate, w_up,
+ * w_down, uk, uv of each layer, fc_w, lm_head) from a copy in MFMA fragment order: 16 rows x 32 k-values
+ * per 1 KB fragment, in the order one 64-lane wave reads them, so that each weight load of the
+ * weight-streaming GEMMs is one coalesced 1 KB access.  This is a re-layout only (the values are the
+ * row-major matrices' bits), made once per handle.
+ * dflash_packed_weight_bytes: bytes the store needs (0 for F32 handles, which read the row-major matrices).
+ * dflash_pack_weights: enqueues the repacking on `stream` into dst (device memory the caller owns, 256-byte
+ * aligned, at least dflash_packed_weight_bytes(h) bytes, kept allocated while the handle is used); the
+ * handle reads dst from then on, and the row-major projection matrices are not read again (embed, the
+ * norm gains and fc_b still are).  Must be called before dflash_draft_block / dflash_inject_ctx on a BF16
+ * handle (they return DFLASH_E_ARG otherwise).  Every matrix must be 16-byte aligned.  F32 handles: no-op. */
+size_t dflash_packed_weight_bytes(const dflash_handle *h);
+int dflash_pack_weights(dflash_handle *h, void *dst, size_t dst_bytes, void *stream);
+
 /* Workspace bytes for dflash_draft_block with batch <= max_batch, context lengths <= max_ctx and
  * top_k <= 8.  Returns 0 on invalid arguments.                                                           */
 size_t dflash_draft_workspace_bytes(const dflash_handle *h, int max_batch, int max_ctx);
@@ -178,8 +192,9 @@ const char *dflash_last_error(void);
 /* ---- building blocks (tests, measurement) ----------------------------------------------------------- */
 
 /* y[m][n] = sum_k x[m][k] * w[n][k] for m < M, n < N, with float32 output (row stride N).  x is [M][K]
- * (row stride ldx elements) and w [N][K], both of `dtype`.  Uses the same GEMM kernels as the drafter
- * pass.  ws must hold dflash_linear_workspace_bytes(dtype, M, N, K) bytes.                                 */
+ * (row stride ldx elements) and w [N][K] row-major, both of `dtype`, 16-byte aligned.  Uses the same GEMM
+ * kernels as the drafter pass (BF16: w is first packed into the workspace).  ws (16-byte aligned) must hold
+ * dflash_linear_workspace_bytes(dtype, M, N, K) bytes.                                                     */
 size_t dflash_linear_workspace_bytes(int dtype, int M, int N, int K);
 int dflash_linear(int dtype, int M, int N, int K, const void *x, int64_t ldx, const void *w, float *y, void *ws,
                   size_t ws_bytes, void *stream);

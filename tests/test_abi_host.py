@@ -61,7 +61,7 @@ class _Fake:
 
 
 def _create(D, shape, bad=None):
-    return D.DraftModel(shape, _fake_weights(shape, bad))
+    return D.DraftModel(shape, _fake_weights(shape, bad), pack=False)
 
 
 def test_create_accepts_supported_shapes(D):
@@ -179,3 +179,51 @@ def test_accept_and_linear_validation(D):
     assert D.dflash_linear(1, 16, 64, 256, 0x10, 256, 0x20, 0x30, 0x40, 16, None) == -3
     assert D.dflash_linear_workspace_bytes(1, 16, 4096, 4096) > 0
     assert D.dflash_copy(0x10, 0x20, 17, None) == -1
+
+
+def _packed_elems(n, k):
+    return -(-n // 16) * 16 * k
+
+
+def test_packed_weight_store_size(D):
+    """The packed store holds every projection matrix once, each padded to whole 16-row fragments."""
+    import workloads as W
+    for s in (W.QWEN3_8B, W.SMALL_BF16, W.SMALL_GQA8):
+        m = _create(D, s)
+        qd, kvd, H, F = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim, s.hidden, s.ffn
+        per_layer = (_packed_elems(qd, H) + 4 * _packed_elems(kvd, H) + _packed_elems(H, qd) + 2 * _packed_elems(F, H)
+                     + _packed_elems(H, F))
+        want = 2 * (s.n_layers * per_layer + _packed_elems(H, s.feat_dim) + _packed_elems(s.vocab, H))
+        assert D.dflash_packed_weight_bytes(m.handle) == want
+        m.close()
+    m = _create(D, W.SMALL_FP32)
+    assert D.dflash_packed_weight_bytes(m.handle) == 0
+    assert D.dflash_pack_weights(m.handle, None, 0, None) == 0  # float32: nothing to pack, no HIP call
+    m.close()
+
+
+@pytest.mark.parametrize("dst,nbytes,code", [
+    (None, 1 << 40, -1),
+    (0x100010, 1 << 40, -1),   # misaligned
+    (0x100000, 1024, -3),      # too small
+])
+def test_pack_weights_validation(D, dst, nbytes, code):
+    m = _create(D, _shape())
+    try:
+        assert D.dflash_pack_weights(m.handle, dst, nbytes, None) == code
+        assert D.dflash_last_error()
+    finally:
+        m.close()
+
+
+def test_unpacked_bf16_handle_refuses_to_run(D):
+    m = _create(D, _shape())
+    try:
+        assert _draft(D, m.handle) == D.DFLASH_E_ARG
+        assert "packed" in D.dflash_last_error()
+        kv = D.dflash_kv(0x40, 0x50, 8)
+        rc = D.dflash_inject_ctx(m.handle, 1, 4, 0x10, m.shape.feat_dim, 0x20, 0x30, 0x40, 8, kv, 0x100000, 1 << 40,
+                                 None)
+        assert rc == D.DFLASH_E_ARG and "packed" in D.dflash_last_error()
+    finally:
+        m.close()
