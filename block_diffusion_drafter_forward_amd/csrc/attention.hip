@@ -13,16 +13,26 @@
 
 namespace df {
 
-AttnPlan plan_attention(int batch, int n_kv, int max_ctx) {
-    AttnPlan p{0, 64};
+#define AT_MAX_PAGES 256  // pages of one context chunk (their ids are staged in LDS up front)
+
+// Keys staged per LDS round (four pages).  Measured on MI355X at the Qwen3-8B decode shape: 64-key rounds
+// with 128-key chunks beat 128-key rounds (fewer registers, two rounds to overlap load and compute).
+static int attn_sub(int) { return 64; }
+
+AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx) {
+    const int sub = attn_sub(n_q / n_kv);
+    AttnPlan p{0, sub};
     if (max_ctx <= 0) return p;
+    // about one workgroup per CU over (request, KV head, chunk), chunks of whole staging rounds and at
+    // most AT_MAX_PAGES pages
     const int units = batch * n_kv;
     int want = (256 + units - 1) / units;
-    const int max_chunks = (max_ctx + 127) / 128;  // at least two sub-chunks per workgroup
+    const int max_chunks = (max_ctx + sub - 1) / sub;
     if (want > max_chunks) want = max_chunks;
     if (want < 1) want = 1;
     int ct = (max_ctx + want - 1) / want;
-    ct = (ct + 63) / 64 * 64;  // whole 64-key sub-chunks
+    ct = (ct + sub - 1) / sub * sub;
+    if (ct > 16 * AT_MAX_PAGES) ct = 16 * AT_MAX_PAGES;
     p.chunk_tokens = ct;
     p.n_chunks = (max_ctx + ct - 1) / ct;
     return p;
@@ -32,23 +42,23 @@ size_t attn_partial_floats(int batch, int nq, int n_chunks, int d) {
     return (size_t)batch * nq * (n_chunks + 1) * 16 * (size_t)(d + 2);
 }
 
-__device__ __forceinline__ uint32_t pack2(bf16_t lo, bf16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
 // ------------------------------------------------------------------------------------------------------
 // bfloat16 MFMA kernel (head_dim 128)
 // ------------------------------------------------------------------------------------------------------
-// Sub-chunks of 64 keys (four 16-key pages) are staged in LDS by the whole workgroup, so the G query heads
-// of a KV group read each K/V byte from HBM once.  While the waves compute on one sub-chunk, the next one is
-// already in flight into registers.  Slots past the chunk's last key and pages the table does not map are
-// staged as zeros, so uninitialised cache memory can never reach the MFMAs.
+// Sub-chunks of SUB keys (SUB / 16 pages) are staged in LDS by the whole
+// workgroup, so the G query heads of a KV group read each K/V byte from HBM once.  The chunk's page ids and
+// the context length are fetched together up front (neither load waits on the other), and while the waves
+// compute on one sub-chunk the next one is already in flight into registers.  Slots past the chunk's last
+// key and pages the table does not map are staged as zeros, so uninitialised cache memory can never reach
+// the MFMAs.
 // q and the block's own k / v are activation pairs (hi + lo bfloat16 planes); the cached K/V are plain
 // bfloat16.  The block chunk stages its hi page in page slot 0 and its lo page in slot 1 and multiplies
 // every pair of terms.
-#define AT_SUB 64
 #define AT_KLD (128 + 8)  // padded LDS row of a key (elements): 16 consecutive keys hit distinct banks
 #define AT_VLD (16 + 8)   // padded LDS row of one d within a page's transposed values
 
-template <int G>
+template <int G, int SUB>
 __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kb,
                                                     const bf16_t* __restrict__ vbt, const bf16_t* __restrict__ kpool,
                                                     const bf16_t* __restrict__ vpool, int layer, int n_pages,
@@ -59,10 +69,12 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
                                                     uint32_t* err) {
     constexpr int D = 128;
     constexpr int NT = 64 * G;
-    constexpr int PIECES = 4 * 512;  // 16-byte pieces per sub-chunk: per page 256 of K and 256 of V^T
+    constexpr int NPG = SUB / 16;        // pages per sub-chunk
+    constexpr int PIECES = NPG * 512;    // 16-byte pieces per sub-chunk: per page 256 of K and 256 of V^T
     constexpr int PPT = PIECES / NT;
-    __shared__ __attribute__((aligned(16))) bf16_t sk[AT_SUB * AT_KLD];
-    __shared__ __attribute__((aligned(16))) bf16_t sv[4 * D * AT_VLD];
+    __shared__ __attribute__((aligned(16))) bf16_t sk[SUB * AT_KLD];
+    __shared__ __attribute__((aligned(16))) bf16_t sv[NPG * D * AT_VLD];
+    __shared__ int spg[AT_MAX_PAGES];
     const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -74,6 +86,10 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
     int t0 = 0, t1 = 0;
     const bool block_chunk = (c == 0);
     if (!block_chunk) {
+        // page ids of the chunk (-1 past the table), loaded before the context length is known
+        const int pg0 = (c - 1) * (chunk_tokens / 16);
+        for (int j = tid; j < chunk_tokens / 16; j += NT)
+            spg[j] = pg0 + j < max_pages ? pt[(size_t)b * max_pages + pg0 + j] : -1;
         int ctx = ctx_len[b];
         if (ctx > max_ctx || ctx < 0) {
             if (c == 1 && tid == 0) set_err(err, DFLASH_DEVERR_POS);
@@ -87,70 +103,68 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
 
     const size_t bplane = (size_t)gridDim.z * nkv * page_elems;  // hi -> lo plane of the block's k / v
     const size_t qplane = (size_t)gridDim.z * L * nq * D;          // hi -> lo plane of q
-    // source page of page slot e of the sub-chunk starting at key ts; nullptr if unmapped
-    auto page_src = [&](int ts, int e, const bf16_t*& kp, const bf16_t*& vp) {
-        const int tp = ts + 16 * e;
-        kp = nullptr;
-        vp = nullptr;
-        if (block_chunk) {
-            if (e < 2) {
-                kp = kb + ((size_t)b * nkv + kvh) * page_elems + e * bplane;
-                vp = vbt + ((size_t)b * nkv + kvh) * page_elems + e * bplane;
-            }
-            return;
-        }
-        if (tp >= t1) return;
-        const int pi = tp >> 4;
-        if (pi >= max_pages) {
-            if (lane == 0 && w == 0) set_err(err, DFLASH_DEVERR_POS);
-            return;
-        }
-        const int page = pt[(size_t)b * max_pages + pi];
-        if (page < 0 || page >= n_pages) {
-            if (lane == 0 && w == 0) set_err(err, DFLASH_DEVERR_PAGE);
-            return;
-        }
-        const size_t pg = ((size_t)layer * n_pages + page) * nkv + kvh;
-        kp = kpool + pg * page_elems;
-        vp = vpool + pg * page_elems;
-    };
-
+    // Staging: a page is 512 16-byte pieces (256 of K, then 256 of V^T), and piece j of either half sits at
+    // element 8 j of its page, so thread tid moves pieces tid, tid + NT, ... of every page of the sub-chunk:
+    // the per-thread offsets are compile-time constants and only the page bases change per sub-chunk.
+    constexpr int PPP = 512 / NT;  // pieces per page per thread
     u32x4 pf[PPT];
+    uint32_t okmask = 0;
+    // Page slot e of the sub-chunk starting at key ts: its K and V^T bases always name readable memory (an
+    // unmapped or out-of-range slot reads page 0 of the layer) and bit e of okmask says whether the slot
+    // holds data.  Loads are issued unconditionally and the unmapped slots zeroed at stash time, so no
+    // load has to wait for another.
     auto prefetch = [&](int ts) {
+        okmask = 0;
 #pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            const int p = tid + i * NT;
-            const int e = p >> 9, qq = p & 511;
-            const bf16_t *kp, *vp;
-            page_src(ts, e, kp, vp);
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (qq < 256) {
-                if (kp) v = ld16(kp + (qq >> 4) * D + (qq & 15) * 8);
-            } else if (vp) {
-                const int q2 = qq - 256, d = q2 >> 1, half = q2 & 1;
-                v = ld16(vp + d * 16 + half * 8);
-                // zero the values of slots past the last key (they may hold anything)
-                const int nvalid = block_chunk ? L : t1 - (ts + 16 * e);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int s0 = half * 8 + 2 * j;
-                    uint32_t m = (s0 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
-                    v[j] &= m;
-                }
+        for (int e = 0; e < NPG; ++e) {
+            size_t kofs, vofs;
+            bool ok;
+            if (block_chunk) {
+                kofs = vofs = ((size_t)b * nkv + kvh) * page_elems + (e < 2 ? e : 0) * bplane;
+                ok = e < 2;
+            } else {
+                const int tp = ts + 16 * e;
+                const int page = tp < t1 ? spg[(tp - t0) >> 4] : -1;
+                ok = page >= 0 && page < n_pages;
+                kofs = vofs = (((size_t)layer * n_pages + (ok ? page : 0)) * nkv + kvh) * page_elems;
             }
-            pf[i] = v;
+            okmask |= (ok ? 1u : 0u) << e;
+            const bf16_t* kbase = (block_chunk ? kb : kpool) + kofs;
+            const bf16_t* vbase = (block_chunk ? vbt : vpool) + vofs;
+#pragma unroll
+            for (int u = 0; u < PPP; ++u) {
+                const int qq = tid + u * NT;
+                pf[e * PPP + u] = ld16((qq < 256 ? kbase : vbase) + (qq & 255) * 8);
+            }
         }
     };
-    auto stash = [&]() {
+    auto stash = [&](int ts) {
+        okmask = __builtin_amdgcn_readfirstlane(okmask);  // the same in every lane: keep the branches scalar
 #pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            const int p = tid + i * NT;
-            const int e = p >> 9, qq = p & 511;
-            if (qq < 256) {
-                *(u32x4*)(sk + (e * 16 + (qq >> 4)) * AT_KLD + (qq & 15) * 8) = pf[i];
-            } else {
-                const int q2 = qq - 256, d = q2 >> 1, half = q2 & 1;
-                *(u32x4*)(sv + (e * D + d) * AT_VLD + half * 8) = pf[i];
+        for (int e = 0; e < NPG; ++e) {
+            const bool ok = (okmask >> e) & 1u;
+            const int nvalid = block_chunk ? L : t1 - (ts + 16 * e);
+#pragma unroll
+            for (int u = 0; u < PPP; ++u) {
+                const int qq = tid + u * NT;
+                u32x4 v = pf[e * PPP + u];
+                if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+                if (qq < 256) {
+                    *(u32x4*)(sk + (e * 16 + (qq >> 4)) * AT_KLD + (qq & 15) * 8) = v;
+                } else {
+                    const int q2 = qq - 256;
+                    if (nvalid < 16) {
+                        // zero the values of slots past the last key (they may hold anything)
+                        const int half = q2 & 1;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int s0 = half * 8 + 2 * j;
+                            const uint32_t m = (s0 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
+                            v[j] &= m;
+                        }
+                    }
+                    *(u32x4*)(sv + (e * D + (q2 >> 1)) * AT_VLD + (q2 & 1) * 8) = v;
+                }
             }
         }
     };
@@ -172,14 +186,23 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
     for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
+    __syncthreads();  // page ids in LDS
+    if (!block_chunk) {
+        // flag pages the chunk needs that lie beyond the table or outside the pool (their slots read as zero)
+        for (int j = tid; j < chunk_tokens / 16 && t0 + 16 * j < t1; j += NT) {
+            if ((t0 >> 4) + j >= max_pages) set_err(err, DFLASH_DEVERR_POS);
+            else if (spg[j] < 0 || spg[j] >= n_pages) set_err(err, DFLASH_DEVERR_PAGE);
+        }
+    }
     if (t0 < t1) prefetch(t0);
-    for (int ts = t0; ts < t1; ts += AT_SUB) {
+    for (int ts = t0; ts < t1; ts += SUB) {
+        const int ts_staged = ts;
         __syncthreads();
-        stash();
+        stash(ts_staged);
         __syncthreads();
-        if (ts + AT_SUB < t1) prefetch(ts + AT_SUB);
+        if (ts + SUB < t1) prefetch(ts + SUB);
         // scores S^T[key][query]: lane holds keys 4g+i of each page for query r
-        float x[4][4];
+        float x[NPG][4];
         if (block_chunk) {
             // the block's keys: (K_hi + K_lo)(Q_hi + Q_lo)^T, keys in page slot 0 only
             f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -196,29 +219,41 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 x[0][i] = 4 * g + i < L ? sa[i] * scale_log2 : -INFINITY;
-                x[1][i] = x[2][i] = x[3][i] = -INFINITY;
+#pragma unroll
+                for (int e = 1; e < NPG; ++e) x[e][i] = -INFINITY;
             }
         } else {
+            // every page's tile first (independent MFMA chains; hi and lo query terms in separate
+            // accumulators), then scale, and mask only in a sub-chunk that runs past the chunk's end
+            f32x4 sh[NPG], sl[NPG];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
-                const bf16_t* kr = sk + (e * 16 + r) * AT_KLD + g * 8;
+            for (int e = 0; e < NPG; ++e) {
+                sh[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+                sl[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const u32x4 kf = ld16(kr + s * 32);
-                    sa = mfma16(kf, qf[s], sa);
-                    sa = mfma16(kf, ql[s], sa);
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int e = 0; e < NPG; ++e) {
+                    const u32x4 kf = ld16(sk + (e * 16 + r) * AT_KLD + g * 8 + s * 32);
+                    sh[e] = mfma16(kf, qf[s], sh[e]);
+                    sl[e] = mfma16(kf, ql[s], sl[e]);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = ts + 16 * e + 4 * g + i;
-                    x[e][i] = key < t1 ? sa[i] * scale_log2 : -INFINITY;
-                }
+            for (int e = 0; e < NPG; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[e][i] = (sh[e][i] + sl[e][i]) * scale_log2;
+            if (ts + SUB > t1) {
+                const int nk = t1 - ts;
+#pragma unroll
+                for (int e = 0; e < NPG; ++e)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[e][i] = 16 * e + 4 * g + i < nk ? x[e][i] : -INFINITY;
             }
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < NPG; ++e)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[e][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -226,15 +261,15 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
         const float m_new = fmaxf(m_run, mx);
         // while every key so far is masked use 0 as reference: alpha and p become 0, not exp2(-inf + inf)
         const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_ref);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
         m_run = m_new;
-        float p[4][4];
+        float p[NPG][4];
         float psum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < NPG; ++e)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[e][i] = exp2f(x[e][i] - m_ref);
+                p[e][i] = __builtin_amdgcn_exp2f(x[e][i] - m_ref);
                 psum += p[e][i];
             }
         l_run = l_run * alpha + psum;
@@ -242,20 +277,18 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
         for (int dt = 0; dt < 8; ++dt) {
             o[dt][0] *= alpha; o[dt][1] *= alpha; o[dt][2] *= alpha; o[dt][3] *= alpha;
         }
-        // O^T += V^T P^T over the two 32-key halves; P enters as two bfloat16 terms (hi + lo)
+        // O^T += V^T P^T over the sub-chunk's 32-key slices; P enters as two bfloat16 terms (hi + lo)
 #pragma unroll
-        for (int hk = 0; hk < 2; ++hk) {
+        for (int hk = 0; hk < NPG / 2; ++hk) {
             if (ts + 32 * hk >= t1) break;  // uniform: the rest of the sub-chunk is masked
-            bf16_t hi[8], lo[8];
+            u32x4 phi, plo;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float v = p[2 * hk + (j >> 2)][j & 3];
-                const bf16_t hb = f2bf(v);
-                hi[j] = hb;
-                lo[j] = f2bf(v - bf2f(hb));
+            for (int j = 0; j < 4; ++j) {
+                const float v0 = p[2 * hk + (j >> 1)][2 * (j & 1)], v1 = p[2 * hk + (j >> 1)][2 * (j & 1) + 1];
+                const uint32_t h2 = f2bf2(v0, v1);
+                phi[j] = h2;
+                plo[j] = f2bf2(v0 - __uint_as_float(h2 << 16), v1 - __uint_as_float(h2 & 0xFFFF0000u));
             }
-            const u32x4 phi = u32x4{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])};
-            const u32x4 plo = u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])};
             if (block_chunk) {
                 // (V_hi + V_lo)^T over the block's keys (page slot 0 of the operand; slot 1 holds the lo plane)
 #pragma unroll
@@ -422,8 +455,9 @@ hipError_t launch_attention(int bf16, const AttnPlan& p, int B, int L, int nq, i
     if (bf16) {
         const int G = nq / nkv;
         const dim3 grid(p.n_chunks + 1, nkv, B);
+        if (p.chunk_tokens % attn_sub(G) || p.chunk_tokens > 16 * AT_MAX_PAGES) return hipErrorInvalidValue;
 #define DF_ATTN(GG)                                                                                                \
-    hipLaunchKernelGGL(attn_bf16<GG>, grid, dim3(64 * GG), 0, st, (const bf16_t*)q, (const bf16_t*)kb,            \
+    hipLaunchKernelGGL((attn_bf16<GG, 64>), grid, dim3(64 * GG), 0, st, (const bf16_t*)q, (const bf16_t*)kb,            \
                        (const bf16_t*)vbt, (const bf16_t*)kpool, (const bf16_t*)vpool, layer, n_pages, page_table, \
                        max_pages, ctx_len, max_ctx, p.chunk_tokens, p.n_chunks, L, nq, nkv, opart, mlpart, err)
         switch (G) {
