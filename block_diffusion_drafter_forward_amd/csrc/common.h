@@ -134,33 +134,3 @@ __device__ __forceinline__ bool df_better(float v, int id, float w, int jd) {
     return v > w || (v == w && id < jd);
 }
 
-struct TopK {
-    float v[DF_TOPK];
-    int id[DF_TOPK];
-    float mx;   // running max of every value seen
-    float se;   // running sum of exp(value - mx)
-    __device__ __forceinline__ void init() {
-#pragma unroll
-        for (int j = 0; j < DF_TOPK; ++j) { v[j] = -INFINITY; id[j] = 0x7FFFFFFF; }
-        mx = -INFINITY;
-        se = 0.f;
-    }
-    __device__ __forceinline__ void push(float x, int xid) {
-        if (x > mx) { se = se * expf(mx - x) + 1.f; mx = x; }
-        else se += expf(x - mx);
-        if (!df_better(x, xid, v[DF_TOPK - 1], id[DF_TOPK - 1])) return;
-        // insertion into the sorted list, branch-free over the fixed length
-        float cv = x;
-        int ci = xid;
-#pragma unroll
-        for (int j = 0; j < DF_TOPK; ++j) {
-            bool b = df_better(cv, ci, v[j], id[j]);
-            float tv = v[j];
-            int ti = id[j];
-            v[j] = b ? cv : tv;
-            id[j] = b ? ci : ti;
-            cv = b ? tv : cv;
-            ci = b ? ti : ci;
-        }
-    }
-};

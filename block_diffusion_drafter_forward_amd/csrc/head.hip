@@ -1,9 +1,8 @@
-// Shared LM head fused with the per-row reductions the drafter needs: running max, sum of exponentials
-// (for the log-sum-exp over the full vocabulary) and the top-8 (logit, id) list, ordered by logit then id.
-// Logits live only in registers and LDS.  Stage 1 (lm_head): one workgroup per 64 vocabulary rows, four
-// waves splitting K, writes one (max, sumexp, top-8) record per block row.  Stage 2 (head_merge): one
-// workgroup per block row merges the records in a fixed order and emits the greedy token, the top-k ids
-// and their log-probabilities.
+// Shared LM head fused with the per-row reductions the drafter needs: max, sum of exponentials (for the
+// log-sum-exp over the full vocabulary) and the top-8 (logit, id) list, ordered by logit then id.  Logits
+// live only in registers and LDS.  Stage 1 (lm_head): one workgroup per 64 vocabulary rows, four waves
+// splitting K, writes one (max, sumexp, top-8) record per block row.  Stage 2 (head_merge): one workgroup
+// per block row combines the records and emits the greedy token, the top-k ids and their log-probabilities.
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -11,6 +10,8 @@
 namespace df {
 
 #define HEAD_REC 18  // max, sumexp, 8 values, 8 ids (as int bits)
+// Records are stored field-major per block row, hpart[(row * HEAD_REC + field) * groups + group], so that the
+// merge reads each field of consecutive groups with coalesced loads.
 
 // Vocabulary columns per record group: 64 for the skinny head (block rows <= 32), 128 for the tiled head.
 int head_group_width(int bf16, int M) { return (bf16 && M > 32) ? 128 : 64; }
@@ -19,81 +20,110 @@ size_t head_partial_floats(int bf16, int V, int M) {
     return (size_t)head_groups(V, head_group_width(bf16, M)) * M * HEAD_REC;
 }
 
-__device__ __forceinline__ void topk_insert(TopK& s, float x, int xid) {
-    if (!df_better(x, xid, s.v[DF_TOPK - 1], s.id[DF_TOPK - 1])) return;
-    float cv = x;
-    int ci = xid;
+// Top-8 lists: (value, id) entries sorted best-first by df_better; empty slots hold (-inf, INT_MAX).
+struct Top8 {
+    float v[DF_TOPK];
+    int id[DF_TOPK];
+    __device__ __forceinline__ void clear() {
 #pragma unroll
-    for (int j = 0; j < DF_TOPK; ++j) {
-        const bool b = df_better(cv, ci, s.v[j], s.id[j]);
-        const float tv = s.v[j];
-        const int ti = s.id[j];
-        s.v[j] = b ? cv : tv;
-        s.id[j] = b ? ci : ti;
-        cv = b ? tv : cv;
-        ci = b ? ti : ci;
+        for (int j = 0; j < DF_TOPK; ++j) { v[j] = -INFINITY; id[j] = 0x7FFFFFFF; }
     }
-}
-
-// merge state o into s: lists by insertion (o's list is sorted, so the first candidate that does not make
-// s's list ends the merge), (max, sumexp) by rescaling to the larger max
-__device__ __forceinline__ void topk_merge(TopK& s, const float* ov, const int* oid, float omx, float ose) {
-    bool go = true;  // fully unrolled with a predicate so that ov / oid stay in registers
-#pragma unroll
-    for (int j = 0; j < DF_TOPK; ++j) {
-        go = go && df_better(ov[j], oid[j], s.v[DF_TOPK - 1], s.id[DF_TOPK - 1]);
-        if (go) topk_insert(s, ov[j], oid[j]);
-    }
-    if (omx == -INFINITY) return;
-    if (s.mx == -INFINITY) { s.mx = omx; s.se = ose; return; }
-    const float M = fmaxf(s.mx, omx);
-    s.se = s.se * expf(s.mx - M) + ose * expf(omx - M);
-    s.mx = M;
-}
-
-// Row reductions over a logits tile lg[R][C] held in LDS (vocabulary columns n0 .. n0+C-1, block rows
-// row0 .. row0+R-1, of which `rows` are valid).  Threads split each row into TPR pieces, then the first
-// thread of the row merges the pieces and writes the record of (group, row).
-template <int R, int C>
-__device__ void head_epilogue(const float (*lg)[C + 1], float (*st)[HEAD_REC], int rows, int row0, int Mtot, int n0,
-                              int V, int group, float* __restrict__ hpart, float* __restrict__ logits_dbg) {
-    constexpr int TPR = 256 / R, CPT = C / TPR;
-    const int t = threadIdx.x;
-    const int m = t / TPR, c0 = (t % TPR) * CPT;
-    TopK s;
-    s.init();
-    if (m < rows) {
-        for (int c = c0; c < c0 + CPT; ++c) {
-            const int v = n0 + c;
-            if (v >= V) break;
-            const float x = lg[m][c];
-            s.push(x, v);
-            if (logits_dbg) logits_dbg[(size_t)(row0 + m) * V + v] = x;
-        }
-    }
-    st[t][0] = s.mx;
-    st[t][1] = s.se;
-#pragma unroll
-    for (int j = 0; j < DF_TOPK; ++j) {
-        st[t][2 + j] = s.v[j];
-        st[t][2 + DF_TOPK + j] = __int_as_float(s.id[j]);
-    }
-    __syncthreads();
-    if (m < rows && (t % TPR) == 0) {
-        for (int q = 1; q < TPR; ++q) {
-            const float* o = st[t + q];
-            int oid[DF_TOPK];
-#pragma unroll
-            for (int j = 0; j < DF_TOPK; ++j) oid[j] = __float_as_int(o[2 + DF_TOPK + j]);
-            topk_merge(s, o + 2, oid, o[0], o[1]);
-        }
-        float* dst = hpart + ((size_t)group * Mtot + row0 + m) * HEAD_REC;
-        dst[0] = s.mx;
-        dst[1] = s.se;
+    // insertion of one entry, branch-free over the fixed length
+    __device__ __forceinline__ void insert(float x, int xid) {
+        float cv = x;
+        int ci = xid;
 #pragma unroll
         for (int j = 0; j < DF_TOPK; ++j) {
-            dst[2 + j] = s.v[j];
-            dst[2 + DF_TOPK + j] = __int_as_float(s.id[j]);
+            const bool b = df_better(cv, ci, v[j], id[j]);
+            const float tv = v[j];
+            const int ti = id[j];
+            v[j] = b ? cv : tv;
+            id[j] = b ? ci : ti;
+            cv = b ? tv : cv;
+            ci = b ? ti : ci;
+        }
+    }
+    // this := best 8 of this and o (both sorted).  Bitonic merge: the better of v[i] and o[7 - i] for every i
+    // is a bitonic sequence holding the best 8 of the union; three half-cleaner stages sort it.
+    __device__ __forceinline__ void merge(const float (&ov)[DF_TOPK], const int (&oid)[DF_TOPK]) {
+#pragma unroll
+        for (int i = 0; i < DF_TOPK; ++i) {
+            const bool t = df_better(ov[DF_TOPK - 1 - i], oid[DF_TOPK - 1 - i], v[i], id[i]);
+            v[i] = t ? ov[DF_TOPK - 1 - i] : v[i];
+            id[i] = t ? oid[DF_TOPK - 1 - i] : id[i];
+        }
+#pragma unroll
+        for (int d = DF_TOPK / 2; d > 0; d >>= 1)
+#pragma unroll
+            for (int i = 0; i < DF_TOPK; ++i)
+                if ((i & d) == 0) {
+                    const bool sw = df_better(v[i + d], id[i + d], v[i], id[i]);
+                    const float a = v[i], b = v[i + d];
+                    const int ia = id[i], ib = id[i + d];
+                    v[i] = sw ? b : a;
+                    id[i] = sw ? ib : ia;
+                    v[i + d] = sw ? a : b;
+                    id[i + d] = sw ? ia : ib;
+                }
+    }
+    // merge with the list held by lane (lane ^ o) of the wave
+    __device__ __forceinline__ void merge_lane_xor(int o) {
+        float ov[DF_TOPK];
+        int oid[DF_TOPK];
+#pragma unroll
+        for (int j = 0; j < DF_TOPK; ++j) {
+            ov[j] = __shfl_xor(v[j], o, DF_WAVE);
+            oid[j] = __shfl_xor(id[j], o, DF_WAVE);
+        }
+        merge(ov, oid);
+    }
+};
+
+// Row reductions over a logits tile lg[R][C] held in LDS (vocabulary columns n0 .. n0+C-1, block rows
+// row0 .. row0+R-1, of which `rows` are valid).  The TPR = 256 / R threads of a row are consecutive lanes of
+// one wave; each takes C / TPR columns, and the row's max, sum of exponentials and top-8 list are combined
+// by a butterfly over those lanes (xor shuffles: every lane ends with the same, order-independent result).
+// The first thread of the row writes the record of (group, row).
+template <int R, int C>
+__device__ void head_epilogue(const float (*lg)[C + 1], int rows, int row0, int Mtot, int n0, int V, int group,
+                              float* __restrict__ hpart, float* __restrict__ logits_dbg) {
+    constexpr int TPR = 256 / R, CPT = C / TPR;
+    static_assert(TPR <= DF_WAVE && (TPR & (TPR - 1)) == 0, "a row's threads must share a wave");
+    const int t = threadIdx.x;
+    const int m = t / TPR, piece = t % TPR, c0 = piece * CPT;
+    const bool live = m < rows;
+    const int ncol = live ? min(CPT, V - (n0 + c0)) : 0;  // valid columns of this thread (may be <= 0)
+    float mx = -INFINITY;
+    for (int c = 0; c < ncol; ++c) {
+        const float x = lg[m][c0 + c];
+        mx = fmaxf(mx, x);
+        if (logits_dbg) logits_dbg[(size_t)(row0 + m) * V + n0 + c0 + c] = x;
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, DF_WAVE));
+    float se = 0.f;
+    Top8 s;
+    s.clear();
+    for (int c = 0; c < ncol; ++c) {
+        const float x = lg[m][c0 + c];
+        se += expf(x - mx);
+        s.insert(x, n0 + c0 + c);
+    }
+    // (kept rolled: one copy of the merge network keeps the compiler's work linear)
+#pragma unroll 1
+    for (int o = 1; o < TPR; o <<= 1) {
+        se += __shfl_xor(se, o, DF_WAVE);
+        s.merge_lane_xor(o);
+    }
+    if (live && piece == 0) {
+        const size_t G = gridDim.x;  // record groups
+        float* dst = hpart + (size_t)(row0 + m) * HEAD_REC * G + group;
+        dst[0] = mx;
+        dst[G] = se;
+#pragma unroll
+        for (int j = 0; j < DF_TOPK; ++j) {
+            dst[(2 + j) * G] = s.v[j];
+            dst[(2 + DF_TOPK + j) * G] = __int_as_float(s.id[j]);
         }
     }
 }
@@ -110,7 +140,6 @@ __global__ __launch_bounds__(256) void lm_head_bf16(const bf16_t* __restrict__ z
     constexpr int NT = 4;
     __shared__ f32x4 red[4][NT * MT][64];
     __shared__ float lg[16 * MT][65];
-    __shared__ float st[256][HEAD_REC];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * 64;
@@ -188,7 +217,7 @@ __global__ __launch_bounds__(256) void lm_head_bf16(const bf16_t* __restrict__ z
         lg[m][c + 3] = v[3];
     }
     __syncthreads();
-    head_epilogue<16 * MT, 64>(lg, st, M, 0, M, n0, V, blockIdx.x, hpart, logits_dbg);
+    head_epilogue<16 * MT, 64>(lg, M, 0, M, n0, V, blockIdx.x, hpart, logits_dbg);
 }
 
 // ------------------------------------------------------------------------------------------------------
@@ -198,7 +227,6 @@ __global__ __launch_bounds__(256) void lm_head_f32(const float* __restrict__ z, 
                                                    int V, int K, float* __restrict__ hpart,
                                                    float* __restrict__ logits_dbg) {
     __shared__ float lg[32][65];
-    __shared__ float st[256][HEAD_REC];
     const int n0 = blockIdx.x * 64;
     const int c = threadIdx.x & 63;
     const float* wr = W + (size_t)min(n0 + c, V - 1) * K;
@@ -211,7 +239,7 @@ __global__ __launch_bounds__(256) void lm_head_f32(const float* __restrict__ z, 
         lg[m][c] = a;
     }
     __syncthreads();
-    head_epilogue<32, 64>(lg, st, M, 0, M, n0, V, blockIdx.x, hpart, logits_dbg);
+    head_epilogue<32, 64>(lg, M, 0, M, n0, V, blockIdx.x, hpart, logits_dbg);
 }
 
 // ------------------------------------------------------------------------------------------------------
@@ -220,16 +248,14 @@ __global__ __launch_bounds__(256) void lm_head_f32(const float* __restrict__ z, 
 // The tiled GEMM main loop leaves each wave a 64 x 64 block of logits in registers; the tile is parked in
 // LDS (over the staging buffers, which are free after the loop) and the row reductions run on it.
 #define TH_LG_BYTES (128 * 129 * 4)
-#define TH_ST_BYTES (256 * HEAD_REC * 4)
 __global__ __launch_bounds__(256) void lm_head_tiled_bf16(const bf16_t* __restrict__ z, size_t zplane, int M,
                                                           const bf16_t* __restrict__ W, int V, int K,
                                                           float* __restrict__ hpart, float* __restrict__ logits_dbg) {
     static_assert(TH_LG_BYTES >= (TL_SW + 2 * TL_BM * TL_LD) * 2, "logits tile must cover the staging buffers");
-    __shared__ __attribute__((aligned(16))) char smem[TH_LG_BYTES + TH_ST_BYTES];
+    __shared__ __attribute__((aligned(16))) char smem[TH_LG_BYTES];
     bf16_t* sw = (bf16_t*)smem;
     bf16_t* sx = sw + TL_SW;
     float(*lg)[129] = (float(*)[129])smem;
-    float(*st)[HEAD_REC] = (float(*)[HEAD_REC])(smem + TH_LG_BYTES);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int wn = wave >> 1, wm = wave & 1;
@@ -249,7 +275,7 @@ __global__ __launch_bounds__(256) void lm_head_tiled_bf16(const bf16_t* __restri
             lg[m][n + 3] = acc[a][b][3];
         }
     __syncthreads();
-    head_epilogue<128, 128>(lg, st, min(128, M - m0), m0, M, n0, V, blockIdx.x, hpart, logits_dbg);
+    head_epilogue<128, 128>(lg, min(128, M - m0), m0, M, n0, V, blockIdx.x, hpart, logits_dbg);
 }
 
 hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V, int K, float* hpart,
@@ -274,57 +300,147 @@ hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V
 // ------------------------------------------------------------------------------------------------------
 // stage 2: merge the per-group records of one block row
 // ------------------------------------------------------------------------------------------------------
+// One workgroup per block row.  The log-sum-exp needs only the records' (max, sumexp).  For the top-8, a
+// lower bound T of the row's 8th best logit: (a) the largest 8th entry of any record (that record alone has
+// 8 entries >= it), and (b) the 8th largest of the 16 waves' maxima over their records' maxima (8 distinct
+// records reach it).  Every entry of the row's top 8 is then among the record entries >= T -- about a dozen
+// for continuous logits -- which are gathered in LDS and placed by rank (number of better candidates; ranks
+// are unique because ids are).  If ties push the candidate count past the buffer, a tree of bitonic merges
+// over all records takes over.  The result does not depend on the gathering order: deterministic.
 #define MERGE_THREADS 1024
+#define MERGE_CAP 1024
+__device__ __forceinline__ float block_max(float v, float* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    v = wave_max(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float t = -INFINITY;
+    for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
+    return t;
+}
+
 __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_groups, int top_k,
                                                             const float* __restrict__ hpart,
                                                             const int32_t* __restrict__ btok,
                                                             int32_t* __restrict__ tokens, int32_t* __restrict__ topk_ids,
                                                             float* __restrict__ topk_lp, uint32_t* err) {
-    __shared__ float st[MERGE_THREADS / 2][HEAD_REC];
+    __shared__ float cv[MERGE_CAP];
+    __shared__ int cid[MERGE_CAP];
+    __shared__ float red[MERGE_THREADS / 64];
+    __shared__ float outv[DF_TOPK];
+    __shared__ int outi[DF_TOPK];
+    __shared__ int cnt;
+    __shared__ float t8;
     const int m = blockIdx.x, t = threadIdx.x;
-    if (t == 0 && (btok[m] < 0 || btok[m] >= V)) set_err(err, DFLASH_DEVERR_TOKEN);
-    TopK s;
-    s.init();
-    for (int gi = t; gi < n_groups; gi += MERGE_THREADS) {
-        const float* rec = hpart + ((size_t)gi * M + m) * HEAD_REC;
-        float r[HEAD_REC];
-#pragma unroll
-        for (int j = 0; j < HEAD_REC; ++j) r[j] = rec[j];
-        int oid[DF_TOPK];
-#pragma unroll
-        for (int j = 0; j < DF_TOPK; ++j) oid[j] = __float_as_int(r[2 + DF_TOPK + j]);
-        topk_merge(s, r + 2, oid, r[0], r[1]);
+    if (t == 0) {
+        cnt = 0;
+        t8 = -INFINITY;
+        if (btok[m] < 0 || btok[m] >= V) set_err(err, DFLASH_DEVERR_TOKEN);
     }
-    // fixed-order tree over the thread states
-    for (int half = MERGE_THREADS / 2; half > 0; half >>= 1) {
-        __syncthreads();
-        if (t >= half && t < 2 * half) {
-            float* d = st[t - half];
-            d[0] = s.mx;
-            d[1] = s.se;
+    const size_t G = n_groups;
+    const float* row = hpart + (size_t)m * HEAD_REC * G;  // field f of group gi at row[f * G + gi]
+    float mx = -INFINITY, th = -INFINITY;
+    for (int gi = t; gi < n_groups; gi += MERGE_THREADS) {
+        mx = fmaxf(mx, row[gi]);
+        th = fmaxf(th, row[(2 + DF_TOPK - 1) * G + gi]);
+    }
+    mx = block_max(mx, red);  // leaves the wave maxima in red until the next block reduction
+    if (t < MERGE_THREADS / 64) {
+        const float x = red[t];
+        int rank = 0;
+        for (int j = 0; j < MERGE_THREADS / 64; ++j) rank += (red[j] > x || (red[j] == x && j < t)) ? 1 : 0;
+        if (rank == DF_TOPK - 1) t8 = x;
+    }
+    const float th1 = block_max(th, red);
+    th = fmaxf(th1, t8);  // t8 was written before block_max's barriers
+    float se = 0.f;
+    for (int gi = t; gi < n_groups; gi += MERGE_THREADS) {
+        const float r0 = row[gi];
+        if (r0 != -INFINITY) se += row[G + gi] * expf(r0 - mx);
+        if (r0 >= th) {  // the record's best entry reaches the threshold: scan its list
+            for (int j = 0; j < DF_TOPK; ++j) {
+                const float v = row[(2 + j) * G + gi];
+                const int id = __float_as_int(row[(2 + DF_TOPK + j) * G + gi]);
+                if (v < th) break;
+                if (id < V) {
+                    const int k = atomicAdd(&cnt, 1);
+                    if (k < MERGE_CAP) {
+                        cv[k] = v;
+                        cid[k] = id;
+                    }
+                }
+            }
+        }
+    }
+    se = block_sum(se, red);  // ends with a barrier: cnt and the candidates are complete
+    const int n = cnt;
+    if (n <= MERGE_CAP) {
+        for (int i = t; i < n; i += MERGE_THREADS) {
+            const float vi = cv[i];
+            const int ii = cid[i];
+            int rank = 0;
+            for (int k = 0; k < n; ++k) rank += df_better(cv[k], cid[k], vi, ii) ? 1 : 0;
+            if (rank < DF_TOPK) {
+                outv[rank] = vi;
+                outi[rank] = ii;
+            }
+        }
+    } else {
+        // fallback: bitonic-merge tree over all records (cv / cid reused as list storage)
+        Top8 s;
+        s.clear();
+#pragma unroll 1
+        for (int gi = t; gi < n_groups; gi += MERGE_THREADS) {
+            float ov[DF_TOPK];
+            int oid[DF_TOPK];
 #pragma unroll
             for (int j = 0; j < DF_TOPK; ++j) {
-                d[2 + j] = s.v[j];
-                d[2 + DF_TOPK + j] = __int_as_float(s.id[j]);
+                ov[j] = row[(2 + j) * G + gi];
+                oid[j] = __float_as_int(row[(2 + DF_TOPK + j) * G + gi]);
+            }
+            s.merge(ov, oid);
+        }
+#pragma unroll 1
+        for (int o = 1; o < DF_WAVE; o <<= 1) s.merge_lane_xor(o);
+        const int lane = t & 63, w = t >> 6;
+        __syncthreads();
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < DF_TOPK; ++j) {
+                cv[w * DF_TOPK + j] = s.v[j];
+                cid[w * DF_TOPK + j] = s.id[j];
             }
         }
         __syncthreads();
-        if (t < half) {
-            const float* o = st[t];
-            int oid[DF_TOPK];
+        if (t == 0) {
+#pragma unroll 1
+            for (int q = 1; q < MERGE_THREADS / 64; ++q) {
+                float ov[DF_TOPK];
+                int oid[DF_TOPK];
 #pragma unroll
-            for (int j = 0; j < DF_TOPK; ++j) oid[j] = __float_as_int(o[2 + DF_TOPK + j]);
-            topk_merge(s, o + 2, oid, o[0], o[1]);
+                for (int j = 0; j < DF_TOPK; ++j) {
+                    ov[j] = cv[q * DF_TOPK + j];
+                    oid[j] = cid[q * DF_TOPK + j];
+                }
+                s.merge(ov, oid);
+            }
+#pragma unroll
+            for (int j = 0; j < DF_TOPK; ++j) {
+                outv[j] = s.v[j];
+                outi[j] = s.id[j];
+            }
         }
     }
+    __syncthreads();
     if (t == 0) {
-        const float lse = s.mx + logf(s.se);
-        tokens[m] = s.id[0];
+        const float lse = mx + logf(se);
+        tokens[m] = outi[0];
 #pragma unroll
         for (int j = 0; j < DF_TOPK; ++j) {  // static indices keep the state in registers
             if (j < top_k) {
-                topk_ids[(size_t)m * top_k + j] = s.id[j];
-                topk_lp[(size_t)m * top_k + j] = s.v[j] - lse;
+                topk_ids[(size_t)m * top_k + j] = outi[j];
+                topk_lp[(size_t)m * top_k + j] = outv[j] - lse;
             }
         }
     }
