@@ -3,6 +3,7 @@
 // injected context, and greedy acceptance.  All of them are bandwidth-trivial next to the weight streams;
 // they exist to keep every reduction in a fixed order and every stored tensor in its final layout.
 #include "common.h"
+#include "epilogue.h"
 #include "kernels.h"
 
 namespace df {
@@ -130,16 +131,6 @@ hipError_t launch_resid_norm(int bf16, const float* part, int S, int M, int H, f
 // One thread per (block row m, head, rotary pair i): sums the splits of columns i and i + d/2, applies the
 // rotation at position ctx_len[b] + row to q and k heads, rounds, and stores q row-major, the block's keys as
 // a 16-slot page [b][kv head][slot][d] and its values transposed [b][kv head][d][slot].
-__device__ __forceinline__ void rope_pair(float& a, float& b, int pos, int i, const RopeFreq& rf) {
-    if (!rf.on) return;
-    const float ang = (float)pos * rf.inv[i];
-    float sn, cs;
-    sincosf(ang, &sn, &cs);
-    const float x1 = a, x2 = b;
-    a = x1 * cs - x2 * sn;
-    b = x2 * cs + x1 * sn;
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_epilogue(const float* __restrict__ part, int S, int B, int L, int nq,
                                                     int nkv, int d, const int32_t* __restrict__ ctx_len, RopeFreq rf,
@@ -153,32 +144,13 @@ __global__ __launch_bounds__(256) void qkv_epilogue(const float* __restrict__ pa
     const int i = idx % half;
     const int hd = (idx / half) % heads;
     const int m = idx / ((long)half * heads);
-    const int b = m / L, row = m % L;
     const int c1 = hd * d + i, c2 = c1 + half;
     float a = 0.f, c = 0.f;
     for (int s = 0; s < S; ++s) {
         a += part[((size_t)s * M + m) * N + c1];
         c += part[((size_t)s * M + m) * N + c2];
     }
-    const int pos = ctx_len[b] + row;
-    const size_t qplane = (size_t)M * nq * d, bplane = (size_t)B * nkv * 16 * d;
-    if (hd < nq) {
-        rope_pair(a, c, pos, i, rf);
-        const size_t o = (size_t)m * nq * d + hd * d + i;
-        put_act(q, qplane, o, a);
-        put_act(q, qplane, o + half, c);
-    } else if (hd < nq + nkv) {
-        const int kh = hd - nq;
-        rope_pair(a, c, pos, i, rf);
-        const size_t o = (((size_t)b * nkv + kh) * 16 + row) * d + i;
-        put_act(kb, bplane, o, a);
-        put_act(kb, bplane, o + half, c);
-    } else {
-        const int kh = hd - nq - nkv;
-        const size_t o = ((size_t)b * nkv + kh) * d * 16 + row;
-        put_act(vbt, bplane, o + (size_t)i * 16, a);
-        put_act(vbt, bplane, o + (size_t)(i + half) * 16, c);
-    }
+    qkv_store(a, c, m, hd, i, B, L, nq, nkv, d, ctx_len, rf, q, kb, vbt);
 }
 
 hipError_t launch_qkv_epilogue(int bf16, const float* part, int S, int B, int L, int nq, int nkv, int d,
@@ -199,7 +171,8 @@ hipError_t launch_qkv_epilogue(int bf16, const float* part, int S, int B, int L,
 // SwiGLU and plain reduce + cast
 // ------------------------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void swiglu(const float* __restrict__ part, int S, int M, int F, T* __restrict__ a) {
+__global__ __launch_bounds__(256) void swiglu(const float* __restrict__ part, int S, int M, int F,
+                                              T* __restrict__ a) {
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (long)M * F) return;
     const int m = idx / F, j = idx % F;
@@ -209,8 +182,7 @@ __global__ __launch_bounds__(256) void swiglu(const float* __restrict__ part, in
         g += part[((size_t)s * M + m) * N + j];
         up += part[((size_t)s * M + m) * N + F + j];
     }
-    const float silu = g / (1.0f + expf(-g));
-    put_act(a, (size_t)M * F, idx, silu * up);
+    put_act(a, (size_t)M * F, idx, swiglu_value(g, up));
 }
 
 hipError_t launch_swiglu(int bf16, const float* part, int S, int M, int F, void* a, hipStream_t st) {

@@ -132,19 +132,21 @@ __device__ void head_epilogue(const float (*lg)[C + 1], int rows, int row0, int 
 // bfloat16 MFMA LM head: the GEMM core of the skinny kernel with the reductions as epilogue
 // ------------------------------------------------------------------------------------------------------
 // W is the packed (fragment-major) V x K matrix; z is an activation pair of bfloat16 planes (lo plane at
-// z + zplane): two MFMAs per weight fragment.
-template <int MT>
-__global__ __launch_bounds__(256) void lm_head_bf16(const bf16_t* __restrict__ z, size_t zplane, int M,
-                                                    const bf16_t* __restrict__ W, int V, int K,
-                                                    float* __restrict__ hpart, float* __restrict__ logits_dbg) {
+// z + zplane): two MFMAs per weight fragment.  NW waves split K.  Four waves per workgroup keep two
+// workgroups resident per CU, so one streams weights while the other runs its reduction epilogue (measured
+// on MI355X: eight waves per workgroup, one workgroup per CU, is ~20% slower end to end).
+template <int MT, int NW>
+__global__ __launch_bounds__(64 * NW) void lm_head_bf16(const bf16_t* __restrict__ z, size_t zplane, int M,
+                                                        const bf16_t* __restrict__ W, int V, int K,
+                                                        float* __restrict__ hpart, float* __restrict__ logits_dbg) {
     constexpr int NT = 4;
-    __shared__ f32x4 red[4][NT * MT][64];
+    __shared__ f32x4 red[NW][NT * MT][64];
     __shared__ float lg[16 * MT][65];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * 64;
     const int chunks = K / 256;
-    const int kb = (wave * chunks / 4) * 256, ke = ((wave + 1) * chunks / 4) * 256;
+    const int kb = (wave * chunks / NW) * 256, ke = ((wave + 1) * chunks / NW) * 256;
 
     const int KS = K / 32, tiles = (V + 15) / 16;
     const bf16_t* wt[NT];
@@ -200,12 +202,12 @@ __global__ __launch_bounds__(256) void lm_head_bf16(const bf16_t* __restrict__ z
             red[wave][nt * MT + mt][lane] = v;
         }
     __syncthreads();
-    for (int e = threadIdx.x; e < NT * MT * 64; e += 256) {
+    for (int e = threadIdx.x; e < NT * MT * 64; e += 64 * NW) {
         const int t = e >> 6, l = e & 63;
         const int nt = t / MT, mt = t % MT;
         f32x4 v = red[0][t][l];
 #pragma unroll
-        for (int q = 1; q < 4; ++q) {
+        for (int q = 1; q < NW; ++q) {
             const f32x4 u = red[q][t][l];
             v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
         }
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(256) void lm_head_bf16(const bf16_t* __restrict__ z
         lg[m][c + 3] = v[3];
     }
     __syncthreads();
-    head_epilogue<16 * MT, 64>(lg, M, 0, M, n0, V, blockIdx.x, hpart, logits_dbg);
+    if (threadIdx.x < 256) head_epilogue<16 * MT, 64>(lg, M, 0, M, n0, V, blockIdx.x, hpart, logits_dbg);
 }
 
 // ------------------------------------------------------------------------------------------------------
@@ -289,11 +291,11 @@ hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V
         hipLaunchKernelGGL(lm_head_f32, grid, dim3(256), 0, st, (const float*)z, M, (const float*)wlm, V, K, hpart,
                            logits_dbg);
     else if (M <= 16)
-        hipLaunchKernelGGL(lm_head_bf16<1>, grid, dim3(256), 0, st, (const bf16_t*)z, zplane, M, (const bf16_t*)wlm,
-                           V, K, hpart, logits_dbg);
+        hipLaunchKernelGGL((lm_head_bf16<1, 4>), grid, dim3(256), 0, st, (const bf16_t*)z, zplane, M,
+                           (const bf16_t*)wlm, V, K, hpart, logits_dbg);
     else
-        hipLaunchKernelGGL(lm_head_bf16<2>, grid, dim3(256), 0, st, (const bf16_t*)z, zplane, M, (const bf16_t*)wlm,
-                           V, K, hpart, logits_dbg);
+        hipLaunchKernelGGL((lm_head_bf16<2, 4>), grid, dim3(256), 0, st, (const bf16_t*)z, zplane, M,
+                           (const bf16_t*)wlm, V, K, hpart, logits_dbg);
     return hipGetLastError();
 }
 
