@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--cpu-sample-s", type=float, default=30.0, help="cap on CPU oracle work (seconds)")
     p.add_argument("--graph", type=int, default=1,
                    help="1: also time the step replayed as a captured HIP graph (reported beside the eager value)")
+    p.add_argument("--sweep-block", default=None,
+                   help="comma-separated block lengths: time the cycle and the drafter pass at each (one JSON "
+                        "line per length) instead of the default benchmark")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run the library's stream-copy kernel on 1 GiB (HBM-counter calibration)")
     return p.parse_args()
@@ -151,10 +154,74 @@ def cpu_baseline(wl, weights, n_new, cap_s):
                       f"{dt:.1f} s"}
 
 
+def sweep_block(args):
+    """Block-size sweep: the same drafter and context at several block lengths L.  Bytes per pass do not
+    depend on L (weights and cache dominate), so the pass time should stay flat while tokens per pass grow."""
+    import dataclasses
+    import torch
+    import workloads as W
+    from block_diffusion_drafter_forward_amd import session as S
+    base = W.by_name(args.workload)
+    weights = base.weights()
+    for L in [int(x) for x in args.sweep_block.split(",")]:
+        wl = dataclasses.replace(base, shape=dataclasses.replace(base.shape, block_len=L))
+        g = S.GpuWorkload(wl, weights=weights)
+        ctx = g.ctx.astype(np.int64)
+        n_new = min(N_NEW, L, int(ctx.min()))
+        full_ctx = g.ctx.copy()
+        g.ctx = (full_ctx - n_new).astype(np.int32)
+        g.prefill()
+        g.ctx = full_ctx
+        feats = [wl.features(r, n_new, row0=int(ctx[r]) - n_new) for r in range(wl.batch)]
+        feats_d = S.to_device(np.concatenate(feats, axis=0))
+        offs_d = S.to_device(np.arange(wl.batch + 1, dtype=np.int32) * n_new)
+        start_d = S.to_device((ctx - n_new).astype(np.int32))
+        inj_ws = g.model.inject_workspace(feats_d.shape[0])
+        stream = torch.cuda.current_stream()
+        g.model.inject(feats_d, offs_d, start_d, g.page_table, g.kv, inj_ws, stream=stream)
+        g.draft(stream=stream)
+        torch.cuda.synchronize()
+        bern, rand = wl.target_draws()
+        target = S.to_device(W.make_target(g.tokens.cpu().numpy(), bern, rand))
+
+        def step():
+            g.model.inject(feats_d, offs_d, start_d, g.page_table, g.kv, inj_ws, stream=stream)
+            g.draft(stream=stream)
+            g.accept(target, stream=stream)
+
+        def timed(fn):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps * 1e3
+
+        us_step = timed(step)
+        us_draft = timed(lambda: g.draft(stream=stream))
+        assert g.error_word() == 0, "device error word set"
+        print(json.dumps({"sweep": "block_len", "workload": wl.name, "block_len": L, "n_new_per_step": n_new,
+                          "draft_block_us": round(us_draft, 1), "us_per_step": round(us_step, 1),
+                          "block_positions_per_s": round(wl.batch * L * 1e6 / us_draft, 1),
+                          "steps": args.steps, "warmup": args.warmup}), flush=True)
+        g.model.close()
+        del g
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.sweep_block:
+        if args.gpus != 1:
+            sys.exit("bench.py runs on one GPU only")
+        sweep_block(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",

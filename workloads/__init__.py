@@ -317,6 +317,13 @@ SMALL = [
     # more than 32 block rows: tiled GEMMs and the tiled LM head (two row tiles, ragged)
     Workload(106, "small-bf16-serve9", SMALL_BF16, 9, None, (0, 400), True, None, (0.6, 0.95)),
     Workload(107, "small-gqa8-b3", SMALL_GQA8, 3, None, (1, 70), True, 0.7, None, top_k=5),
+    # the block-size sweep (L in {4, 8, 10}; 16 is the default above)
+    Workload(108, "small-bf16-l4-b2", dataclasses.replace(SMALL_BF16, block_len=4), 2, None, (1, 200), True, 0.8,
+             None, top_k=4),
+    Workload(109, "small-bf16-l8-b2", dataclasses.replace(SMALL_BF16, block_len=8), 2, None, (1, 200), True, 0.8,
+             None),
+    Workload(110, "small-bf16-l10-b3", dataclasses.replace(SMALL_BF16, block_len=10), 3, None, (1, 200), True,
+             None, (0.6, 0.95)),
 ]
 
 
