@@ -4,3 +4,4 @@ Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.
 package.  The HIP library and its Python binding never import it, and it imports nothing from them.
 """
 from .dflash_ref import *  # noqa: F401,F403
+from . import ddtree  # noqa: F401,E402
