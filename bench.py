@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--sweep-block", default=None,
                    help="comma-separated block lengths: time the cycle and the drafter pass at each (one JSON "
                         "line per length) instead of the default benchmark")
+    p.add_argument("--ddtree", default=None,
+                   help="comma-separated node budgets: time the DDTree chain (wide top-K of the drafter's marginals, "
+                        "tree construction, verifier walk) after a drafter pass, one JSON line per budget")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run the library's stream-copy kernel on 1 GiB (HBM-counter calibration)")
     return p.parse_args()
@@ -213,8 +216,94 @@ def sweep_block(args):
         torch.cuda.empty_cache()
 
 
+def ddtree_bench(args):
+    """DDTree on the drafter's marginals at the default workload: the drafter pass with its full-logits output,
+    the per-depth top-K (K = min(budget, V)), Algorithm 1 at the budget, and the greedy walk over synthetic
+    target choices (the target agrees with the tree's most probable child with probability 0.8)."""
+    import torch
+    import workloads as W
+    from block_diffusion_drafter_forward_amd import dflash as D
+    from block_diffusion_drafter_forward_amd import session as S
+    wl = W.by_name(args.workload)
+    s = wl.shape
+    g = S.GpuWorkload(wl)
+    g.prefill()
+    B, L, V = wl.batch, s.block_len, s.vocab
+    stream = torch.cuda.current_stream()
+    logits = torch.empty((B, L, V), dtype=torch.float32, device="cuda")
+    st = stream.cuda_stream
+
+    def timed(fn, n=args.steps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    us_draft = timed(lambda: g.draft(stream=stream))
+    us_draft_logits = timed(lambda: g.draft(logits=logits, stream=stream))
+    rng = np.random.default_rng(11)
+    for budget in [int(x) for x in args.ddtree.split(",")]:
+        K = min(budget, V, 1024)
+        ids = torch.empty((B, L, K), dtype=torch.int32, device="cuda")
+        lp = torch.empty((B, L, K), dtype=torch.float32, device="cuda")
+        tok = torch.empty((B, budget), dtype=torch.int32, device="cuda")
+        par, dep = torch.empty_like(tok), torch.empty_like(tok)
+        lq = torch.empty((B, budget), dtype=torch.float32, device="cuda")
+        n = torch.empty(B, dtype=torch.int32, device="cuda")
+        alen = torch.empty(B, dtype=torch.int32, device="cuda")
+        anodes = torch.empty((B, L - 1), dtype=torch.int32, device="cuda")
+        bonus = torch.empty(B, dtype=torch.int32, device="cuda")
+
+        def topk():
+            D.check(D.dflash_topk_logprobs(B * L, V, K, logits.data_ptr(), V, ids.data_ptr(), lp.data_ptr(), st), "topk")
+
+        def build():
+            D.check(D.dflash_ddtree_build(B, L - 1, K, lp.data_ptr() + 4 * K, ids.data_ptr() + 4 * K, L * K, budget,
+                                          tok.data_ptr(), par.data_ptr(), dep.data_ptr(), lq.data_ptr(), n.data_ptr(),
+                                          st), "build")
+
+        topk()
+        build()
+        torch.cuda.synchronize()
+        tk, pa, nn = tok.cpu().numpy(), par.cpu().numpy(), n.cpu().numpy()
+        tgt = rng.integers(0, V, size=(B, budget + 1)).astype(np.int32)
+        for b in range(B):
+            first = {}
+            for i in range(nn[b]):
+                first.setdefault(int(pa[b, i]), int(tk[b, i]))
+            for node, t in first.items():
+                if rng.random() < 0.8:
+                    tgt[b, node + 1] = t
+        tgt_d = S.to_device(tgt)
+
+        def walk():
+            D.check(D.dflash_ddtree_walk(B, budget, L - 1, tok.data_ptr(), par.data_ptr(), n.data_ptr(),
+                                         tgt_d.data_ptr(), alen.data_ptr(), anodes.data_ptr(), bonus.data_ptr(), st),
+                    "walk")
+
+        us_topk, us_build, us_walk = timed(topk), timed(build), timed(walk)
+        walk()
+        torch.cuda.synchronize()
+        print(json.dumps({"ddtree": wl.name, "budget": budget, "K": K, "depth": L - 1, "nodes": int(nn[0]),
+                          "draft_block_us": round(us_draft, 1), "draft_block_with_logits_us": round(us_draft_logits, 1),
+                          "topk_us": round(us_topk, 1), "build_us": round(us_build, 1), "walk_us": round(us_walk, 1),
+                          "accepted_nodes": int(alen.cpu()[0]),
+                          "topk_logits_gbs": round(B * L * V * 4 / (us_topk * 1e-6) / 1e9, 1)}), flush=True)
+
+
 def main():
     args = parse()
+    if args.ddtree:
+        if args.gpus != 1:
+            sys.exit("bench.py runs on one GPU only")
+        ddtree_bench(args)
+        return
     if args.copy_probe:
         copy_probe()
         return

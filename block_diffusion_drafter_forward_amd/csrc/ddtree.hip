@@ -1,0 +1,464 @@
+// DDTree on the drafter's marginals ("Accelerating Speculative Decoding with Block Diffusion Draft Trees",
+// §3.4.4 and §3.4.5): the per-position top-K log-probabilities (K up to 1024), the best-first construction
+// of the top-B prefix tree over rank tuples, and the greedy verifier walk over the target's choices.
+#include "common.h"
+#include "kernels.h"
+
+namespace df {
+
+// ------------------------------------------------------------------------------------------------------
+// wide top-K of one logits row: radix select of the K-th largest key, gather, bitonic sort
+// ------------------------------------------------------------------------------------------------------
+// One workgroup of 1024 threads per row.  Floats map to unsigned keys that order like the floats
+// (negative: all bits flipped; non-negative: sign bit set).  Three radix passes (11, 11 and 10 bits, the
+// first one over the row also accumulating an online max / sum of exponentials) find the key T of the K-th
+// largest value and how many entries equal to T belong to the top K; a gather takes every key above T and
+// the entries equal to T (all of them in the common case where they all fit, else the ones with the
+// smallest ids, found by a radix select on the ids of the tied entries).  When the keys at or above the
+// first pass's bin number at most TK_CAND (a few thousand for continuous logits), they are gathered into
+// LDS once and every later step runs there, so the row is read twice; otherwise every step re-reads the
+// row.  Rows are read with 16-byte loads, eight in flight per thread.  The K winners are sorted by (value descending, id ascending) with a bitonic
+// network in LDS; log-probabilities are value - logsumexp(row).
+#define TK_THREADS 1024
+#define TK_MAX 1024
+#define TK_BINS 2048
+#define TK_UNROLL 8
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Calls f(id, key) for every element of the row; 16-byte loads, TK_UNROLL of them in flight per thread.
+// Rows whose start is not 16-byte aligned or whose length is not a multiple of 4 take a scalar tail.
+template <typename F>
+__device__ __forceinline__ void tk_for_row(const float* __restrict__ x, int V, F&& f) {
+    const int t = threadIdx.x;
+    const bool vec = (((uintptr_t)x) & 15) == 0;
+    const int nv = vec ? V / 4 : 0;
+    const float4* x4 = (const float4*)x;
+    for (int i0 = 0; i0 < nv; i0 += TK_THREADS * TK_UNROLL) {
+        float4 v[TK_UNROLL];
+#pragma unroll
+        for (int u = 0; u < TK_UNROLL; ++u) {
+            const int i = i0 + u * TK_THREADS + t;
+            v[u] = i < nv ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < TK_UNROLL; ++u) {
+            const int i = i0 + u * TK_THREADS + t;
+            if (i < nv) {
+                f(4 * i + 0, order_key(v[u].x));
+                f(4 * i + 1, order_key(v[u].y));
+                f(4 * i + 2, order_key(v[u].z));
+                f(4 * i + 3, order_key(v[u].w));
+            }
+        }
+    }
+    for (int j = 4 * nv + t; j < V; j += TK_THREADS) f(j, order_key(x[j]));
+}
+
+__device__ __forceinline__ float tk_block_max(float v, float* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_max(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float t = -INFINITY;
+    for (int i = 0; i < TK_THREADS / 64; ++i) t = fmaxf(t, red[i]);
+    return t;
+}
+
+// Radix step over the histogram: the bin (from the top) that holds the krem-th largest, and the rank left
+// inside it.  Wave 0 scans TK_BINS bins from the top, 32 per lane, with a wave prefix sum.
+__device__ __forceinline__ void tk_pick_bin(const uint32_t* hist, int nbins, int krem, int* s_bin, int* s_krem) {
+    const int t = threadIdx.x;
+    if (t < 64) {
+        const int per = nbins / 64;
+        // lane 0 takes the top bins: lane l covers bins [nbins - (l + 1) per, nbins - l per)
+        int cnt = 0;
+        for (int q = 0; q < per; ++q) cnt += (int)hist[nbins - 1 - (t * per + q)];
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (t >= o) incl += y;
+        }
+        const int excl = incl - cnt;
+        if (excl < krem && incl >= krem) {
+            int cum = excl;
+            for (int q = 0; q < per; ++q) {
+                const int b = nbins - 1 - (t * per + q);
+                const int c = (int)hist[b];
+                if (cum + c >= krem) {
+                    *s_bin = b;
+                    *s_krem = krem - cum;
+                    break;
+                }
+                cum += c;
+            }
+        }
+    }
+}
+
+// The selection after the first radix pass: radix passes 2 and 3 (11 and 10 bits) among the keys with
+// the chosen top bits, the gather of every key above the K-th key T, and the entries equal to T (all, or
+// the smallest ids by a radix select on ids).  `each(f)` calls f(id, key) for every element of the source:
+// the row itself, or the candidates already gathered into LDS.  Leaves the K winners in skey / sid.
+template <typename Each>
+__device__ void tk_select(Each&& each, uint32_t prefix, uint32_t mask, int krem, int K, uint32_t* hist,
+                          float* red, uint32_t* skey, int* sid, int* s_bin, int* s_krem, int* s_slot) {
+    const int t = threadIdx.x;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = pass == 0 ? 10 : 0;
+        const int nb = pass == 0 ? 2048 : 1024;
+        for (int i = t; i < TK_BINS; i += TK_THREADS) hist[i] = 0u;
+        __syncthreads();
+        each([&](int, uint32_t k) {
+            if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1u);
+        });
+        __syncthreads();
+        tk_pick_bin(hist, nb, krem, s_bin, s_krem);
+        __syncthreads();
+        prefix |= (uint32_t)*s_bin << shift;
+        mask |= (uint32_t)(nb - 1) << shift;
+        krem = *s_krem;
+        __syncthreads();
+    }
+    const uint32_t T = prefix;  // key of the K-th largest entry; krem entries equal to T are in the top K
+    if (t == 0) *s_slot = 0;
+    __syncthreads();
+    int n_eq = 0;
+    each([&](int j, uint32_t k) {
+        if (k > T) {
+            const int slot = atomicAdd(s_slot, 1);
+            skey[slot] = k;
+            sid[slot] = j;
+        }
+        n_eq += k == T ? 1 : 0;
+    });
+    n_eq = (int)block_sum((float)n_eq, red);  // exact: counts stay far below 2^24
+    int id_cut = 0x7FFFFFFF;
+    if (n_eq > krem) {
+        uint32_t ipre = 0u, imask = 0u;
+        int irem = krem;
+        for (int shift = 22; shift >= 0; shift -= 11) {  // ids < 2^31: 9 + 11 + 11 bits, smallest first
+            const int nb = shift == 22 ? 512 : 2048;
+            for (int i = t; i < TK_BINS; i += TK_THREADS) hist[i] = 0u;
+            __syncthreads();
+            each([&](int j, uint32_t k) {
+                if (k == T && ((uint32_t)j & imask) == ipre)
+                    atomicAdd(&hist[nb - 1 - (((uint32_t)j >> shift) & (nb - 1))], 1u);
+            });
+            __syncthreads();
+            tk_pick_bin(hist, nb, irem, s_bin, s_krem);  // bins reversed: "largest" = smallest id digit
+            __syncthreads();
+            ipre |= (uint32_t)(nb - 1 - *s_bin) << shift;
+            imask |= (uint32_t)(nb - 1) << shift;
+            irem = *s_krem;
+            __syncthreads();
+        }
+        id_cut = (int)ipre;  // the krem-th smallest id among the tied entries
+    }
+    each([&](int j, uint32_t k) {
+        if (k == T && j <= id_cut) {
+            const int slot = atomicAdd(s_slot, 1);
+            skey[slot] = k;
+            sid[slot] = j;
+        }
+    });
+    __syncthreads();
+}
+
+#define TK_CAND 6144  // candidates kept in LDS after the first radix pass
+
+__global__ __launch_bounds__(TK_THREADS) void topk_rows(const float* __restrict__ logits, int64_t stride, int V,
+                                                         int K, int32_t* __restrict__ ids, float* __restrict__ lp) {
+    __shared__ uint32_t hist[TK_BINS];
+    __shared__ float red[TK_THREADS / 64];
+    __shared__ float red2[TK_THREADS / 64];
+    __shared__ uint32_t skey[TK_MAX];
+    __shared__ int sid[TK_MAX];
+    __shared__ uint32_t ckey[TK_CAND];
+    __shared__ int cid[TK_CAND];
+    __shared__ int s_bin, s_krem, s_slot, s_cnt;
+    const int t = threadIdx.x;
+    const float* x = logits + (size_t)blockIdx.x * stride;
+
+    // pass 1: online max / sum of exponentials, and the histogram of the top 11 key bits
+    for (int i = t; i < TK_BINS; i += TK_THREADS) hist[i] = 0u;
+    if (t == 0) s_cnt = 0;
+    __syncthreads();
+    float m = -INFINITY, se = 0.f;
+    tk_for_row(x, V, [&](int, uint32_t k) {
+        const float v = key_value(k);
+        if (v > m) {
+            se = se * expf(m - v) + 1.f;
+            m = v;
+        } else {
+            se += expf(v - m);
+        }
+        atomicAdd(&hist[k >> 21], 1u);
+    });
+    const float mx = tk_block_max(m, red);
+    se = m == -INFINITY ? 0.f : se * expf(m - mx);
+    se = block_sum(se, red2);
+    const float lse = mx + logf(se);
+    tk_pick_bin(hist, TK_BINS, K, &s_bin, &s_krem);
+    __syncthreads();
+    const uint32_t b1 = (uint32_t)s_bin;
+    const int krem = s_krem;
+    const int n_cand = (K - krem) + (int)hist[b1];  // keys in bin b1 or above
+    __syncthreads();
+    if (n_cand <= TK_CAND) {
+        // gather the candidates once; the rest of the selection runs on LDS
+        tk_for_row(x, V, [&](int j, uint32_t k) {
+            if ((k >> 21) >= b1) {
+                const int slot = atomicAdd(&s_cnt, 1);
+                ckey[slot] = k;
+                cid[slot] = j;
+            }
+        });
+        __syncthreads();
+        auto each = [&](auto&& f) {
+            for (int i = t; i < n_cand; i += TK_THREADS) f(cid[i], ckey[i]);
+        };
+        tk_select(each, b1 << 21, 0xFFE00000u, krem, K, hist, red, skey, sid, &s_bin, &s_krem, &s_slot);
+    } else {
+        auto each = [&](auto&& f) { tk_for_row(x, V, f); };
+        tk_select(each, b1 << 21, 0xFFE00000u, krem, K, hist, red, skey, sid, &s_bin, &s_krem, &s_slot);
+    }
+    // pad to a power of two and sort: better = larger key, then smaller id
+    int P = 1;
+    while (P < K) P <<= 1;
+    for (int i = K + t; i < P; i += TK_THREADS) {
+        skey[i] = 0u;
+        sid[i] = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = t; i < P; i += TK_THREADS) {
+                const int o = i ^ j;
+                if (o > i) {
+                    const uint32_t ki = skey[i], ko = skey[o];
+                    const int ii = sid[i], io = sid[o];
+                    const bool o_better = ko > ki || (ko == ki && io < ii);
+                    const bool first = (i & k) == 0;  // this pair's half runs best-first
+                    if (first == o_better) {
+                        skey[i] = ko;
+                        skey[o] = ki;
+                        sid[i] = io;
+                        sid[o] = ii;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = t; i < K; i += TK_THREADS) {
+        ids[(size_t)blockIdx.x * K + i] = sid[i];
+        lp[(size_t)blockIdx.x * K + i] = key_value(skey[i]) - lse;
+    }
+}
+
+hipError_t launch_topk_rows(int rows, const float* logits, int64_t stride, int V, int K, int32_t* ids, float* lp,
+                            hipStream_t st) {
+    hipLaunchKernelGGL(topk_rows, dim3(rows), dim3(TK_THREADS), 0, st, logits, stride, V, K, ids, lp);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------------
+// best-first tree construction (Algorithm 1), one wave per request
+// ------------------------------------------------------------------------------------------------------
+// The heap is a pool of candidate slots in LDS; slot i belongs to lane i % 64, and each lane caches the best
+// of its own live slots as one 64-bit key (order key of the score, then the inverted slot index, so that
+// equal scores pop in creation order).  A pop is a wave-wide max over the cached keys; the popped slot's
+// owner gets its new best from a wave-wide max over its remaining slots (one slot per lane).  The popped rank
+// tuple becomes node n; its next sibling (same parent, next rank; score = parent score + that rank's
+// log-probability) and its first child (rank 1 at the next depth; score = its own + that log-probability) are
+// appended as new slots.  The per-depth log-probabilities sit in LDS.
+#define DT_POOL 4096
+#define DT_MAXD 16
+
+__device__ __forceinline__ uint64_t dt_key(float s, int slot) {
+    return ((uint64_t)order_key(s) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)slot);
+}
+// Wave-wide max of a 64-bit key with DPP row operations (quad swaps, half-row and row mirrors, then the
+// row broadcasts of lanes 15 and 31), which leave the maximum in lane 63; it is then read into every lane.
+// All 64 lanes must be active.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dt_dpp_max(uint64_t k) {
+    const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+    const uint32_t ylo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t yhi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
+    const uint64_t y = ((uint64_t)yhi << 32) | ylo;
+    return y > k ? y : k;
+}
+__device__ __forceinline__ uint64_t dt_wave_max(uint64_t k) {
+    k = dt_dpp_max<0xB1, 0xF>(k);   // quad_perm [1, 0, 3, 2]
+    k = dt_dpp_max<0x4E, 0xF>(k);   // quad_perm [2, 3, 0, 1]
+    k = dt_dpp_max<0x141, 0xF>(k);  // row_half_mirror
+    k = dt_dpp_max<0x140, 0xF>(k);  // row_mirror
+    k = dt_dpp_max<0x142, 0xA>(k);  // row_bcast:15 into rows 1 and 3
+    k = dt_dpp_max<0x143, 0xC>(k);  // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 63), hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Slot record in LDS (16 bytes, one read per pop): the 64-bit key, the packed (parent + 1, depth, rank)
+// and the parent's score.
+struct DtSlot {
+    uint32_t key_lo, key_hi, meta, psig;
+};
+__device__ __forceinline__ uint32_t dt_meta(int parent, int depth, int rank) {
+    return ((uint32_t)(parent + 1) << 16) | ((uint32_t)depth << 11) | (uint32_t)rank;
+}
+
+__global__ __launch_bounds__(64) void ddtree_build(int D, int K, const float* __restrict__ lp,
+                                                   const int32_t* __restrict__ ids, int64_t req_stride, int budget,
+                                                   int32_t* __restrict__ node_token, int32_t* __restrict__ node_parent,
+                                                   int32_t* __restrict__ node_depth, float* __restrict__ node_logq,
+                                                   int32_t* __restrict__ n_nodes) {
+    __shared__ DtSlot slot[DT_POOL];                 // key 0: popped (or never written)
+    __shared__ uint2 nrec[DT_POOL / 2];              // popped nodes: (meta, score bits)
+    __shared__ float slq[DT_MAXD * TK_MAX];
+    const int r = blockIdx.x, lane = threadIdx.x;
+    const float* l = lp + (size_t)r * req_stride;
+    const int32_t* idr = ids + (size_t)r * req_stride;
+    // the log-probabilities into LDS, sixteen independent loads in flight per lane
+    for (int i0 = 0; i0 < D * K; i0 += 64 * 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int i = i0 + u * 64 + lane;
+            v[u] = i < D * K ? l[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int i = i0 + u * 64 + lane;
+            if (i < D * K) slq[(i / K) * TK_MAX + i % K] = v[u];
+        }
+    }
+    const float lqf = lane < D ? l[(size_t)lane * K] : 0.f;  // lane d: best log-prob at depth d + 1
+    if (lane == 0) {
+        const uint64_t k0 = dt_key(l[0], 0);
+        slot[0] = DtSlot{(uint32_t)k0, (uint32_t)(k0 >> 32), dt_meta(-1, 1, 0), __float_as_uint(0.f)};
+    }
+    __syncthreads();
+    uint64_t best = lane == 0 ? dt_key(slq[0], 0) : 0ull;  // 0: no live slot
+    int next = 1;
+    int n = 0;
+    for (; n < budget; ++n) {
+        const uint64_t top = dt_wave_max(best);
+        if (top == 0ull) break;  // every prefix of the rank space is already in the tree
+        const int sl = (int)(0xFFFFFFFFu - (uint32_t)top);
+        const DtSlot rec = slot[sl];
+        const float s = key_value((uint32_t)(top >> 32));
+        const int p = (int)(rec.meta >> 16) - 1, d = (rec.meta >> 11) & 31, k = rec.meta & 2047;
+        const float ps = __uint_as_float(rec.psig);
+        // independent LDS reads: the owner's other slots (one per lane) and the next sibling's log-prob
+        const int owner = sl & 63;
+        const int q = owner + 64 * lane;
+        const DtSlot c = q < next ? slot[q] : DtSlot{0u, 0u, 0u, 0u};
+        const float lq_sib = k + 1 < K ? slq[(d - 1) * TK_MAX + k + 1] : 0.f;
+        const float lq_child = __shfl(lqf, d < D ? d : 0, 64);
+        if (lane == 0) nrec[n] = make_uint2(rec.meta, __float_as_uint(s));
+        uint64_t cand = (q != sl) ? (((uint64_t)c.key_hi << 32) | c.key_lo) : 0ull;
+        cand = dt_wave_max(cand);
+        if (lane == owner) best = cand;
+        if (lane == 0) {
+            slot[sl].key_lo = 0u;
+            slot[sl].key_hi = 0u;
+        }
+        if (k + 1 < K) {  // next sibling: same parent, next rank
+            const float ss = ps + lq_sib;
+            if (lane == (next & 63)) {
+                const uint64_t kk = dt_key(ss, next);
+                slot[next] = DtSlot{(uint32_t)kk, (uint32_t)(kk >> 32), dt_meta(p, d, k + 1), rec.psig};
+                best = kk > best ? kk : best;
+            }
+            ++next;
+        }
+        if (d < D) {  // first child: best token at the next depth
+            const float cs = s + lq_child;
+            if (lane == (next & 63)) {
+                const uint64_t kk = dt_key(cs, next);
+                slot[next] = DtSlot{(uint32_t)kk, (uint32_t)(kk >> 32), dt_meta(n, d + 1, 0), __float_as_uint(s)};
+                best = kk > best ? kk : best;
+            }
+            ++next;
+        }
+        __syncthreads();  // this pop's LDS writes before the next pop reads them
+    }
+    int32_t* out_tok = node_token + (size_t)r * budget;
+    int32_t* out_par = node_parent + (size_t)r * budget;
+    int32_t* out_dep = node_depth + (size_t)r * budget;
+    float* out_lq = node_logq + (size_t)r * budget;
+    for (int i = lane; i < n; i += 64) {
+        const uint2 e = nrec[i];
+        const int di = (e.x >> 11) & 31, ki = e.x & 2047;
+        out_tok[i] = idr[(size_t)(di - 1) * K + ki];
+        out_par[i] = (int)(e.x >> 16) - 1;
+        out_dep[i] = di;
+        out_lq[i] = __uint_as_float(e.y);
+    }
+    if (lane == 0) n_nodes[r] = n;
+}
+
+hipError_t launch_ddtree_build(int batch, int D, int K, const float* lp, const int32_t* ids, int64_t req_stride,
+                               int budget, int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
+                               float* node_logq, int32_t* n_nodes, hipStream_t st) {
+    hipLaunchKernelGGL(ddtree_build, dim3(batch), dim3(64), 0, st, D, K, lp, ids, req_stride, budget, node_token,
+                       node_parent, node_depth, node_logq, n_nodes);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------------
+// greedy verifier walk, one wave per request
+// ------------------------------------------------------------------------------------------------------
+// From the root: the target's choice after the current prefix (target_next[0] after the root, [i + 1]
+// after node i) is looked up among the current node's children (a wave-wide scan of the parent links); the
+// walk moves there or stops, and the stopping choice is the next bonus token.
+__global__ __launch_bounds__(64) void ddtree_walk(int budget, int max_accept, const int32_t* __restrict__ node_token,
+                                                  const int32_t* __restrict__ node_parent,
+                                                  const int32_t* __restrict__ n_nodes,
+                                                  const int32_t* __restrict__ target_next,
+                                                  int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
+                                                  int32_t* __restrict__ bonus) {
+    const int r = blockIdx.x, lane = threadIdx.x;
+    const int n = min(n_nodes[r], budget);
+    const int32_t* tok = node_token + (size_t)r * budget;
+    const int32_t* par = node_parent + (size_t)r * budget;
+    const int32_t* tgt = target_next + (size_t)r * (budget + 1);
+    int cur = -1, len = 0, y = 0;
+    while (true) {
+        y = tgt[cur + 1];
+        int found = 0x7FFFFFFF;
+        for (int i = lane; i < n; i += 64)
+            if (par[i] == cur && tok[i] == y) found = min(found, i);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) found = min(found, __shfl_xor(found, o, 64));
+        if (found == 0x7FFFFFFF || len >= max_accept) break;
+        if (lane == 0) accept_nodes[(size_t)r * max_accept + len] = found;
+        ++len;
+        cur = found;
+    }
+    if (lane == 0) {
+        accept_len[r] = len;
+        bonus[r] = y;
+    }
+}
+
+hipError_t launch_ddtree_walk(int batch, int budget, int max_accept, const int32_t* node_token,
+                              const int32_t* node_parent, const int32_t* n_nodes, const int32_t* target_next,
+                              int32_t* accept_len, int32_t* accept_nodes, int32_t* bonus, hipStream_t st) {
+    hipLaunchKernelGGL(ddtree_walk, dim3(batch), dim3(64), 0, st, budget, max_accept, node_token, node_parent,
+                       n_nodes, target_next, accept_len, accept_nodes, bonus);
+    return hipGetLastError();
+}
+
+}  // namespace df

@@ -636,6 +636,52 @@ extern "C" int dflash_linear(int dtype, int M, int N, int K, const void* x, int6
     return DFLASH_OK;
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// DDTree: wide top-K, tree construction, verifier walk
+// ---------------------------------------------------------------------------------------------------------
+#define DDT_MAX_K 1024
+#define DDT_MAX_DEPTH 16
+#define DDT_MAX_BUDGET 2047
+
+extern "C" int dflash_topk_logprobs(int rows, int vocab, int k, const float* logits, int64_t row_stride,
+                                    int32_t* ids, float* logprobs, void* stream) {
+    if (rows < 1 || vocab < 1) return fail(DFLASH_E_ARG, "rows and vocab must be >= 1");
+    if (!logits || !ids || !logprobs) return fail(DFLASH_E_ARG, "a required pointer is NULL");
+    if (k < 1 || k > vocab) return fail(DFLASH_E_ARG, "k must be in [1, vocab]");
+    if (k > DDT_MAX_K) return fail(DFLASH_E_UNSUPPORTED, "k must be <= %d", DDT_MAX_K);
+    if (row_stride < vocab) return fail(DFLASH_E_ARG, "row_stride < vocab");
+    HIP_TRY(launch_topk_rows(rows, logits, row_stride, vocab, k, ids, logprobs, (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
+extern "C" int dflash_ddtree_build(int batch, int depth, int k, const float* logprobs, const int32_t* ids,
+                                   int64_t req_stride, int budget, int32_t* node_token, int32_t* node_parent,
+                                   int32_t* node_depth, float* node_logq, int32_t* n_nodes, void* stream) {
+    if (batch < 1) return fail(DFLASH_E_ARG, "batch must be >= 1");
+    if (!logprobs || !ids || !node_token || !node_parent || !node_depth || !node_logq || !n_nodes)
+        return fail(DFLASH_E_ARG, "a required pointer is NULL");
+    if (depth < 1 || k < 1 || budget < 1) return fail(DFLASH_E_ARG, "depth, k and budget must be >= 1");
+    if (depth > DDT_MAX_DEPTH || k > DDT_MAX_K || budget > DDT_MAX_BUDGET)
+        return fail(DFLASH_E_UNSUPPORTED, "depth <= %d, k <= %d and budget <= %d", DDT_MAX_DEPTH, DDT_MAX_K,
+                    DDT_MAX_BUDGET);
+    if (req_stride < (int64_t)depth * k) return fail(DFLASH_E_ARG, "req_stride < depth * k");
+    HIP_TRY(launch_ddtree_build(batch, depth, k, logprobs, ids, req_stride, budget, node_token, node_parent,
+                                node_depth, node_logq, n_nodes, (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
+extern "C" int dflash_ddtree_walk(int batch, int budget, int max_accept, const int32_t* node_token,
+                                  const int32_t* node_parent, const int32_t* n_nodes, const int32_t* target_next,
+                                  int32_t* accept_len, int32_t* accept_nodes, int32_t* bonus, void* stream) {
+    if (batch < 1 || budget < 1 || max_accept < 1) return fail(DFLASH_E_ARG, "batch, budget and max_accept must be >= 1");
+    if (budget > DDT_MAX_BUDGET) return fail(DFLASH_E_UNSUPPORTED, "budget must be <= %d", DDT_MAX_BUDGET);
+    if (!node_token || !node_parent || !n_nodes || !target_next || !accept_len || !accept_nodes || !bonus)
+        return fail(DFLASH_E_ARG, "a required pointer is NULL");
+    HIP_TRY(launch_ddtree_walk(batch, budget, max_accept, node_token, node_parent, n_nodes, target_next, accept_len,
+                               accept_nodes, bonus, (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
 extern "C" int dflash_copy(void* dst, const void* src, size_t n_bytes, void* stream) {
     if (!dst || !src) return fail(DFLASH_E_ARG, "a required pointer is NULL");
     if ((n_bytes & 15) || (((uintptr_t)dst | (uintptr_t)src) & 15))

@@ -80,6 +80,14 @@ _SIGS = {
     "dflash_accept_len": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     "dflash_last_error": (ctypes.c_char_p, []),
+    "dflash_topk_logprobs": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "dflash_ddtree_build": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "dflash_ddtree_walk": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]),
     "dflash_linear_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "dflash_linear": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -129,6 +137,22 @@ def dflash_create(cfg: dflash_config, w: dflash_weights) -> int:
 
 def dflash_destroy(h: int) -> None:
     lib().dflash_destroy(h)
+
+
+def dflash_topk_logprobs(rows, vocab, k, logits, row_stride, ids, logprobs, stream) -> int:
+    return lib().dflash_topk_logprobs(rows, vocab, k, logits, row_stride, ids, logprobs, stream)
+
+
+def dflash_ddtree_build(batch, depth, k, logprobs, ids, req_stride, budget, node_token, node_parent, node_depth,
+                        node_logq, n_nodes, stream) -> int:
+    return lib().dflash_ddtree_build(batch, depth, k, logprobs, ids, req_stride, budget, node_token, node_parent,
+                                     node_depth, node_logq, n_nodes, stream)
+
+
+def dflash_ddtree_walk(batch, budget, max_accept, node_token, node_parent, n_nodes, target_next, accept_len,
+                       accept_nodes, bonus, stream) -> int:
+    return lib().dflash_ddtree_walk(batch, budget, max_accept, node_token, node_parent, n_nodes, target_next,
+                                    accept_len, accept_nodes, bonus, stream)
 
 
 def dflash_packed_weight_bytes(h: int) -> int:

@@ -115,7 +115,7 @@ typedef struct {
 
 /* Optional test taps (device pointers, float32; NULL = off).                                              */
 typedef struct {
-    float *logits;  /* [batch][L][V] full logits                                                           */
+    float *logits;  /* [batch][L][V] full logits (tests; the input of the DDTree wide top-K below)         */
     float *hidden;  /* [n_layers + 1][batch * L][H] residual stream after the embedding and each layer       */
 } dflash_debug;
 
@@ -185,6 +185,37 @@ int dflash_draft_block(dflash_handle *h, int batch, const int32_t *block_tokens,
  * All arrays are device int32.  No workspace is used.                                                     */
 int dflash_accept_len(int batch, int n_draft, const int32_t *draft, int64_t draft_stride, const int32_t *target,
                       int64_t target_stride, int32_t *tau, void *stream);
+
+/* ---- DDTree on the drafter's marginals ("Accelerating Speculative Decoding with Block Diffusion Draft
+ * Trees", §3.4.4 Lemma 1 and Algorithm 1, §3.4.5 the verifier walk) --------------------------------------
+ * The drafter's full logits come from dflash_draft_block's dbg->logits output ([batch][L][V]); block row d
+ * (1 .. L-1) is the distribution of draft depth d.                                                        */
+
+/* The k best tokens of each of `rows` logit rows (device float, row stride row_stride >= vocab), ordered by
+ * (logit descending, id ascending), and their log-probabilities logit - logsumexp(row).  Outputs are device
+ * [rows][k] int32 ids and float log-probs.  1 <= k <= min(vocab, 1024).  No workspace.                    */
+int dflash_topk_logprobs(int rows, int vocab, int k, const float *logits, int64_t row_stride, int32_t *ids,
+                         float *logprobs, void *stream);
+
+/* Algorithm 1 per request: the `budget` most probable prefixes under the factorised distribution, popped
+ * best-first from a heap of rank tuples (next sibling and first child pushed per pop; equal scores pop in
+ * creation order).  Input: depth d (0-based, d < depth) of request r has its k sorted log-probs and ids at
+ * logprobs / ids + r * req_stride + d * k (device).  Output, device [batch][budget], node i = the i-th pop:
+ * node_token (token id), node_parent (node index of its prefix, -1 = the root / bonus token), node_depth
+ * (1-based), node_logq (log-probability score, float32 sums: parent's score + own log-prob); n_nodes[b] =
+ * nodes written (min(budget, prefixes available)).  depth <= 16, k <= 1024, budget <= 2047.              */
+int dflash_ddtree_build(int batch, int depth, int k, const float *logprobs, const int32_t *ids, int64_t req_stride,
+                        int budget, int32_t *node_token, int32_t *node_parent, int32_t *node_depth,
+                        float *node_logq, int32_t *n_nodes, void *stream);
+
+/* Greedy verifier walk per request over a tree from dflash_ddtree_build: target_next[b][0] is the target's
+ * choice after the root and target_next[b][i + 1] its choice after node i (device [batch][budget + 1]).
+ * From the root, move to the child holding the target's choice while there is one.  Outputs (device):
+ * accept_len[b] = nodes accepted (<= max_accept), accept_nodes[b][0 .. accept_len) their indices,
+ * bonus[b] = the target's choice where the walk stopped.  budget <= 2047.                                 */
+int dflash_ddtree_walk(int batch, int budget, int max_accept, const int32_t *node_token, const int32_t *node_parent,
+                       const int32_t *n_nodes, const int32_t *target_next, int32_t *accept_len,
+                       int32_t *accept_nodes, int32_t *bonus, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none).                                */
 const char *dflash_last_error(void);

@@ -227,3 +227,40 @@ def test_unpacked_bf16_handle_refuses_to_run(D):
         assert rc == D.DFLASH_E_ARG and "packed" in D.dflash_last_error()
     finally:
         m.close()
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(rows=0), -1), (dict(k=0), -1), (dict(k=6000), -1), (dict(k=1025, vocab=4096), -4),
+    (dict(row_stride=10), -1), (dict(logits=None), -1),
+])
+def test_topk_logprobs_validation(D, args, code):
+    a = dict(rows=2, vocab=5003, k=8, logits=0x1000, row_stride=5003, ids=0x2000, lp=0x3000)
+    a.update(args)
+    assert D.dflash_topk_logprobs(a["rows"], a["vocab"], a["k"], a["logits"], a["row_stride"], a["ids"], a["lp"],
+                                  None) == code
+    assert D.dflash_last_error()
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(batch=0), -1), (dict(depth=0), -1), (dict(depth=17), -4), (dict(k=1025), -4),
+    (dict(budget=2048), -4), (dict(budget=0), -1), (dict(req_stride=7), -1), (dict(n_nodes=None), -1),
+])
+def test_ddtree_build_validation(D, args, code):
+    a = dict(batch=1, depth=15, k=64, lp=0x1000, ids=0x2000, req_stride=15 * 64, budget=256, tok=0x3000,
+             par=0x4000, dep=0x5000, lq=0x6000, n_nodes=0x7000)
+    a.update(args)
+    assert D.dflash_ddtree_build(a["batch"], a["depth"], a["k"], a["lp"], a["ids"], a["req_stride"], a["budget"],
+                                 a["tok"], a["par"], a["dep"], a["lq"], a["n_nodes"], None) == code
+    assert D.dflash_last_error()
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(batch=0), -1), (dict(budget=2048), -4), (dict(max_accept=0), -1), (dict(target=None), -1),
+])
+def test_ddtree_walk_validation(D, args, code):
+    a = dict(batch=1, budget=256, max_accept=15, tok=0x1000, par=0x2000, n=0x3000, target=0x4000, alen=0x5000,
+             anodes=0x6000, bonus=0x7000)
+    a.update(args)
+    assert D.dflash_ddtree_walk(a["batch"], a["budget"], a["max_accept"], a["tok"], a["par"], a["n"], a["target"],
+                                a["alen"], a["anodes"], a["bonus"], None) == code
+    assert D.dflash_last_error()

@@ -1,0 +1,153 @@
+"""DDTree kernels against the oracle ([DDT] = "Accelerating Speculative Decoding with Block Diffusion Draft
+Trees"): the wide top-K (ids exact, log-probs to float32 rounding, ties by id), the best-first tree (node for
+node, with the oracle's tree decisions taken in float32 like the kernel's), the verifier walk (exact), and the
+whole chain on a drafter pass."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from oracle import ddtree as T
+
+pytestmark = pytest.mark.gpu
+
+
+def _mods():
+    import torch
+    assert torch.cuda.is_available()
+    from block_diffusion_drafter_forward_amd import dflash as D, session as S
+    return torch, D, S
+
+
+def _topk_gpu(torch, D, lg, k):
+    rows, V = lg.shape
+    x = torch.from_numpy(np.ascontiguousarray(lg.astype(np.float32))).cuda()
+    ids = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    lp = torch.empty((rows, k), dtype=torch.float32, device="cuda")
+    D.check(D.dflash_topk_logprobs(rows, V, k, x.data_ptr(), V, ids.data_ptr(), lp.data_ptr(), D._stream()), "topk")
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), lp.cpu().numpy()
+
+
+@pytest.mark.parametrize("k", [1, 8, 100, 1000, 1024])
+def test_topk_logprobs_matches_oracle(k):
+    torch, D, S = _mods()
+    rng = np.random.default_rng(500 + k)
+    V = 5003
+    lg = rng.normal(0.0, 2.0, size=(6, V)).astype(np.float32)
+    lg[1] = np.round(lg[1] * 2) / 2          # heavy ties: half-integer levels
+    lg[2] = 0.5                              # every logit equal
+    lg[3, rng.choice(V, 40, replace=False)] = lg[3].max() + 1.0  # a 40-way tie at the top
+    lg[4] = -lg[4]                           # negative keys dominate the order
+    ids, lp = _topk_gpu(torch, D, lg, k)
+    want_ids, want_lp = T.topk_logprobs(lg.astype(np.float64), k)
+    np.testing.assert_array_equal(ids, want_ids)
+    assert np.all(np.abs(lp - want_lp) <= 2e-5 + 2e-6 * np.abs(want_lp))
+
+
+def _sorted_logprobs(rng, batch, depth, K, V=3000):
+    lg = rng.normal(0.0, 2.5, size=(batch * depth, V))
+    ids, lp = T.topk_logprobs(lg, K)
+    return ids.reshape(batch, depth, K).astype(np.int32), lp.reshape(batch, depth, K).astype(np.float32)
+
+
+def _build_gpu(torch, D, ids, lp, budget):
+    batch, depth, K = lp.shape
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    lpd, idd = dev(lp), dev(ids)
+    tok = torch.empty((batch, budget), dtype=torch.int32, device="cuda")
+    par = torch.empty_like(tok)
+    dep = torch.empty_like(tok)
+    lq = torch.empty((batch, budget), dtype=torch.float32, device="cuda")
+    n = torch.empty(batch, dtype=torch.int32, device="cuda")
+    D.check(D.dflash_ddtree_build(batch, depth, K, lpd.data_ptr(), idd.data_ptr(), depth * K, budget, tok.data_ptr(),
+                                  par.data_ptr(), dep.data_ptr(), lq.data_ptr(), n.data_ptr(), D._stream()), "build")
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), par.cpu().numpy(), dep.cpu().numpy(), lq.cpu().numpy(), n.cpu().numpy()
+
+
+@pytest.mark.parametrize("depth,K,budget", [(15, 64, 1), (15, 64, 16), (15, 256, 256), (15, 1024, 1000),
+                                            (6, 512, 2047), (3, 3, 100), (1, 50, 64), (16, 8, 512)])
+def test_ddtree_build_matches_oracle(depth, K, budget):
+    torch, D, S = _mods()
+    rng = np.random.default_rng(600 + depth * 7 + K + budget)
+    batch = 3
+    ids, lp = _sorted_logprobs(rng, batch, depth, K)
+    tok, par, dep, lq, n = _build_gpu(torch, D, ids, lp, budget)
+    for b in range(batch):
+        nodes = T.build_tree(lp[b], budget, dtype=np.float32)
+        assert n[b] == len(nodes) == min(budget, sum(K ** d for d in range(1, depth + 1)))
+        np.testing.assert_array_equal(tok[b, :n[b]], T.tree_tokens(nodes, ids[b]))
+        np.testing.assert_array_equal(par[b, :n[b]], [p for _, _, p in nodes])
+        np.testing.assert_array_equal(dep[b, :n[b]], [len(r) for r, _, _ in nodes])
+        np.testing.assert_array_equal(lq[b, :n[b]].view(np.uint32), np.array([s for _, s, _ in nodes], np.float32).view(np.uint32))
+        # pops non-increasing, prefix-closed
+        assert np.all(np.diff(lq[b, :n[b]]) <= 0)
+        assert np.all(par[b, :n[b]] < np.arange(n[b]))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_ddtree_walk_matches_oracle(seed):
+    torch, D, S = _mods()
+    rng = np.random.default_rng(700 + seed)
+    batch, depth, K, budget = 4, 12, 32, 300
+    ids, lp = _sorted_logprobs(rng, batch, depth, K)
+    tok, par, dep, lq, n = _build_gpu(torch, D, ids, lp, budget)
+    # target choices: follow the tree's first child with probability 0.8, else a token outside the tree
+    tgt = rng.integers(0, 3000, size=(batch, budget + 1)).astype(np.int32)
+    for b in range(batch):
+        first_child = {}
+        for i in range(n[b]):
+            first_child.setdefault(int(par[b, i]), int(tok[b, i]))
+        for node in range(-1, n[b]):
+            if node in first_child and rng.random() < 0.8:
+                tgt[b, node + 1] = first_child[node]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    alen = torch.empty(batch, dtype=torch.int32, device="cuda")
+    anodes = torch.full((batch, depth), -1, dtype=torch.int32, device="cuda")
+    bonus = torch.empty(batch, dtype=torch.int32, device="cuda")
+    keep = [dev(a) for a in (tok, par, n, tgt)]  # held until the kernel has run
+    D.check(D.dflash_ddtree_walk(batch, budget, depth, keep[0].data_ptr(), keep[1].data_ptr(), keep[2].data_ptr(),
+                                 keep[3].data_ptr(), alen.data_ptr(), anodes.data_ptr(), bonus.data_ptr(),
+                                 D._stream()), "walk")
+    torch.cuda.synchronize()
+    alen, anodes, bonus = alen.cpu().numpy(), anodes.cpu().numpy(), bonus.cpu().numpy()
+    for b in range(batch):
+        path, y = T.verify_walk(tok[b, :n[b]].tolist(), par[b, :n[b]].tolist(), tgt[b])
+        assert alen[b] == len(path) and list(anodes[b, :alen[b]]) == path and bonus[b] == y
+
+
+def test_ddtree_chain_on_a_drafter_pass():
+    """Drafter pass -> full logits -> per-depth top-K -> tree, checked against the oracle on the same logits."""
+    torch, D, S = _mods()
+    wl = W.by_name("small-bf16-paged-b2")
+    s = wl.shape
+    g = S.GpuWorkload(wl)
+    g.prefill()
+    B, L, V = wl.batch, s.block_len, s.vocab
+    logits = torch.zeros((B, L, V), dtype=torch.float32, device="cuda")
+    g.draft(logits=logits)
+    torch.cuda.synchronize()
+    budget = 128
+    K = min(budget, V)
+    ids = torch.empty((B, L, K), dtype=torch.int32, device="cuda")
+    lp = torch.empty((B, L, K), dtype=torch.float32, device="cuda")
+    D.check(D.dflash_topk_logprobs(B * L, V, K, logits.data_ptr(), V, ids.data_ptr(), lp.data_ptr(), D._stream()),
+            "topk")
+    tok = torch.empty((B, budget), dtype=torch.int32, device="cuda")
+    par, dep = torch.empty_like(tok), torch.empty_like(tok)
+    lq = torch.empty((B, budget), dtype=torch.float32, device="cuda")
+    n = torch.empty(B, dtype=torch.int32, device="cuda")
+    # depth d reads block row d (rows 1 .. L-1): start one row in, request stride L * K
+    D.check(D.dflash_ddtree_build(B, L - 1, K, lp.data_ptr() + 4 * K, ids.data_ptr() + 4 * K, L * K, budget,
+                                  tok.data_ptr(), par.data_ptr(), dep.data_ptr(), lq.data_ptr(), n.data_ptr(),
+                                  D._stream()), "build")
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        want_ids, want_lp = T.topk_logprobs(lg[b], K)
+        np.testing.assert_array_equal(ids[b].cpu().numpy(), want_ids)
+        nodes = T.build_tree(lp[b, 1:].cpu().numpy(), budget, dtype=np.float32)
+        assert n[b].item() == len(nodes)
+        np.testing.assert_array_equal(tok[b, :len(nodes)].cpu().numpy(), T.tree_tokens(nodes, want_ids[1:]))
+        np.testing.assert_array_equal(par[b, :len(nodes)].cpu().numpy(), [p for _, _, p in nodes])
