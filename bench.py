@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--ddtree", default=None,
                    help="comma-separated node budgets: time the DDTree chain (wide top-K of the drafter's marginals, "
                         "tree construction, verifier walk) after a drafter pass, one JSON line per budget")
+    p.add_argument("--sample", action="store_true",
+                   help="temperature 1: time the sampled drafter pass and the rejection-sampling verifier")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run the library's stream-copy kernel on 1 GiB (HBM-counter calibration)")
     return p.parse_args()
@@ -297,8 +299,85 @@ def ddtree_bench(args):
                           "topk_logits_gbs": round(B * L * V * 4 / (us_topk * 1e-6) / 1e9, 1)}), flush=True)
 
 
+def sample_bench(args):
+    """Temperature 1 at the default workload: the drafter pass with Gumbel-max sampling (with and without its
+    full-logits output, which the verifier reads), beside the greedy pass, and the modified rejection-sampling
+    verifier over the drafts against synthetic target logits (each draft's drafter row plus N(0, 0.5^2)
+    noise, so that drafts are kept at a realistic rate)."""
+    import torch
+    import workloads as W
+    from block_diffusion_drafter_forward_amd import dflash as D
+    from block_diffusion_drafter_forward_amd import session as S
+    wl = W.by_name(args.workload)
+    s = wl.shape
+    g = S.GpuWorkload(wl)
+    g.prefill()
+    B, L, V = wl.batch, s.block_len, s.vocab
+    n = L - 1
+    stream = torch.cuda.current_stream()
+    logits = torch.empty((B, L, V), dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps=args.steps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    seed = [0x5EED]
+
+    def draft_sample(with_logits):
+        seed[0] += 1
+        g.draft_sample(seed[0], logits=logits if with_logits else None, stream=stream)
+
+    us_greedy = timed(lambda: g.draft(stream=stream))
+    us_sample = timed(lambda: draft_sample(False))
+    us_sample_logits = timed(lambda: draft_sample(True))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    # target row j pairs with draft j, i.e. drafter row j + 1; the last (bonus) row reuses drafter row 0
+    p = (torch.cat([logits[:, 1:], logits[:, :1]], dim=1)
+         + 0.5 * torch.randn((B, L, V), generator=gen, device="cuda")).contiguous()
+    drafts = g.tokens[:, 1:]
+    q = logits[:, 1:]
+    tau = torch.empty(B, dtype=torch.int32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(D.verify_sample_workspace_bytes(B, n, V), dtype=torch.uint8, device="cuda")
+    assert ws.data_ptr() % 256 == 0
+
+    def verify():
+        seed[0] += 1
+        D.verify_sample(drafts, q, p, seed[0], tau, nxt, ws, stream=stream)
+
+    us_verify = timed(verify)
+    taus = []
+    for _ in range(20):
+        draft_sample(True)
+        verify()
+        taus.append(tau.cpu().numpy().copy())
+    us_cycle = timed(lambda: (draft_sample(True), verify()))
+    verify_bytes = B * (2 * n + 1) * V * 4 + B * 2 * V * 4
+    print(json.dumps({"sample": wl.name, "batch": B, "block_len": L, "vocab": V,
+                      "draft_greedy_us": round(us_greedy, 1), "draft_sample_us": round(us_sample, 1),
+                      "draft_sample_with_logits_us": round(us_sample_logits, 1),
+                      "verify_sample_us": round(us_verify, 1),
+                      "verify_algorithmic_bytes": verify_bytes,
+                      "verify_gbs": round(verify_bytes / (us_verify * 1e-6) / 1e9, 1),
+                      "cycle_us": round(us_cycle, 1), "mean_tau": round(float(np.mean(taus)), 2)}), flush=True)
+
+
 def main():
     args = parse()
+    if args.sample:
+        if args.gpus != 1:
+            sys.exit("bench.py runs on one GPU; --gpus must be 1")
+        sample_bench(args)
+        return
     if args.ddtree:
         if args.gpus != 1:
             sys.exit("bench.py runs on one GPU only")

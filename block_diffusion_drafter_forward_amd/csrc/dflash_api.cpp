@@ -388,10 +388,12 @@ static hipError_t project(const dflash_handle* h, const GemmPlan& p, const void*
     return launch_gemm_f32((const float*)x, ldx, M, rows, N, K, part, st);
 }
 
-extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* block_tokens, const int32_t* ctx_len,
-                                  const int32_t* page_table, int max_pages, const dflash_kv* kv, int max_ctx,
-                                  int top_k, int32_t* tokens, int32_t* topk_ids, float* topk_logprobs,
-                                  const dflash_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
+// The drafter pass; sample != 0 draws each row's token at temperature 1 (Gumbel-max, keyed by seed) instead
+// of taking the argmax, and logits_out (nullable) receives the full logits.
+static int draft_impl(dflash_handle* h, int batch, const int32_t* block_tokens, const int32_t* ctx_len,
+                      const int32_t* page_table, int max_pages, const dflash_kv* kv, int max_ctx, int top_k,
+                      int sample, uint64_t seed, int32_t* tokens, int32_t* topk_ids, float* topk_logprobs,
+                      float* logits_out, const dflash_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
     if (!h) return fail(DFLASH_E_ARG, "handle is NULL");
     const dflash_config& c = h->cfg;
     if (batch < 1) return fail(DFLASH_E_ARG, "batch must be >= 1");
@@ -506,13 +508,31 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
     {
         Timed t(h, bf ? "lm_head_bf16" : "lm_head_f32", st);
         const void* wlm = bf ? (const void*)(h->packed + h->pl.lm) : h->w.lm_head;
-        HIP_TRY(launch_lm_head(bf, u, M, wlm, c.vocab, H, hpart, dbg ? dbg->logits : nullptr, st));
+        HIP_TRY(launch_lm_head(bf, u, M, wlm, c.vocab, H, hpart, logits_out, sample, seed, st));
     }
     {
         Timed t(h, "head_merge", st);
-        HIP_TRY(launch_head_merge(bf, M, c.vocab, top_k, hpart, block_tokens, tokens, topk_ids, topk_logprobs, err, st));
+        HIP_TRY(launch_head_merge(bf, M, c.vocab, top_k, sample, hpart, block_tokens, tokens, topk_ids,
+                                  topk_logprobs, err, st));
     }
     return DFLASH_OK;
+}
+
+extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* block_tokens, const int32_t* ctx_len,
+                                  const int32_t* page_table, int max_pages, const dflash_kv* kv, int max_ctx,
+                                  int top_k, int32_t* tokens, int32_t* topk_ids, float* topk_logprobs,
+                                  const dflash_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
+    return draft_impl(h, batch, block_tokens, ctx_len, page_table, max_pages, kv, max_ctx, top_k, 0, 0, tokens,
+                      topk_ids, topk_logprobs, dbg ? dbg->logits : nullptr, dbg, ws, ws_bytes, stream);
+}
+
+extern "C" int dflash_draft_block_sample(dflash_handle* h, int batch, const int32_t* block_tokens,
+                                         const int32_t* ctx_len, const int32_t* page_table, int max_pages,
+                                         const dflash_kv* kv, int max_ctx, int top_k, uint64_t seed, int32_t* tokens,
+                                         int32_t* topk_ids, float* topk_logprobs, float* logits, void* ws,
+                                         size_t ws_bytes, void* stream) {
+    return draft_impl(h, batch, block_tokens, ctx_len, page_table, max_pages, kv, max_ctx, top_k, 1, seed, tokens,
+                      topk_ids, topk_logprobs, logits, nullptr, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -597,6 +617,33 @@ extern "C" int dflash_accept_len(int batch, int n_draft, const int32_t* draft, i
     if (!draft || !target || !tau) return fail(DFLASH_E_ARG, "a required pointer is NULL");
     if (draft_stride < n_draft || target_stride < n_draft) return fail(DFLASH_E_ARG, "stride smaller than n_draft");
     HIP_TRY(launch_accept(batch, n_draft, draft, draft_stride, target, target_stride, tau, (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
+#define VERIFY_MAX_DRAFT 63  // one lane per draft position in the acceptance tests
+
+extern "C" size_t dflash_verify_sample_workspace_bytes(int batch, int n_draft, int vocab) {
+    if (batch < 1 || n_draft < 0 || n_draft > VERIFY_MAX_DRAFT || vocab < 1) return 0;
+    return sv_workspace_bytes(batch, n_draft, vocab);
+}
+
+extern "C" int dflash_verify_sample(int batch, int n_draft, int vocab, const int32_t* draft, int64_t draft_stride,
+                                    const float* q_logits, int64_t q_req_stride, const float* p_logits,
+                                    int64_t p_req_stride, uint64_t seed, int32_t* tau, int32_t* next_token, void* ws,
+                                    size_t ws_bytes, void* stream) {
+    if (batch < 1 || batch > 65535) return fail(DFLASH_E_ARG, "batch must be in [1, 65535]");
+    if (n_draft < 0 || n_draft > VERIFY_MAX_DRAFT) return fail(DFLASH_E_UNSUPPORTED, "n_draft must be in [0, 63]");
+    if (vocab < 1) return fail(DFLASH_E_ARG, "vocab must be >= 1");
+    if (!p_logits || !tau || !next_token || !ws) return fail(DFLASH_E_ARG, "a required pointer is NULL");
+    if (n_draft > 0 && (!draft || !q_logits)) return fail(DFLASH_E_ARG, "drafts or drafter logits are NULL");
+    if (draft_stride < n_draft) return fail(DFLASH_E_ARG, "draft_stride < n_draft");
+    if (p_req_stride < (int64_t)(n_draft + 1) * vocab) return fail(DFLASH_E_ARG, "p_req_stride < (n_draft + 1) * vocab");
+    if (n_draft > 0 && q_req_stride < (int64_t)n_draft * vocab) return fail(DFLASH_E_ARG, "q_req_stride < n_draft * vocab");
+    const size_t need = sv_workspace_bytes(batch, n_draft, vocab);
+    if (ws_bytes < need) return fail(DFLASH_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (((uintptr_t)ws) & 255) return fail(DFLASH_E_ARG, "workspace must be 256-byte aligned");
+    HIP_TRY(launch_verify_sample(batch, n_draft, vocab, draft, draft_stride, q_logits, q_req_stride, p_logits,
+                                 p_req_stride, seed, tau, next_token, ws, (hipStream_t)stream));
     return DFLASH_OK;
 }
 

@@ -1,15 +1,17 @@
 // Shared LM head fused with the per-row reductions the drafter needs: max, sum of exponentials (for the
-// log-sum-exp over the full vocabulary) and the top-8 (logit, id) list, ordered by logit then id.  Logits
-// live only in registers and LDS.  Stage 1 (lm_head): one workgroup per 64 vocabulary rows, four waves
+// log-sum-exp over the full vocabulary) and the top-8 (logit, id) list, ordered by logit then id; at
+// temperature 1 also the row's Gumbel-max sample (best logit + Gumbel noise, drawn per logit from a
+// counter-based generator).  Logits live only in registers and LDS.  Stage 1 (lm_head): one workgroup per 64 vocabulary rows, four waves
 // splitting K, writes one (max, sumexp, top-8) record per block row.  Stage 2 (head_merge): one workgroup
 // per block row combines the records and emits the greedy token, the top-k ids and their log-probabilities.
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
+#include "philox.h"
 
 namespace df {
 
-#define HEAD_REC 18  // max, sumexp, 8 values, 8 ids (as int bits)
+#define HEAD_REC 20  // max, sumexp, 8 values, 8 ids (as int bits), sampled score and id (temperature 1 only)
 // Records are stored field-major per block row, hpart[(row * HEAD_REC + field) * groups + group], so that the
 // merge reads each field of consecutive groups with coalesced loads.
 
@@ -86,7 +88,7 @@ struct Top8 {
 // The first thread of the row writes the record of (group, row).
 template <int R, int C>
 __device__ void head_epilogue(const float (*lg)[C + 1], int rows, int row0, int Mtot, int n0, int V, int group,
-                              float* __restrict__ hpart, float* __restrict__ logits_dbg) {
+                              float* __restrict__ hpart, float* __restrict__ logits_dbg, RngKey key, int sample) {
     constexpr int TPR = 256 / R, CPT = C / TPR;
     static_assert(TPR <= DF_WAVE && (TPR & (TPR - 1)) == 0, "a row's threads must share a wave");
     const int t = threadIdx.x;
@@ -115,6 +117,35 @@ __device__ void head_epilogue(const float (*lg)[C + 1], int rows, int row0, int 
         se += __shfl_xor(se, o, DF_WAVE);
         s.merge_lane_xor(o);
     }
+    // Temperature 1: the row's Gumbel-max candidate over these columns.  A thread's columns start at a
+    // multiple of 4, so each generator block serves four consecutive logits.
+    float bs = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    if (sample) {
+        for (int c = 0; c < ncol; c += 4) {
+            const int j0 = n0 + c0 + c;
+            uint32_t w[4];
+            philox_block(key, (uint32_t)j0 >> 2, (uint32_t)(row0 + m), RNG_TAG_DRAFT, w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c + e < ncol) {
+                    const float sc = lg[m][c0 + c + e] + rng_gumbel(w[e]);
+                    if (sc > bs) {  // columns ascend: a tie keeps the smaller id
+                        bs = sc;
+                        bi = j0 + e;
+                    }
+                }
+        }
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) {
+            const float os = __shfl_xor(bs, o, DF_WAVE);
+            const int oi = __shfl_xor(bi, o, DF_WAVE);
+            if (df_better(os, oi, bs, bi)) {
+                bs = os;
+                bi = oi;
+            }
+        }
+    }
     if (live && piece == 0) {
         const size_t G = gridDim.x;  // record groups
         float* dst = hpart + (size_t)(row0 + m) * HEAD_REC * G + group;
@@ -124,6 +155,10 @@ __device__ void head_epilogue(const float (*lg)[C + 1], int rows, int row0, int 
         for (int j = 0; j < DF_TOPK; ++j) {
             dst[(2 + j) * G] = s.v[j];
             dst[(2 + DF_TOPK + j) * G] = __int_as_float(s.id[j]);
+        }
+        if (sample) {
+            dst[(2 + 2 * DF_TOPK) * G] = bs;
+            dst[(3 + 2 * DF_TOPK) * G] = __int_as_float(bi);
         }
     }
 }
@@ -138,7 +173,8 @@ __device__ void head_epilogue(const float (*lg)[C + 1], int rows, int row0, int 
 template <int MT, int NW>
 __global__ __launch_bounds__(64 * NW) void lm_head_bf16(const bf16_t* __restrict__ z, size_t zplane, int M,
                                                         const bf16_t* __restrict__ W, int V, int K,
-                                                        float* __restrict__ hpart, float* __restrict__ logits_dbg) {
+                                                        float* __restrict__ hpart, float* __restrict__ logits_dbg,
+                                                        RngKey key, int sample) {
     constexpr int NT = 4;
     __shared__ f32x4 red[NW][NT * MT][64];
     __shared__ float lg[16 * MT][65];
@@ -219,7 +255,8 @@ __global__ __launch_bounds__(64 * NW) void lm_head_bf16(const bf16_t* __restrict
         lg[m][c + 3] = v[3];
     }
     __syncthreads();
-    if (threadIdx.x < 256) head_epilogue<16 * MT, 64>(lg, M, 0, M, n0, V, blockIdx.x, hpart, logits_dbg);
+    if (threadIdx.x < 256)
+        head_epilogue<16 * MT, 64>(lg, M, 0, M, n0, V, blockIdx.x, hpart, logits_dbg, key, sample);
 }
 
 // ------------------------------------------------------------------------------------------------------
@@ -227,7 +264,7 @@ __global__ __launch_bounds__(64 * NW) void lm_head_bf16(const bf16_t* __restrict
 // ------------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void lm_head_f32(const float* __restrict__ z, int M, const float* __restrict__ W,
                                                    int V, int K, float* __restrict__ hpart,
-                                                   float* __restrict__ logits_dbg) {
+                                                   float* __restrict__ logits_dbg, RngKey key, int sample) {
     __shared__ float lg[32][65];
     const int n0 = blockIdx.x * 64;
     const int c = threadIdx.x & 63;
@@ -241,7 +278,7 @@ __global__ __launch_bounds__(256) void lm_head_f32(const float* __restrict__ z, 
         lg[m][c] = a;
     }
     __syncthreads();
-    head_epilogue<32, 64>(lg, M, 0, M, n0, V, blockIdx.x, hpart, logits_dbg);
+    head_epilogue<32, 64>(lg, M, 0, M, n0, V, blockIdx.x, hpart, logits_dbg, key, sample);
 }
 
 // ------------------------------------------------------------------------------------------------------
@@ -252,7 +289,8 @@ __global__ __launch_bounds__(256) void lm_head_f32(const float* __restrict__ z, 
 #define TH_LG_BYTES (128 * 129 * 4)
 __global__ __launch_bounds__(256) void lm_head_tiled_bf16(const bf16_t* __restrict__ z, size_t zplane, int M,
                                                           const bf16_t* __restrict__ W, int V, int K,
-                                                          float* __restrict__ hpart, float* __restrict__ logits_dbg) {
+                                                          float* __restrict__ hpart, float* __restrict__ logits_dbg,
+                                                          RngKey key, int sample) {
     static_assert(TH_LG_BYTES >= (TL_SW + 2 * TL_BM * TL_LD) * 2, "logits tile must cover the staging buffers");
     __shared__ __attribute__((aligned(16))) char smem[TH_LG_BYTES];
     bf16_t* sw = (bf16_t*)smem;
@@ -277,25 +315,26 @@ __global__ __launch_bounds__(256) void lm_head_tiled_bf16(const bf16_t* __restri
             lg[m][n + 3] = acc[a][b][3];
         }
     __syncthreads();
-    head_epilogue<128, 128>(lg, min(128, M - m0), m0, M, n0, V, blockIdx.x, hpart, logits_dbg);
+    head_epilogue<128, 128>(lg, min(128, M - m0), m0, M, n0, V, blockIdx.x, hpart, logits_dbg, key, sample);
 }
 
 hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V, int K, float* hpart,
-                          float* logits_dbg, hipStream_t st) {
+                          float* logits_dbg, int sample, uint64_t seed, hipStream_t st) {
     const dim3 grid(head_groups(V, head_group_width(bf16, M)));
+    const RngKey key{(uint32_t)seed, (uint32_t)(seed >> 32)};
     const size_t zplane = (size_t)M * K;
     if (bf16 && M > 32)
         hipLaunchKernelGGL(lm_head_tiled_bf16, dim3(grid.x, (M + TL_BM - 1) / TL_BM), dim3(256), 0, st,
-                           (const bf16_t*)z, zplane, M, (const bf16_t*)wlm, V, K, hpart, logits_dbg);
+                           (const bf16_t*)z, zplane, M, (const bf16_t*)wlm, V, K, hpart, logits_dbg, key, sample);
     else if (!bf16)
         hipLaunchKernelGGL(lm_head_f32, grid, dim3(256), 0, st, (const float*)z, M, (const float*)wlm, V, K, hpart,
-                           logits_dbg);
+                           logits_dbg, key, sample);
     else if (M <= 16)
         hipLaunchKernelGGL((lm_head_bf16<1, 4>), grid, dim3(256), 0, st, (const bf16_t*)z, zplane, M,
-                           (const bf16_t*)wlm, V, K, hpart, logits_dbg);
+                           (const bf16_t*)wlm, V, K, hpart, logits_dbg, key, sample);
     else
         hipLaunchKernelGGL((lm_head_bf16<2, 4>), grid, dim3(256), 0, st, (const bf16_t*)z, zplane, M,
-                           (const bf16_t*)wlm, V, K, hpart, logits_dbg);
+                           (const bf16_t*)wlm, V, K, hpart, logits_dbg, key, sample);
     return hipGetLastError();
 }
 
@@ -322,7 +361,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
     return t;
 }
 
-__global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_groups, int top_k,
+__global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_groups, int top_k, int sample,
                                                             const float* __restrict__ hpart,
                                                             const int32_t* __restrict__ btok,
                                                             int32_t* __restrict__ tokens, int32_t* __restrict__ topk_ids,
@@ -332,6 +371,8 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
     __shared__ float red[MERGE_THREADS / 64];
     __shared__ float outv[DF_TOPK];
     __shared__ int outi[DF_TOPK];
+    __shared__ float sbest[MERGE_THREADS / 64];
+    __shared__ int sbid[MERGE_THREADS / 64];
     __shared__ int cnt;
     __shared__ float t8;
     const int m = blockIdx.x, t = threadIdx.x;
@@ -343,9 +384,33 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
     const size_t G = n_groups;
     const float* row = hpart + (size_t)m * HEAD_REC * G;  // field f of group gi at row[f * G + gi]
     float mx = -INFINITY, th = -INFINITY;
+    float sb = -INFINITY;  // temperature 1: best (perturbed score, id) over the records
+    int sbi = 0x7FFFFFFF;
     for (int gi = t; gi < n_groups; gi += MERGE_THREADS) {
         mx = fmaxf(mx, row[gi]);
         th = fmaxf(th, row[(2 + DF_TOPK - 1) * G + gi]);
+        if (sample) {
+            const float v = row[(2 + 2 * DF_TOPK) * G + gi];
+            const int id = __float_as_int(row[(3 + 2 * DF_TOPK) * G + gi]);
+            if (df_better(v, id, sb, sbi)) {
+                sb = v;
+                sbi = id;
+            }
+        }
+    }
+    if (sample) {  // (score, id) is a total order: the winner does not depend on the reduction order
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(sb, o, DF_WAVE);
+            const int oi = __shfl_xor(sbi, o, DF_WAVE);
+            if (df_better(ov, oi, sb, sbi)) {
+                sb = ov;
+                sbi = oi;
+            }
+        }
+        if ((t & 63) == 0) {  // read by thread 0 after the barriers below
+            sbest[t >> 6] = sb;
+            sbid[t >> 6] = sbi;
+        }
     }
     mx = block_max(mx, red);  // leaves the wave maxima in red until the next block reduction
     if (t < MERGE_THREADS / 64) {
@@ -437,7 +502,17 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
     __syncthreads();
     if (t == 0) {
         const float lse = mx + logf(se);
-        tokens[m] = outi[0];
+        int tok = outi[0];
+        if (sample) {
+            float b = sbest[0];
+            tok = sbid[0];
+            for (int w = 1; w < MERGE_THREADS / 64; ++w)
+                if (df_better(sbest[w], sbid[w], b, tok)) {
+                    b = sbest[w];
+                    tok = sbid[w];
+                }
+        }
+        tokens[m] = tok;
 #pragma unroll
         for (int j = 0; j < DF_TOPK; ++j) {  // static indices keep the state in registers
             if (j < top_k) {
@@ -448,12 +523,12 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
     }
 }
 
-hipError_t launch_head_merge(int bf16, int M, int V, int top_k, const float* hpart, const int32_t* block_tokens,
-                             int32_t* tokens, int32_t* topk_ids, float* topk_lp, uint32_t* err, hipStream_t st) {
+hipError_t launch_head_merge(int bf16, int M, int V, int top_k, int sample, const float* hpart,
+                             const int32_t* block_tokens, int32_t* tokens, int32_t* topk_ids, float* topk_lp,
+                             uint32_t* err, hipStream_t st) {
     const int groups = head_groups(V, head_group_width(bf16, M));
-    hipLaunchKernelGGL(head_merge, dim3(M), dim3(MERGE_THREADS), 0, st, M, V, groups, top_k, hpart, block_tokens,
-                       tokens,
-                       topk_ids, topk_lp, err);
+    hipLaunchKernelGGL(head_merge, dim3(M), dim3(MERGE_THREADS), 0, st, M, V, groups, top_k, sample, hpart,
+                       block_tokens, tokens, topk_ids, topk_lp, err);
     return hipGetLastError();
 }
 

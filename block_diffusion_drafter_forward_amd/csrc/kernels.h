@@ -76,11 +76,13 @@ int head_group_width(int bf16, int M);  // vocabulary columns per record group (
 int head_groups(int V, int width);
 size_t head_partial_floats(int bf16, int V, int M);
 // bfloat16: wlm is the packed V x K matrix; float32: row-major.
+// sample != 0: temperature 1, each row's token is a Gumbel-max sample with draws keyed by `seed`.
 hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V, int K, float* hpart,
-                          float* logits_dbg, hipStream_t st);
+                          float* logits_dbg, int sample, uint64_t seed, hipStream_t st);
 // Also flags block tokens outside [0, V) in the device error word.
-hipError_t launch_head_merge(int bf16, int M, int V, int top_k, const float* hpart, const int32_t* block_tokens,
-                             int32_t* tokens, int32_t* topk_ids, float* topk_lp, uint32_t* err, hipStream_t st);
+hipError_t launch_head_merge(int bf16, int M, int V, int top_k, int sample, const float* hpart,
+                             const int32_t* block_tokens, int32_t* tokens, int32_t* topk_ids, float* topk_lp,
+                             uint32_t* err, hipStream_t st);
 
 // ---- DDTree ----------------------------------------------------------------------------------------------
 // Per row of logits[rows][stride]: the K best (value desc, id asc) and their log-probabilities.
@@ -93,5 +95,13 @@ hipError_t launch_ddtree_build(int batch, int D, int K, const float* lp, const i
 hipError_t launch_ddtree_walk(int batch, int budget, int max_accept, const int32_t* node_token,
                               const int32_t* node_parent, const int32_t* n_nodes, const int32_t* target_next,
                               int32_t* accept_len, int32_t* accept_nodes, int32_t* bonus, hipStream_t st);
+
+// ---- verification at temperature 1 -------------------------------------------------------------------
+size_t sv_workspace_bytes(int B, int n_draft, int V);
+// Drafter rows of request b at q + b * q_req + j * V (j < n_draft), target rows at p + b * p_req + j * V
+// (j <= n_draft); n_draft < 64.
+hipError_t launch_verify_sample(int batch, int n_draft, int V, const int32_t* draft, int64_t dstride, const float* q,
+                                int64_t q_req, const float* p, int64_t p_req, uint64_t seed, int32_t* tau,
+                                int32_t* next_token, void* ws, hipStream_t st);
 
 }  // namespace df

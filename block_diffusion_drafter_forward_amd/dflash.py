@@ -79,6 +79,16 @@ _SIGS = {
                                           ctypes.c_void_p]),
     "dflash_accept_len": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
+    "dflash_draft_block_sample": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(dflash_kv),
+                                                 ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_size_t, ctypes.c_void_p]),
+    "dflash_verify_sample_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "dflash_verify_sample": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                            ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "dflash_last_error": (ctypes.c_char_p, []),
     "dflash_topk_logprobs": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -188,6 +198,24 @@ def dflash_draft_block(h, batch, block_tokens, ctx_len, page_table, max_pages, k
 
 def dflash_accept_len(batch, n_draft, draft, draft_stride, target, target_stride, tau, stream) -> int:
     return lib().dflash_accept_len(batch, n_draft, draft, draft_stride, target, target_stride, tau, stream)
+
+
+def dflash_draft_block_sample(h, batch, block_tokens, ctx_len, page_table, max_pages, kv: Optional[dflash_kv],
+                              max_ctx, top_k, seed, tokens, topk_ids, topk_logprobs, logits, ws, ws_bytes,
+                              stream) -> int:
+    return lib().dflash_draft_block_sample(h, batch, block_tokens, ctx_len, page_table, max_pages,
+                                           ctypes.byref(kv) if kv is not None else None, max_ctx, top_k, seed,
+                                           tokens, topk_ids, topk_logprobs, logits, ws, ws_bytes, stream)
+
+
+def dflash_verify_sample_workspace_bytes(batch, n_draft, vocab) -> int:
+    return lib().dflash_verify_sample_workspace_bytes(batch, n_draft, vocab)
+
+
+def dflash_verify_sample(batch, n_draft, vocab, draft, draft_stride, q_logits, q_req_stride, p_logits, p_req_stride,
+                         seed, tau, next_token, ws, ws_bytes, stream) -> int:
+    return lib().dflash_verify_sample(batch, n_draft, vocab, draft, draft_stride, q_logits, q_req_stride, p_logits,
+                                      p_req_stride, seed, tau, next_token, ws, ws_bytes, stream)
 
 
 def dflash_last_error() -> str:
@@ -300,11 +328,41 @@ class DraftModel:
                                  max_ctx, top_k, tokens.data_ptr(), _ptr(topk_ids), _ptr(topk_logprobs), dbg,
                                  ws.data_ptr(), ws.numel(), _stream(stream)), "dflash_draft_block")
 
+    def draft_sample(self, block_tokens, ctx_len, page_table, kv: Optional[dflash_kv], max_ctx: int, top_k: int,
+                     seed: int, tokens, topk_ids=None, topk_logprobs=None, ws=None, logits=None, stream=None) -> None:
+        """Temperature-1 drafting: tokens are Gumbel-max samples keyed by `seed`; logits (optional) receives
+        the full [batch][L][V] float32 logits that verify_sample reads."""
+        batch = block_tokens.shape[0]
+        check(dflash_draft_block_sample(self.handle, batch, block_tokens.data_ptr(), ctx_len.data_ptr(),
+                                        _ptr(page_table), page_table.shape[1] if page_table is not None else 0, kv,
+                                        max_ctx, top_k, seed, tokens.data_ptr(), _ptr(topk_ids), _ptr(topk_logprobs),
+                                        _ptr(logits), ws.data_ptr(), ws.numel(), _stream(stream)),
+              "dflash_draft_block_sample")
+
 
 def accept_len(draft, target, tau, stream=None) -> None:
     """tau[r] = 1 + common-prefix length of draft[r] and target[r] (int32 CUDA tensors, row-major)."""
     check(dflash_accept_len(draft.shape[0], draft.shape[1], draft.data_ptr(), draft.stride(0), target.data_ptr(),
                             target.stride(0), tau.data_ptr(), _stream(stream)), "dflash_accept_len")
+
+
+def verify_sample_workspace_bytes(batch: int, n_draft: int, vocab: int) -> int:
+    return dflash_verify_sample_workspace_bytes(batch, n_draft, vocab)
+
+
+def verify_sample(draft, q_logits, p_logits, seed: int, tau, next_token, ws, stream=None) -> None:
+    """Temperature-1 verification.  draft: int32 [B, n] (any row stride); q_logits: float32 [B, n, V] view
+    (rows contiguous, any request stride); p_logits: float32 [B, n + 1, V] likewise; tau, next_token: int32 [B];
+    ws: a 256-byte-aligned tensor of at least verify_sample_workspace_bytes(B, n, V) bytes."""
+    B, n = draft.shape
+    V = p_logits.shape[-1]
+    if p_logits.stride(-1) != 1 or p_logits.stride(1) != V or (n and (q_logits.stride(-1) != 1 or
+                                                                     q_logits.stride(1) != V)):
+        raise ValueError("logit rows must be contiguous with stride V")
+    check(dflash_verify_sample(B, n, V, draft.data_ptr(), draft.stride(0), _ptr(q_logits) if n else None,
+                               q_logits.stride(0) if n else 0, p_logits.data_ptr(), p_logits.stride(0), seed,
+                               tau.data_ptr(), next_token.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                               _stream(stream)), "dflash_verify_sample")
 
 
 def make_kv(kpool, vpool, n_pages: int) -> dflash_kv:

@@ -91,6 +91,14 @@ class GpuWorkload:
                          self.topk_ids if k > 0 else None, self.topk_lp if k > 0 else None, self.draft_ws,
                          logits=logits, hidden=hidden, stream=stream)
 
+    def draft_sample(self, seed: int, top_k=None, logits=None, stream=None):
+        """Temperature-1 pass: tokens are Gumbel-max samples keyed by seed; logits (optional) gets the full
+        float32 logits."""
+        k = self.wl.top_k if top_k is None else top_k
+        self.model.draft_sample(self.block_tokens, self.ctx_len, self.page_table, self.kv, self.max_ctx, k, seed,
+                                self.tokens, self.topk_ids if k > 0 else None, self.topk_lp if k > 0 else None,
+                                self.draft_ws, logits=logits, stream=stream)
+
     def accept(self, target: torch.Tensor, stream=None):
         L = self.shape.block_len
         D.check(D.dflash_accept_len(self.wl.batch, L - 1, self.tokens.data_ptr() + 4, L, target.data_ptr(),

@@ -15,6 +15,9 @@
  *                        Trees", paper-graph summary, section 3.4.2: per-position marginals softmax(l_i));
  *   dflash_accept_len   greedy acceptance: accepted drafts up to the first mismatch, plus the bonus token
  *                       (DFlash page, section 3.4.1, the bonus-token paragraph under Eq. 1).
+ *   dflash_draft_block_sample, dflash_verify_sample
+ *                       the same pass and its verification at temperature 1 (section 3.4.4 "Single forward
+ *                       pass prediction" and "Integration with verification").
  *
  * Conventions
  *   - Every pointer marked "device" is GPU memory owned by the caller; the library never allocates, frees
@@ -185,6 +188,43 @@ int dflash_draft_block(dflash_handle *h, int batch, const int32_t *block_tokens,
  * All arrays are device int32.  No workspace is used.                                                     */
 int dflash_accept_len(int batch, int n_draft, const int32_t *draft, int64_t draft_stride, const int32_t *target,
                       int64_t target_stride, int32_t *tau, void *stream);
+
+/* ---- Temperature 1 (DFlash page, section 3.4.4: "Single forward pass prediction" samples each row from the
+ * softmax of its logits, "Integration with verification" verifies by standard speculative decoding) --------
+ * Random draws come from Philox4x32-10 (Salmon et al., SC 2011), counter-based: the word for (tag, row, j)
+ * under a 64-bit seed is word j % 4 of the block at counter (j / 4, row, tag, 0), key (seed & 0xffffffff,
+ * seed >> 32); a word c is the uniform u = (c + 1/2) / 2^32 and the Gumbel variable -ln(-ln(1 - u)).  Use a
+ * fresh seed per cycle.                                                                                   */
+
+/* As dflash_draft_block, but each row's token is sampled from softmax(logits) by the Gumbel-max rule:
+ * tokens[r][i] = argmax_j logit_j + G_j (ties -> smaller id), G from stream tag 1, row r * L + i, j = token
+ * id.  top-k outputs are unchanged (by logit).  logits: device float [batch][L][V] full logits, or NULL;
+ * dflash_verify_sample needs them (the drafter rows of the drafts are rows 1 .. L-1).  Same workspace as
+ * dflash_draft_block.                                                                                     */
+int dflash_draft_block_sample(dflash_handle *h, int batch, const int32_t *block_tokens, const int32_t *ctx_len,
+                              const int32_t *page_table, int max_pages, const dflash_kv *kv, int max_ctx, int top_k,
+                              uint64_t seed, int32_t *tokens, int32_t *topk_ids, float *topk_logprobs, float *logits,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes for dflash_verify_sample (0 on invalid arguments).                                      */
+size_t dflash_verify_sample_workspace_bytes(int batch, int n_draft, int vocab);
+
+/* Verification at temperature 1 by modified rejection sampling (Leviathan, Kalman and Matias, ICML 2023,
+ * Algorithm 1).  For request r, with p_j = softmax of target row j and q_j = softmax of drafter row j:
+ * draft j (in order, j < n_draft) is kept iff ln u_j < ln p_j(y_j) - ln q_j(y_j), u_j from stream tag 2,
+ * row r, index j; a draft id outside [0, vocab) is rejected.  At the first rejection k the next token is a
+ * Gumbel-max sample (tag 3, row r, j = token id) from max(0, p_k - q_k), or from p_k where that vanishes;
+ * if all drafts are kept, from p_{n_draft} (the bonus row).  tau[r] = kept + 1, next_token[r] = the token.
+ *   draft        device int32, draft[r * draft_stride + j]; typical: sampled tokens + 1, stride L
+ *   q_logits     device float, drafter row j of request r at q_logits + r * q_req_stride + j * vocab
+ *                (typical: dflash_draft_block_sample's logits + vocab, stride L * vocab); NULL if n_draft == 0
+ *   p_logits     device float, target row j (0 .. n_draft) of request r at p_logits + r * p_req_stride +
+ *                j * vocab: row j is the target's distribution after the block prefix ending in draft j - 1
+ *   Every row needs a finite entry.  0 <= n_draft <= 63, 1 <= batch <= 65535.  ws: 256-byte aligned, at least
+ *   dflash_verify_sample_workspace_bytes(batch, n_draft, vocab) bytes.                                    */
+int dflash_verify_sample(int batch, int n_draft, int vocab, const int32_t *draft, int64_t draft_stride,
+                         const float *q_logits, int64_t q_req_stride, const float *p_logits, int64_t p_req_stride,
+                         uint64_t seed, int32_t *tau, int32_t *next_token, void *ws, size_t ws_bytes, void *stream);
 
 /* ---- DDTree on the drafter's marginals ("Accelerating Speculative Decoding with Block Diffusion Draft
  * Trees", §3.4.4 Lemma 1 and Algorithm 1, §3.4.5 the verifier walk) --------------------------------------

@@ -264,3 +264,46 @@ def test_ddtree_walk_validation(D, args, code):
     assert D.dflash_ddtree_walk(a["batch"], a["budget"], a["max_accept"], a["tok"], a["par"], a["n"], a["target"],
                                 a["alen"], a["anodes"], a["bonus"], None) == code
     assert D.dflash_last_error()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(batch=0), -1), (dict(tokens=None), -1), (dict(top_k=9), -4), (dict(ws_bytes=100), -3),
+    (dict(max_ctx=129), -3), (dict(ws=0x100010), -1),
+])
+def test_draft_block_sample_validation(D, over, code):
+    """The temperature-1 pass shares the greedy pass's checks (same shapes, same workspace)."""
+    m = _create(D, _shape())
+    a = dict(batch=1, max_ctx=100, top_k=8, tokens=0x60, ws=0x100000, ws_bytes=1 << 40)
+    a.update(over)
+    try:
+        assert D.dflash_draft_block_sample(m.handle, a["batch"], 0x10, 0x20, 0x30, 8, D.dflash_kv(0x40, 0x50, 8),
+                                           a["max_ctx"], a["top_k"], 12345, a["tokens"], 0x70, 0x80, 0x90, a["ws"],
+                                           a["ws_bytes"], None) == code
+        assert D.dflash_last_error()
+    finally:
+        m.close()
+
+
+def test_verify_sample_workspace_size(D):
+    a = D.dflash_verify_sample_workspace_bytes(1, 15, 151936)
+    assert a >= 31 * 38 * 8 + 38 * 16 + 4 and a % 256 == 0
+    assert D.dflash_verify_sample_workspace_bytes(16, 15, 151936) > a
+    assert D.dflash_verify_sample_workspace_bytes(1, 0, 10) > 0
+    assert D.dflash_verify_sample_workspace_bytes(0, 15, 100) == 0
+    assert D.dflash_verify_sample_workspace_bytes(1, 64, 100) == 0
+    assert D.dflash_verify_sample_workspace_bytes(1, 15, 0) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(batch=0), -1), (dict(batch=65536), -1), (dict(n_draft=64), -4), (dict(n_draft=-1), -4),
+    (dict(vocab=0), -1), (dict(p=None), -1), (dict(tau=None), -1), (dict(nxt=None), -1), (dict(ws=None), -1),
+    (dict(draft=None), -1), (dict(q=None), -1), (dict(dstride=14), -1), (dict(p_req=15 * 1000), -1),
+    (dict(q_req=14 * 1000), -1), (dict(ws_bytes=100), -3), (dict(ws=0x100010), -1),
+])
+def test_verify_sample_validation(D, over, code):
+    a = dict(batch=2, n_draft=15, vocab=1000, draft=0x10, dstride=16, q=0x20, q_req=16 * 1000, p=0x30,
+             p_req=16 * 1000, tau=0x40, nxt=0x50, ws=0x100000, ws_bytes=1 << 30)
+    a.update(over)
+    assert D.dflash_verify_sample(a["batch"], a["n_draft"], a["vocab"], a["draft"], a["dstride"], a["q"], a["q_req"],
+                                  a["p"], a["p_req"], 7, a["tau"], a["nxt"], a["ws"], a["ws_bytes"], None) == code
+    assert D.dflash_last_error()

@@ -4,7 +4,9 @@ one drafter pass with top-8, then acceptance.
 
 Checked: greedy tokens (top-2 gap > 1e-2) and top-8 ids (top-9 gaps > 1e-2) bit-exact; top-8 log-probs and
 48 sampled logits per row within 3e-2 + 2e-2 |ref| (float32 drafter: 1e-4 relative); acceptance lengths
-exact; sampled cached K/V rows within the bound of the reduced-shape test; a clean device error word.
+exact; sampled cached K/V rows within the bound of the reduced-shape test; a clean device error word.  The
+temperature-1 pass is checked on the same inputs: identical logits and top-k, and each sampled token equal to
+the oracle's Gumbel-max sample on the kernel's logits.
 """
 import os
 
@@ -85,3 +87,19 @@ def test_full_size_parity(name):
                 rms = np.sqrt(np.mean(want ** 2, axis=-1, keepdims=True))
                 bound = (2.0 ** -5 * np.abs(want) + 2.0 ** -8 * rms) if s.bf16 else 1e-5 * (np.abs(want) + rms)
                 assert np.all(np.abs(got - want) <= bound)
+
+    # temperature 1 at the same size: the sampled pass computes the same logits and top-k, and each row's token
+    # is the oracle's Gumbel-max sample on those logits (exact where float32 noise rounding cannot matter)
+    seed = 0x5EED0000000A + B
+    print(f"[fullsize] {name}: sampled pass, seed {seed:#x}", flush=True)
+    logits2 = torch.full_like(logits, float("nan"))
+    g.draft_sample(seed, top_k=8, logits=logits2)
+    torch.cuda.synchronize()
+    assert g.error_word() == 0
+    assert torch.equal(logits2, logits)
+    np.testing.assert_array_equal(g.topk_ids.cpu().numpy(), ids)
+    stok = g.tokens.cpu().numpy().reshape(-1)
+    sids, gap = O.sampling.sample_rows(logits.cpu().numpy().reshape(B * L, V).astype(np.float64), seed)
+    ok = gap > 1e-4
+    assert ok.mean() > 0.95
+    np.testing.assert_array_equal(stok[ok], sids[ok])
