@@ -6,3 +6,4 @@ package.  The HIP library and its Python binding never import it, and it imports
 from .dflash_ref import *  # noqa: F401,F403
 from . import ddtree  # noqa: F401,E402
 from . import sampling  # noqa: F401,E402
+from . import tree_attention  # noqa: F401,E402
