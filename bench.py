@@ -46,6 +46,9 @@ def parse():
                         "tree construction, verifier walk) after a drafter pass, one JSON line per budget")
     p.add_argument("--sample", action="store_true",
                    help="temperature 1: time the sampled drafter pass and the rejection-sampling verifier")
+    p.add_argument("--tree-attn", default=None,
+                   help="comma-separated DDTree budgets: time tree attention over one target layer (Qwen3-8B "
+                        "attention shape, 4096 cached tokens) for trees of that many nodes")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run the library's stream-copy kernel on 1 GiB (HBM-counter calibration)")
     return p.parse_args()
@@ -371,8 +374,74 @@ def sample_bench(args):
                       "cycle_us": round(us_cycle, 1), "mean_tau": round(float(np.mean(taus)), 2)}), flush=True)
 
 
+def tree_attn_bench(args):
+    """Tree attention over one synthetic target layer at the Qwen3-8B attention shape (32 query heads, 8 KV
+    heads, head_dim 128), 4096 cached context tokens in shuffled 16-token pages, for trees that
+    dflash_ddtree_build pops from random drafter marginals (depth 15).  FLOPs count the context part's two products,
+    4 (N + 1) n_q C d; bytes count the cached K/V once plus the tree's q / k / v and the output."""
+    import torch
+    from block_diffusion_drafter_forward_amd import dflash as D
+    nq, nkv, d, C = 32, 8, 128, 4096
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    rng = np.random.default_rng(3)
+    n_pages = C // 16 + 5
+    kp = torch.randn((n_pages, nkv, 16, d), generator=gen, device="cuda").to(torch.bfloat16)
+    vp = torch.randn((n_pages, nkv, d, 16), generator=gen, device="cuda").to(torch.bfloat16)
+    pt = torch.as_tensor(rng.permutation(n_pages)[: C // 16].astype(np.int32)[None, :], device="cuda")
+    ctx = torch.tensor([C], dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for budget in [int(x) for x in args.tree_attn.split(",")]:
+        T = budget + 1
+        K = min(budget, 64)
+        x = torch.rand((15, 400), generator=gen, device="cuda") ** (1 / 0.3)
+        lp = torch.sort(torch.log(x / x.sum(-1, keepdim=True)), dim=-1, descending=True).values[:, :K].contiguous()
+        ids = torch.arange(K, dtype=torch.int32, device="cuda").repeat(15, 1).contiguous()
+        ntok_t, npar, ndep = (torch.empty((1, budget), dtype=torch.int32, device="cuda") for _ in range(3))
+        nlq = torch.empty((1, budget), dtype=torch.float32, device="cuda")
+        nn = torch.empty(1, dtype=torch.int32, device="cuda")
+        D.check(D.dflash_ddtree_build(1, 15, K, lp.data_ptr(), ids.data_ptr(), 15 * K, budget, ntok_t.data_ptr(),
+                                      npar.data_ptr(), ndep.data_ptr(), nlq.data_ptr(), nn.data_ptr(),
+                                      stream.cuda_stream), "dflash_ddtree_build")
+        # tree token 0 = the root, token i = node i - 1 (its parent token = node parent + 1)
+        par = torch.cat([torch.full((1, 1), -1, dtype=torch.int32, device="cuda"), npar + 1], dim=1).contiguous()
+        assert int(nn.item()) == budget
+        ntok = torch.tensor([T], dtype=torch.int32, device="cuda")
+        q = torch.randn((1, T, nq, d), generator=gen, device="cuda").to(torch.bfloat16)
+        k = torch.randn((1, T, nkv, d), generator=gen, device="cuda").to(torch.bfloat16)
+        v = torch.randn((1, T, nkv, d), generator=gen, device="cuda").to(torch.bfloat16)
+        out = torch.empty((1, T, nq, d), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(D.dflash_tree_attention_workspace_bytes(1, T, nq, nkv, d, C), dtype=torch.uint8,
+                         device="cuda")
+
+        def run():
+            D.tree_attention(ntok, par, q, k, v, kp, vp, pt, ctx, C, 1e6, out, ws, stream=stream)
+
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        flops = 4.0 * T * nq * C * d
+        nbytes = 2 * C * nkv * d * 2 + T * (nq + 2 * nkv) * d * 2 + T * nq * d * 2
+        print(json.dumps({"tree_attention": "qwen3-8b-attention-shape", "ctx": C, "nodes": budget, "tokens": T,
+                          "us": round(us, 1), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                          "mfma_frac_bf16": round(flops / (us * 1e-6) / 2.5e15, 3),
+                          "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}), flush=True)
+
+
 def main():
     args = parse()
+    if args.tree_attn:
+        if args.gpus != 1:
+            sys.exit("bench.py runs on one GPU; --gpus must be 1")
+        tree_attn_bench(args)
+        return
     if args.sample:
         if args.gpus != 1:
             sys.exit("bench.py runs on one GPU; --gpus must be 1")

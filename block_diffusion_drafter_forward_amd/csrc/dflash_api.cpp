@@ -647,6 +647,59 @@ extern "C" int dflash_verify_sample(int batch, int n_draft, int vocab, const int
     return DFLASH_OK;
 }
 
+// Shape checks of the tree attention: DFLASH_OK, or the status and *msg.
+static int tree_shape_check(int batch, int max_tokens, int nq, int nkv, int d, int max_ctx, const char** msg) {
+    if (batch < 1 || batch > 65535) return *msg = "batch must be in [1, 65535]", DFLASH_E_ARG;
+    if (max_tokens < 1 || max_tokens > TREE_MAX_TOKENS) return *msg = "max_tokens must be in [1, 2048]", DFLASH_E_ARG;
+    if (max_ctx < 0) return *msg = "max_ctx must be >= 0", DFLASH_E_ARG;
+    if (nkv < 1 || nq < 1 || nq % nkv) return *msg = "n_q_heads must be a multiple of n_kv_heads", DFLASH_E_ARG;
+    if (d != 128) return *msg = "head_dim must be 128", DFLASH_E_UNSUPPORTED;
+    const int G = nq / nkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return *msg = "n_q_heads / n_kv_heads must be 1, 2, 4 or 8", DFLASH_E_UNSUPPORTED;
+    return DFLASH_OK;
+}
+
+extern "C" size_t dflash_tree_attention_workspace_bytes(int batch, int max_tokens, int n_q_heads, int n_kv_heads,
+                                                        int head_dim, int max_ctx) {
+    const char* msg;
+    if (tree_shape_check(batch, max_tokens, n_q_heads, n_kv_heads, head_dim, max_ctx, &msg) != DFLASH_OK) return 0;
+    return plan_tree(batch, max_tokens, n_q_heads, n_kv_heads, max_ctx).total;
+}
+
+extern "C" int dflash_tree_attention(int batch, int max_tokens, const int32_t* n_tokens, const int32_t* parent,
+                                     int n_q_heads, int n_kv_heads, int head_dim, const void* q, const void* k,
+                                     const void* v, const void* k_pages, const void* v_pages, int n_pages,
+                                     const int32_t* page_table, int max_pages, const int32_t* ctx_len, int max_ctx,
+                                     float rope_theta, void* out, void* ws, size_t ws_bytes, void* stream) {
+    const char* msg;
+    if (const int code = tree_shape_check(batch, max_tokens, n_q_heads, n_kv_heads, head_dim, max_ctx, &msg))
+        return fail(code, "%s", msg);
+    if (!n_tokens || !parent || !q || !k || !v || !ctx_len || !out || !ws)
+        return fail(DFLASH_E_ARG, "a required pointer is NULL");
+    if (max_ctx > 0) {
+        if (!k_pages || !v_pages || !page_table) return fail(DFLASH_E_ARG, "page table or KV pages are NULL");
+        if (max_pages < 1 || n_pages < 1) return fail(DFLASH_E_ARG, "max_pages and n_pages must be >= 1");
+        if ((long long)max_ctx > (long long)max_pages * 16)
+            return fail(DFLASH_E_CAPACITY, "max_ctx %d exceeds max_pages * 16", max_ctx);
+        if ((((uintptr_t)k_pages) | ((uintptr_t)v_pages)) & 15) return fail(DFLASH_E_ARG, "KV pages must be 16-byte aligned");
+    }
+    if (!(rope_theta >= 0.f)) return fail(DFLASH_E_ARG, "rope_theta must be >= 0");
+    if ((((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v) | ((uintptr_t)out)) & 15)
+        return fail(DFLASH_E_ARG, "q, k, v and out must be 16-byte aligned");
+    const TreePlan p = plan_tree(batch, max_tokens, n_q_heads, n_kv_heads, max_ctx);
+    if (ws_bytes < p.total) return fail(DFLASH_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, p.total);
+    if (((uintptr_t)ws) & 255) return fail(DFLASH_E_ARG, "workspace must be 256-byte aligned");
+    RopeFreq rf{};
+    rf.on = rope_theta > 0.f;  // theta = 0: no rotation
+    for (int i = 0; i < head_dim / 2; ++i)  // theta^(-2i/d) in double, rounded to float
+        rf.inv[i] = rf.on ? (float)std::pow((double)rope_theta, -(2.0 * i) / head_dim) : 0.f;
+    HIP_TRY(launch_tree_attention(p, batch, max_tokens, n_tokens, parent, n_q_heads, n_kv_heads, q, k, v, k_pages,
+                                  v_pages, n_pages, page_table, max_pages, ctx_len, max_ctx, rf, out, ws,
+                                  (hipStream_t)stream));
+    return DFLASH_OK;
+}
+
 // Workspace of dflash_linear: the float32 split partials, then (bfloat16) the packed image of w.
 static size_t linear_part_bytes(int dtype, int M, int N, int K) {
     const GemmPlan p = plan_gemm(dtype == DFLASH_BF16, M, N, K);

@@ -104,4 +104,19 @@ hipError_t launch_verify_sample(int batch, int n_draft, int V, const int32_t* dr
                                 int64_t q_req, const float* p, int64_t p_req, uint64_t seed, int32_t* tau,
                                 int32_t* next_token, void* ws, hipStream_t st);
 
+// ---- tree attention -----------------------------------------------------------------------------------
+#define TREE_MAX_TOKENS 2048  // tree tokens per request, root included
+#define TREE_MAX_ANC 64       // per token: its depth, then the root-to-token path (depth <= 62)
+struct TreePlan {
+    int tiles, stiles, chunks, chunk_tokens;  // 16-token tiles, workgroup super tiles, context chunks
+    size_t q_off, k_off, anc_off, o_off, ml_off, total;
+};
+TreePlan plan_tree(int batch, int max_tokens, int nq, int nkv, int max_ctx);
+// q, k, v: bfloat16 [batch][T][heads][128]; kpool / vpool: one layer's pages; out: bfloat16 [batch][T][nq][128].
+hipError_t launch_tree_attention(const TreePlan& p, int batch, int T, const int32_t* n_tokens, const int32_t* parent,
+                                 int nq, int nkv, const void* q, const void* k, const void* v, const void* kpool,
+                                 const void* vpool, int n_pages, const int32_t* pt, int max_pages,
+                                 const int32_t* ctx_len, int max_ctx, const RopeFreq& rf, void* out, void* ws,
+                                 hipStream_t st);
+
 }  // namespace df

@@ -1,0 +1,532 @@
+// Tree attention for verifying a draft tree in one target-layer pass ("Accelerating Speculative Decoding with
+// Block Diffusion Draft Trees", section 3.4.5 "Verification: Tree Attention and the Verifier Walk"): the
+// flattened tree tokens (token 0 = the root / bonus token, every parent before its children) attend to the
+// whole cached context and, inside the tree, only to their ancestors and themselves; a token's position id
+// is its depth, i.e. absolute position ctx_len + depth.
+//
+// Three launches:
+//   tree_prep       per 16 tokens: depth and root-to-token ancestor list from the parent links (walked in
+//                   LDS), and RoPE of q and the tree k at ctx_len + depth (cos / sin per depth from an LDS
+//                   table), rounded to bfloat16
+//   tree_ctx_bf16   the context part, MFMA: one workgroup per (16-token tile, KV head, context chunk,
+//                   request), one wave per query head of the KV group; 64-key rounds staged in LDS as in the
+//                   drafter's attention.  The KV head is the fastest grid index, so with 8 KV heads (or a
+//                   multiple) workgroup i lands on XCD i % 8 = KV head: each XCD's L2 holds one head's K/V
+//                   for every tile.  Writes (m, l, O) partials.
+//   tree_merge      one wave per (token, KV head): the token's ancestor keys (at most depth + 1, a short list)
+//                   by vector dot products, merged with the context partials by log-sum-exp; bfloat16 out.
+#include "common.h"
+#include "kernels.h"
+
+namespace df {
+
+#define TA_D 128
+#define TA_SUB 64         // keys per LDS round
+#define TA_MAX_PAGES 256  // pages of one context chunk
+#define TA_KLD (128 + 8)
+#define TA_VLD (16 + 8)
+
+static size_t ta_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Waves per context workgroup: the G query heads of a KV head times TA_WAVES / G token tiles, all served by
+// the same staged K/V.
+#define TA_WAVES 8
+
+TreePlan plan_tree(int batch, int max_tokens, int nq, int nkv, int max_ctx) {
+    TreePlan p{};
+    p.tiles = (max_tokens + 15) / 16;
+    const int tw = TA_WAVES / (nq / nkv);
+    p.stiles = (p.tiles + tw - 1) / tw;
+    p.chunks = 0;
+    p.chunk_tokens = 0;
+    if (max_ctx > 0) {
+        const int units = batch * p.stiles * nkv;
+        int want = (512 + units - 1) / units;
+        const int max_chunks = (max_ctx + TA_SUB - 1) / TA_SUB;
+        want = want < 1 ? 1 : (want > max_chunks ? max_chunks : want);
+        int ct = (max_ctx + want - 1) / want;
+        ct = (ct + TA_SUB - 1) / TA_SUB * TA_SUB;
+        if (ct > 16 * TA_MAX_PAGES) ct = 16 * TA_MAX_PAGES;
+        p.chunk_tokens = ct;
+        p.chunks = (max_ctx + ct - 1) / ct;
+    }
+    const size_t T = (size_t)p.tiles * 16;
+    size_t off = 256;  // error word
+    p.q_off = off;
+    off += ta_align((size_t)batch * T * nq * TA_D * 2);
+    p.k_off = off;
+    off += ta_align((size_t)batch * T * nkv * TA_D * 2);
+    p.anc_off = off;
+    off += ta_align((size_t)batch * T * TREE_MAX_ANC * 4);
+    p.o_off = off;
+    off += ta_align((size_t)batch * p.tiles * nq * p.chunks * 16 * TA_D * 4);
+    p.ml_off = off;
+    off += ta_align((size_t)batch * p.tiles * nq * p.chunks * 16 * 2 * 4);
+    p.total = off;
+    return p;
+}
+
+// ------------------------------------------------------------------------------------------------------
+// tree_prep
+// ------------------------------------------------------------------------------------------------------
+// anc[b][i][0] = depth d of token i, anc[b][i][1 + j] = its ancestor at depth j (j = 0: the root, j = d:
+// itself); a token past n_tokens has anc[..][0] = -1.  Parent links that are not < the token's own index
+// are flagged and treated as the root.
+__global__ __launch_bounds__(256) void tree_prep(int T, const int32_t* __restrict__ n_tokens,
+                                                 const int32_t* __restrict__ parent, int nq, int nkv,
+                                                 const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                 const int32_t* __restrict__ ctx_len, int max_ctx, RopeFreq rf,
+                                                 bf16_t* __restrict__ qr, bf16_t* __restrict__ kr,
+                                                 int32_t* __restrict__ anc, int Tpad, uint32_t* err) {
+    __shared__ int spar[TREE_MAX_TOKENS];
+    __shared__ int sdep[16];
+    __shared__ int smaxdep;
+    __shared__ float scs[TREE_MAX_ANC][TA_D / 2][2];
+    const int b = blockIdx.y, tile = blockIdx.x, t = threadIdx.x;
+    const int n = min(max(n_tokens[b], 0), T);
+    int C = ctx_len[b];
+    if (C < 0 || C > max_ctx) {
+        if (tile == 0 && t == 0) set_err(err, DFLASH_DEVERR_POS);
+        C = C < 0 ? 0 : max_ctx;
+    }
+    const int i0 = tile * 16;
+    const int need = min(n, i0 + 16);  // parents of tokens below this tile's end
+    for (int j = t; j < need; j += 256) spar[j] = parent[(size_t)b * T + j];
+    if (t == 0) smaxdep = 0;
+    __syncthreads();
+    if (t < 16) {
+        const int i = i0 + t;
+        int32_t* a = anc + ((size_t)b * Tpad + i) * TREE_MAX_ANC;
+        int depth = -1;
+        if (i < n) {
+            // first walk: the depth (a link that does not point to an earlier token, or a path deeper than
+            // TREE_MAX_ANC - 2, is flagged and cut at the root)
+            int cur = i, len = 0;
+            bool bad = false;
+            while (cur != 0) {
+                int p = spar[cur];
+                if (p < 0 || p >= cur || (len == TREE_MAX_ANC - 3 && p != 0)) {  // depth stays <= TREE_MAX_ANC - 2
+                    bad = true;
+                    p = 0;
+                }
+                ++len;
+                cur = p;
+            }
+            if (bad) set_err(err, DFLASH_DEVERR_TREE);
+            depth = len;
+            // second walk: the path from the token up, stored root first
+            a[1] = 0;
+            cur = i;
+            for (int j = len; j >= 1; --j) {
+                a[1 + j] = cur;
+                int p = spar[cur];
+                cur = (p < 0 || p >= cur) ? 0 : p;
+            }
+            atomicMax(&smaxdep, depth);
+        }
+        a[0] = depth;
+        sdep[t] = depth;
+    }
+    __syncthreads();
+    // cos / sin of the angles float32(float32(C + depth) * inv_freq) of the depths present in the tile
+    const int nd = smaxdep + 1;
+    for (int e = t; e < nd * (TA_D / 2); e += 256) {
+        const int dep = e >> 6, pr = e & 63;
+        float s = 0.f, c = 1.f;  // rotary embedding off: identity
+        if (rf.on) sincosf((float)(C + dep) * rf.inv[pr], &s, &c);
+        scs[dep][pr][0] = c;
+        scs[dep][pr][1] = s;
+    }
+    __syncthreads();
+    // RoPE of the tile's rows (16 tokens x (nq + nkv) heads): eight lanes per row, lane j rotating the pairs
+    // (8j + e, 64 + 8j + e), e < 8, from two 16-byte loads; four rows in flight per lane
+    const int hh = nq + nkv, rows = 16 * hh;
+    const int sub = t & 7, slot = t >> 3;  // 32 row slots per pass
+    for (int r0 = 0; r0 < rows; r0 += 32 * 4) {
+        u32x4 x1[4], x2[4];
+        int rr[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = r0 + u * 32 + slot;
+            rr[u] = row;
+            const int tok = row / hh, h = row - tok * hh;
+            const bool ok = row < rows && sdep[min(tok, 15)] >= 0;
+            const bool isq = h < nq;
+            const bf16_t* src = isq ? q + (((size_t)b * T + i0 + tok) * nq + h) * TA_D
+                                    : k + (((size_t)b * T + i0 + tok) * nkv + (h - nq)) * TA_D;
+            x1[u] = ok ? ld16(src + 8 * sub) : u32x4{0u, 0u, 0u, 0u};
+            x2[u] = ok ? ld16(src + 64 + 8 * sub) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = rr[u];
+            if (row >= rows) break;
+            const int tok = row / hh, h = row - tok * hh;
+            const int dep = sdep[tok];
+            const bool isq = h < nq;
+            bf16_t* dst = isq ? qr + (((size_t)b * Tpad + i0 + tok) * nq + h) * TA_D
+                              : kr + (((size_t)b * Tpad + i0 + tok) * nkv + (h - nq)) * TA_D;
+            u32x4 y1, y2;
+            if (dep < 0) {  // outside the tree: zeros, so that the context kernel's rows stay finite
+                y1 = u32x4{0u, 0u, 0u, 0u};
+                y2 = y1;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float o1[2], o2[2];
+#pragma unroll
+                    for (int hw = 0; hw < 2; ++hw) {
+                        const int pr = 8 * sub + 2 * j + hw;
+                        const float a1 = __uint_as_float(hw ? (x1[u][j] & 0xFFFF0000u) : (x1[u][j] << 16));
+                        const float a2 = __uint_as_float(hw ? (x2[u][j] & 0xFFFF0000u) : (x2[u][j] << 16));
+                        const float c = scs[dep][pr][0], s = scs[dep][pr][1];
+                        o1[hw] = a1 * c - a2 * s;
+                        o2[hw] = a2 * c + a1 * s;
+                    }
+                    y1[j] = f2bf2(o1[0], o1[1]);
+                    y2[j] = f2bf2(o2[0], o2[1]);
+                }
+            }
+            *(u32x4*)(dst + 8 * sub) = y1;
+            *(u32x4*)(dst + 64 + 8 * sub) = y2;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------------
+// tree_ctx_bf16: the context part (MFMA)
+// ------------------------------------------------------------------------------------------------------
+// Wave w serves query head kv_head * G + w % G for token tile super_tile * TW + w / G.
+template <int G>
+__global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __restrict__ qr, int Tpad, int tiles, int nq,
+                                                        int nkv, const bf16_t* __restrict__ kpool,
+                                                        const bf16_t* __restrict__ vpool, int n_pages,
+                                                        const int32_t* __restrict__ pt, int max_pages,
+                                                        const int32_t* __restrict__ ctx_len, int max_ctx,
+                                                        int chunk_tokens, int n_chunks, float* __restrict__ opart,
+                                                        float* __restrict__ mlpart, uint32_t* err) {
+    constexpr int D = TA_D;
+    constexpr int TW = TA_WAVES / G;
+    constexpr int NT = 64 * TA_WAVES;
+    constexpr int NPG = TA_SUB / 16;
+    constexpr int PIECES = NPG * 512;
+    constexpr int PPT = PIECES / NT;
+    constexpr int PPP = 512 / NT;
+    __shared__ __attribute__((aligned(16))) bf16_t sk[TA_SUB * TA_KLD];
+    __shared__ __attribute__((aligned(16))) bf16_t sv[NPG * D * TA_VLD];
+    __shared__ int spg[TA_MAX_PAGES];
+    // grid: KV head fastest, then super tile, chunk, request
+    const int stiles = (tiles + TW - 1) / TW;
+    int bid = blockIdx.x;
+    const int kvh = bid % nkv;
+    bid /= nkv;
+    const int stile = bid % stiles;
+    bid /= stiles;
+    const int c = bid % n_chunks;
+    const int b = bid / n_chunks;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int h = kvh * G + w % G;
+    const int tile = stile * TW + w / G;
+    const bool tile_ok = tile < tiles;  // the last super tile may reach past the tree
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+    const size_t page_elems = (size_t)16 * D;
+
+    const int pg0 = c * (chunk_tokens / 16);
+    for (int j = tid; j < chunk_tokens / 16; j += NT)
+        spg[j] = pg0 + j < max_pages ? pt[(size_t)b * max_pages + pg0 + j] : -1;
+    int ctx = ctx_len[b];
+    if (ctx > max_ctx || ctx < 0) ctx = ctx < 0 ? 0 : max_ctx;  // flagged by tree_prep
+    const int t0 = c * chunk_tokens;
+    const int t1 = min(ctx, t0 + chunk_tokens);
+
+    u32x4 pf[PPT];
+    uint32_t okmask = 0;
+    auto prefetch = [&](int ts) {
+        okmask = 0;
+#pragma unroll
+        for (int e = 0; e < NPG; ++e) {
+            const int tp = ts + 16 * e;
+            const int page = tp < t1 ? spg[(tp - t0) >> 4] : -1;
+            const bool ok = page >= 0 && page < n_pages;
+            const size_t ofs = ((size_t)(ok ? page : 0) * nkv + kvh) * page_elems;
+            okmask |= (ok ? 1u : 0u) << e;
+#pragma unroll
+            for (int u = 0; u < PPP; ++u) {
+                const int qq = tid + u * NT;
+                pf[e * PPP + u] = ld16((qq < 256 ? kpool : vpool) + ofs + (qq & 255) * 8);
+            }
+        }
+    };
+    auto stash = [&](int ts) {
+        okmask = __builtin_amdgcn_readfirstlane(okmask);
+#pragma unroll
+        for (int e = 0; e < NPG; ++e) {
+            const bool ok = (okmask >> e) & 1u;
+            const int nvalid = t1 - (ts + 16 * e);
+#pragma unroll
+            for (int u = 0; u < PPP; ++u) {
+                const int qq = tid + u * NT;
+                u32x4 v = pf[e * PPP + u];
+                if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+                if (qq < 256) {
+                    *(u32x4*)(sk + (e * 16 + (qq >> 4)) * TA_KLD + (qq & 15) * 8) = v;
+                } else {
+                    const int q2 = qq - 256;
+                    if (nvalid < 16) {  // values of slots past the last key may hold anything: zero them
+                        const int half = q2 & 1;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int s0 = half * 8 + 2 * j;
+                            const uint32_t m = (s0 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
+                            v[j] &= m;
+                        }
+                    }
+                    *(u32x4*)(sv + (e * D + (q2 >> 1)) * TA_VLD + (q2 & 1) * 8) = v;
+                }
+            }
+        }
+    };
+
+    // Q^T operand: lane supplies query row r of the tile (token tile * 16 + r), 8 d-values per k-step
+    u32x4 qf[4];
+    {
+        const bf16_t* qp = qr + (((size_t)b * Tpad + (tile_ok ? tile : 0) * 16 + r) * nq + h) * D + g * 8;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[s] = tile_ok ? ld16(qp + s * 32) : u32x4{0u, 0u, 0u, 0u};
+    }
+    f32x4 o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    __syncthreads();  // page ids in LDS
+    for (int j = tid; j < chunk_tokens / 16 && t0 + 16 * j < t1; j += NT) {
+        if ((t0 >> 4) + j >= max_pages) set_err(err, DFLASH_DEVERR_POS);
+        else if (spg[j] < 0 || spg[j] >= n_pages) set_err(err, DFLASH_DEVERR_PAGE);
+    }
+    if (t0 < t1) prefetch(t0);
+    for (int ts = t0; ts < t1; ts += TA_SUB) {
+        __syncthreads();
+        stash(ts);
+        __syncthreads();
+        if (ts + TA_SUB < t1) prefetch(ts + TA_SUB);
+        f32x4 sa[NPG];
+#pragma unroll
+        for (int e = 0; e < NPG; ++e) sa[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < NPG; ++e) sa[e] = mfma16(ld16(sk + (e * 16 + r) * TA_KLD + g * 8 + s * 32), qf[s], sa[e]);
+        float x[NPG][4];
+#pragma unroll
+        for (int e = 0; e < NPG; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[e][i] = sa[e][i] * scale_log2;
+        if (ts + TA_SUB > t1) {
+            const int nk = t1 - ts;
+#pragma unroll
+            for (int e = 0; e < NPG; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[e][i] = 16 * e + 4 * g + i < nk ? x[e][i] : -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < NPG; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[e][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+        m_run = m_new;
+        float p[NPG][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < NPG; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[e][i] = __builtin_amdgcn_exp2f(x[e][i] - m_ref);
+                psum += p[e][i];
+            }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            o[dt][0] *= alpha; o[dt][1] *= alpha; o[dt][2] *= alpha; o[dt][3] *= alpha;
+        }
+        // O^T += V^T P^T over 32-key slices, P as bfloat16
+#pragma unroll
+        for (int hk = 0; hk < NPG / 2; ++hk) {
+            if (ts + 32 * hk >= t1) break;
+            u32x4 pb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                pb[j] = f2bf2(p[2 * hk + (j >> 1)][2 * (j & 1)], p[2 * hk + (j >> 1)][2 * (j & 1) + 1]);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const int d = dt * 16 + r;
+                const u32x2 va = *(const u32x2*)(sv + ((2 * hk) * D + d) * TA_VLD + 4 * g);
+                const u32x2 vb = *(const u32x2*)(sv + ((2 * hk + 1) * D + d) * TA_VLD + 4 * g);
+                o[dt] = mfma16(u32x4{va[0], va[1], vb[0], vb[1]}, pb, o[dt]);
+            }
+        }
+    }
+    float l_tot = l_run;
+    l_tot += __shfl_xor(l_tot, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (!tile_ok) return;
+    const size_t base = ((((size_t)b * tiles + tile) * nq + h) * n_chunks + c) * 16 + r;
+    float* op = opart + base * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+        *(float4*)(op + dt * 16 + 4 * g) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (g == 0) {
+        mlpart[base * 2 + 0] = m_run;
+        mlpart[base * 2 + 1] = l_tot;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------------
+// tree_merge: ancestors + context partials -> output
+// ------------------------------------------------------------------------------------------------------
+// Wave layout: lane = 16 * hs + dl: query head hs of the current group of four, eight d-values at 8 dl.
+__global__ __launch_bounds__(256) void tree_merge(int T, int Tpad, int tiles, int nq, int nkv,
+                                                  const int32_t* __restrict__ n_tokens,
+                                                  const bf16_t* __restrict__ qr, const bf16_t* __restrict__ kr,
+                                                  const bf16_t* __restrict__ v, const int32_t* __restrict__ anc,
+                                                  const float* __restrict__ opart, const float* __restrict__ mlpart,
+                                                  int n_chunks, bf16_t* __restrict__ out) {
+    const int b = blockIdx.y;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, KV head)
+    const int lane = threadIdx.x & 63;
+    const int i = item / nkv, kvh = item % nkv;
+    if (i >= T || i >= n_tokens[b]) return;
+    const int G = nq / nkv;
+    const int hs = lane >> 4, dl = lane & 15;
+    const int32_t* a = anc + ((size_t)b * Tpad + i) * TREE_MAX_ANC;
+    const int depth = a[0];
+    if (depth < 0) return;
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)TA_D);
+    const int tile = i >> 4, row = i & 15;
+    for (int hg = 0; hg < G; hg += 4) {
+        const int hq = hg + hs;
+        const bool live = hq < G;
+        const int h = kvh * G + (live ? hq : 0);
+        // query
+        float qv[8];
+        {
+            const u32x4 u = ld16(qr + (((size_t)b * Tpad + i) * nq + h) * TA_D + 8 * dl);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                qv[2 * j] = __uint_as_float(u[j] << 16);
+                qv[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+            }
+        }
+        // context partials (chunk order), in the log2 domain
+        float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+        const size_t cbase = (((size_t)b * tiles + tile) * nq + h) * n_chunks;
+        for (int c0 = 0; c0 < n_chunks; c0 += 4) {  // four chunks' loads in flight at a time
+            float2 mlc[4];
+            float4 oc0[4], oc1[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const size_t base = (cbase + min(c0 + u, n_chunks - 1)) * 16 + row;
+                mlc[u] = *(const float2*)(mlpart + base * 2);
+                oc0[u] = *(const float4*)(opart + base * TA_D + 8 * dl);
+                oc1[u] = *(const float4*)(opart + base * TA_D + 8 * dl + 4);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float mc = mlc[u].x, lc = mlc[u].y;
+                if (c0 + u >= n_chunks || mc == -INFINITY) continue;
+                const float mn = fmaxf(m, mc);
+                const float sa = __builtin_amdgcn_exp2f(m - mn), sb = __builtin_amdgcn_exp2f(mc - mn);
+                l = l * sa + lc * sb;
+                const float oc[8] = {oc0[u].x, oc0[u].y, oc0[u].z, oc0[u].w, oc1[u].x, oc1[u].y, oc1[u].z, oc1[u].w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[j] = acc[j] * sa + oc[j] * sb;
+                m = mn;
+            }
+        }
+        // the token's ancestors and itself, root first: lane e holds the e-th, four keys in flight at a time
+        const int my_anc = lane <= depth ? a[1 + lane] : 0;
+        for (int e0 = 0; e0 <= depth; e0 += 4) {
+            u32x4 ku[4], vu[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int tok = __shfl(my_anc, min(e0 + u, depth), 64);
+                ku[u] = ld16(kr + (((size_t)b * Tpad + tok) * nkv + kvh) * TA_D + 8 * dl);
+                vu[u] = ld16(v + (((size_t)b * T + tok) * nkv + kvh) * TA_D + 8 * dl);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (e0 + u > depth) break;  // uniform
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s += qv[2 * j] * __uint_as_float(ku[u][j] << 16);
+                    s += qv[2 * j + 1] * __uint_as_float(ku[u][j] & 0xFFFF0000u);
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);  // within the head's 16 lanes
+                s *= scale_log2;
+                const float mn = fmaxf(m, s);
+                const float sa = __builtin_amdgcn_exp2f(m - mn), sb = __builtin_amdgcn_exp2f(s - mn);
+                l = l * sa + sb;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[2 * j] = acc[2 * j] * sa + sb * __uint_as_float(vu[u][j] << 16);
+                    acc[2 * j + 1] = acc[2 * j + 1] * sa + sb * __uint_as_float(vu[u][j] & 0xFFFF0000u);
+                }
+                m = mn;
+            }
+        }
+        if (live) {
+            const float inv = 1.f / l;
+            u32x4 ov;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ov[j] = f2bf2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+            *(u32x4*)(out + (((size_t)b * T + i) * nq + h) * TA_D + 8 * dl) = ov;
+        }
+    }
+}
+
+hipError_t launch_tree_attention(const TreePlan& p, int batch, int T, const int32_t* n_tokens, const int32_t* parent,
+                                 int nq, int nkv, const void* q, const void* k, const void* v, const void* kpool,
+                                 const void* vpool, int n_pages, const int32_t* pt, int max_pages,
+                                 const int32_t* ctx_len, int max_ctx, const RopeFreq& rf, void* out, void* ws,
+                                 hipStream_t st) {
+    char* W = (char*)ws;
+    uint32_t* err = (uint32_t*)W;
+    bf16_t* qr = (bf16_t*)(W + p.q_off);
+    bf16_t* kr = (bf16_t*)(W + p.k_off);
+    int32_t* anc = (int32_t*)(W + p.anc_off);
+    float* opart = (float*)(W + p.o_off);
+    float* ml = (float*)(W + p.ml_off);
+    const int Tpad = p.tiles * 16;
+    hipError_t e = launch_clear_err(err, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tree_prep, dim3(p.tiles, batch), dim3(256), 0, st, T, n_tokens, parent, nq, nkv,
+                       (const bf16_t*)q, (const bf16_t*)k, ctx_len, max_ctx, rf, qr, kr, anc, Tpad, err);
+    if (p.chunks > 0) {
+        const dim3 grid(nkv * p.stiles * p.chunks * batch);
+        const int G = nq / nkv;
+#define TA_LAUNCH(GG)                                                                                          \
+    hipLaunchKernelGGL((tree_ctx_bf16<GG>), grid, dim3(64 * TA_WAVES), 0, st, qr, Tpad, p.tiles, nq, nkv,        \
+                       (const bf16_t*)kpool, (const bf16_t*)vpool, n_pages, pt, max_pages, ctx_len, max_ctx,    \
+                       p.chunk_tokens, p.chunks, opart, ml, err)
+        if (G == 1) TA_LAUNCH(1);
+        else if (G == 2) TA_LAUNCH(2);
+        else if (G == 4) TA_LAUNCH(4);
+        else TA_LAUNCH(8);
+#undef TA_LAUNCH
+    }
+    hipLaunchKernelGGL(tree_merge, dim3((T * nkv + 3) / 4, batch), dim3(256), 0, st, T, Tpad, p.tiles, nq, nkv,
+                       n_tokens, qr, kr, (const bf16_t*)v, anc, opart, ml, p.chunks, (bf16_t*)out);
+    return hipGetLastError();
+}
+
+}  // namespace df

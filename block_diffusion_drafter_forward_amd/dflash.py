@@ -22,7 +22,7 @@ DFLASH_E_UNSUPPORTED = -4
 DFLASH_E_HIP = -5
 DFLASH_F32 = 0
 DFLASH_BF16 = 1
-DEVERR_PAGE, DEVERR_POS, DEVERR_TOKEN, DEVERR_ROWS = 1, 2, 4, 8
+DEVERR_PAGE, DEVERR_POS, DEVERR_TOKEN, DEVERR_ROWS, DEVERR_TREE = 1, 2, 4, 8, 16
 
 
 class dflash_config(ctypes.Structure):
@@ -98,6 +98,13 @@ _SIGS = {
     "dflash_ddtree_walk": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p]),
+    "dflash_tree_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 6),
+    "dflash_tree_attention": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_size_t, ctypes.c_void_p]),
     "dflash_linear_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "dflash_linear": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -363,6 +370,33 @@ def verify_sample(draft, q_logits, p_logits, seed: int, tau, next_token, ws, str
                                q_logits.stride(0) if n else 0, p_logits.data_ptr(), p_logits.stride(0), seed,
                                tau.data_ptr(), next_token.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                                _stream(stream)), "dflash_verify_sample")
+
+
+def dflash_tree_attention_workspace_bytes(batch, max_tokens, n_q_heads, n_kv_heads, head_dim, max_ctx) -> int:
+    return lib().dflash_tree_attention_workspace_bytes(batch, max_tokens, n_q_heads, n_kv_heads, head_dim, max_ctx)
+
+
+def dflash_tree_attention(batch, max_tokens, n_tokens, parent, n_q_heads, n_kv_heads, head_dim, q, k, v, k_pages,
+                          v_pages, n_pages, page_table, max_pages, ctx_len, max_ctx, rope_theta, out, ws, ws_bytes,
+                          stream) -> int:
+    return lib().dflash_tree_attention(batch, max_tokens, n_tokens, parent, n_q_heads, n_kv_heads, head_dim, q, k,
+                                       v, k_pages, v_pages, n_pages, page_table, max_pages, ctx_len, max_ctx,
+                                       rope_theta, out, ws, ws_bytes, stream)
+
+
+def tree_attention(n_tokens, parent, q, k, v, k_pages, v_pages, page_table, ctx_len, max_ctx: int,
+                   rope_theta: float, out, ws, stream=None) -> None:
+    """Tree attention over CUDA tensors: n_tokens int32 [B], parent int32 [B, T], q bf16 [B, T, n_q, 128],
+    k / v bf16 [B, T, n_kv, 128], k_pages bf16 [P, n_kv, 16, 128], v_pages bf16 [P, n_kv, 128, 16], page_table
+    int32 [B, max_pages], ctx_len int32 [B], out bf16 [B, T, n_q, 128], ws a 256-byte-aligned uint8 tensor."""
+    B, T, nq, d = q.shape
+    nkv = k.shape[2]
+    check(dflash_tree_attention(B, T, n_tokens.data_ptr(), parent.data_ptr(), nq, nkv, d, q.data_ptr(),
+                                k.data_ptr(), v.data_ptr(), _ptr(k_pages), _ptr(v_pages),
+                                k_pages.shape[0] if k_pages is not None else 0, _ptr(page_table),
+                                page_table.shape[1] if page_table is not None else 0, ctx_len.data_ptr(), max_ctx,
+                                rope_theta, out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
+          "dflash_tree_attention")
 
 
 def make_kv(kpool, vpool, n_pages: int) -> dflash_kv:

@@ -18,6 +18,9 @@
  *   dflash_draft_block_sample, dflash_verify_sample
  *                       the same pass and its verification at temperature 1 (section 3.4.4 "Single forward
  *                       pass prediction" and "Integration with verification").
+ *   dflash_topk_logprobs, dflash_ddtree_build, dflash_ddtree_walk, dflash_tree_attention
+ *                       DDTree on the drafter's marginals and the tree attention that verifies its trees
+ *                       ("Accelerating Speculative Decoding with Block Diffusion Draft Trees", §3.4.4-§3.4.5).
  *
  * Conventions
  *   - Every pointer marked "device" is GPU memory owned by the caller; the library never allocates, frees
@@ -61,6 +64,7 @@ extern "C" {
 #define DFLASH_DEVERR_POS 2u      /* a position fell beyond max_pages * page_size, or ctx_len > max_ctx    */
 #define DFLASH_DEVERR_TOKEN 4u    /* a block token id outside [0, vocab): embedding row 0 used instead    */
 #define DFLASH_DEVERR_ROWS 8u     /* inject row offsets not non-decreasing within [0, n_rows]              */
+#define DFLASH_DEVERR_TREE 16u    /* a tree parent link not pointing to an earlier token, or depth > 62   */
 
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
@@ -256,6 +260,37 @@ int dflash_ddtree_build(int batch, int depth, int k, const float *logprobs, cons
 int dflash_ddtree_walk(int batch, int budget, int max_accept, const int32_t *node_token, const int32_t *node_parent,
                        const int32_t *n_nodes, const int32_t *target_next, int32_t *accept_len,
                        int32_t *accept_nodes, int32_t *bonus, void *stream);
+
+/* ---- Tree attention (the verification side of DDTree: "Accelerating Speculative Decoding with Block
+ * Diffusion Draft Trees", §3.4.5 "Verification: Tree Attention and the Verifier Walk") ---------------------
+ * One attention layer of a target model over a flattened draft tree.  Tree token 0 is the root (the bonus
+ * token); token i > 0 is a tree node whose parent token parent[i] precedes it (0 <= parent[i] < i), as in
+ * the pop order of dflash_ddtree_build (token i = node i - 1, parent token = node_parent + 1).  A token's
+ * position id is its depth (root 0), i.e. absolute position ctx_len + depth.  Each token attends to every
+ * cached context key and, in the tree, only to its ancestors and itself.
+ *   n_tokens     device int32 [batch]: tree tokens of each request (root included), <= max_tokens; later
+ *                rows are neither read nor written
+ *   parent       device int32 [batch][max_tokens]; parent[0] is ignored; depth <= 62
+ *   q            device bfloat16 [batch][max_tokens][n_q_heads][128], before RoPE
+ *   k, v         device bfloat16 [batch][max_tokens][n_kv_heads][128], k before RoPE
+ *   k_pages      device bfloat16 [n_pages][n_kv_heads][16][128]: one layer's cached context keys (rotated
+ *                at their own positions); v_pages [n_pages][n_kv_heads][128][16] (values transposed per page)
+ *   page_table   device int32 [batch][max_pages]; position p of request r in page page_table[r][p / 16],
+ *                slot p % 16
+ *   ctx_len      device int32 [batch], each <= max_ctx (host bound; 0 = no context)
+ *   rope_theta   rotary base (0: no rotation); q and k are rotated in float32 and rounded to bfloat16
+ *   out          device bfloat16 [batch][max_tokens][n_q_heads][128]
+ * Query head h reads KV head h / (n_q_heads / n_kv_heads); that ratio is 1, 2, 4 or 8; head_dim 128;
+ * max_tokens <= 2048.  q, k, v, out and the pages 16-byte aligned; ws 256-byte aligned, at least
+ * dflash_tree_attention_workspace_bytes(...) bytes; its first 4 bytes are the device error word
+ * (DFLASH_DEVERR_PAGE / _POS / _TREE), cleared by every call.                                             */
+size_t dflash_tree_attention_workspace_bytes(int batch, int max_tokens, int n_q_heads, int n_kv_heads,
+                                             int head_dim, int max_ctx);
+int dflash_tree_attention(int batch, int max_tokens, const int32_t *n_tokens, const int32_t *parent,
+                          int n_q_heads, int n_kv_heads, int head_dim, const void *q, const void *k, const void *v,
+                          const void *k_pages, const void *v_pages, int n_pages, const int32_t *page_table,
+                          int max_pages, const int32_t *ctx_len, int max_ctx, float rope_theta, void *out, void *ws,
+                          size_t ws_bytes, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none).                                */
 const char *dflash_last_error(void);

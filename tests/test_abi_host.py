@@ -307,3 +307,31 @@ def test_verify_sample_validation(D, over, code):
     assert D.dflash_verify_sample(a["batch"], a["n_draft"], a["vocab"], a["draft"], a["dstride"], a["q"], a["q_req"],
                                   a["p"], a["p_req"], 7, a["tau"], a["nxt"], a["ws"], a["ws_bytes"], None) == code
     assert D.dflash_last_error()
+
+
+def test_tree_attention_workspace_size(D):
+    a = D.dflash_tree_attention_workspace_bytes(1, 1025, 32, 8, 128, 4096)
+    assert a > 1025 * 40 * 128 * 2 and a % 256 == 0
+    assert D.dflash_tree_attention_workspace_bytes(1, 1025, 32, 8, 128, 0) < a
+    assert D.dflash_tree_attention_workspace_bytes(1, 2049, 32, 8, 128, 100) == 0
+    assert D.dflash_tree_attention_workspace_bytes(1, 16, 32, 8, 64, 100) == 0
+    assert D.dflash_tree_attention_workspace_bytes(1, 16, 24, 8, 128, 100) == 0
+    assert D.dflash_tree_attention_workspace_bytes(0, 16, 32, 8, 128, 100) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(batch=0), -1), (dict(T=0), -1), (dict(T=2049), -1), (dict(d=64), -4), (dict(nq=24), -4), (dict(nq=20), -1),
+    (dict(nq=48, nkv=3), -4), (dict(max_ctx=-1), -1), (dict(n_tok=None), -1), (dict(parent=None), -1),
+    (dict(q=None), -1), (dict(out=None), -1), (dict(kp=None), -1), (dict(pt=None), -1), (dict(max_pages=0), -1),
+    (dict(max_ctx=8 * 16 + 1), -3), (dict(theta=-1.0), -1), (dict(q=0x1008), -1), (dict(ws_bytes=100), -3),
+    (dict(ws=0x100010), -1),
+])
+def test_tree_attention_validation(D, over, code):
+    a = dict(batch=1, T=64, n_tok=0x10, parent=0x20, nq=32, nkv=8, d=128, q=0x1000, k=0x2000, v=0x3000,
+             kp=0x4000, vp=0x5000, n_pages=8, pt=0x6000, max_pages=8, ctx=0x7000, max_ctx=100, theta=1e6,
+             out=0x8000, ws=0x100000, ws_bytes=1 << 30)
+    a.update(over)
+    assert D.dflash_tree_attention(a["batch"], a["T"], a["n_tok"], a["parent"], a["nq"], a["nkv"], a["d"], a["q"],
+                                   a["k"], a["v"], a["kp"], a["vp"], a["n_pages"], a["pt"], a["max_pages"], a["ctx"],
+                                   a["max_ctx"], a["theta"], a["out"], a["ws"], a["ws_bytes"], None) == code
+    assert D.dflash_last_error()
