@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -46,14 +47,31 @@ struct ProfEntry {
     hipEvent_t start, stop;
 };
 
-// Element offsets of every projection matrix in the packed weight store of a bfloat16 drafter (layout of one
-// matrix: gemm_core.h).  Matrices that one GEMM stacks along N are adjacent: [wq; wk; wv], [w_gate; w_up],
-// and [uk; uv] of consecutive layers.
+// Element offsets of every packed matrix in the store of a bfloat16 drafter (layout: gemm_core.h).  Matrices
+// that one GEMM stacks along N are packed as one matrix: [wq; wk; wv], [w_gate; w_up], and the [uk; uv] of the
+// layers one inject GEMM covers (MAX_LAYERS_PER_KV_GEMM at a time).  The store lists the drafter pass's
+// matrices in the order the pass reads them.
+#define MAX_LAYERS_PER_KV_GEMM (DF_MAX_SEG / 2)
 struct PackLayout {
     std::vector<size_t> qkv, o, gu, down;  // per layer
     size_t kv = 0, kv_stride = 0;          // layer l's [uk; uv] at kv + l * kv_stride
     size_t fc = 0, lm = 0, total = 0;
 };
+
+// Row segments of matrices stacked along N (each {rows pointer, row count}).
+static Segs stack_rows(std::initializer_list<std::pair<const void*, int>> parts) {
+    Segs s{};
+    int n = 0, i = 0;
+    for (const auto& p : parts) {
+        s.ptr[i] = p.first;
+        s.start[i] = n;
+        n += p.second;
+        ++i;
+    }
+    s.start[i] = n;
+    s.n = i;
+    return s;
+}
 
 static PackLayout pack_layout(const dflash_config& c) {
     PackLayout pl;
@@ -61,12 +79,12 @@ static PackLayout pack_layout(const dflash_config& c) {
     size_t off = 0;
     auto take = [&](size_t n) { size_t o = off; off += n; return o; };
     for (int l = 0; l < c.n_layers; ++l) {
-        pl.qkv.push_back(take(packed_elems(qd, H) + 2 * packed_elems(kvd, H)));
+        pl.qkv.push_back(take(packed_elems(qd + 2 * kvd, H)));
         pl.o.push_back(take(packed_elems(H, qd)));
-        pl.gu.push_back(take(2 * packed_elems(F, H)));
+        pl.gu.push_back(take(packed_elems(2 * F, H)));
         pl.down.push_back(take(packed_elems(H, F)));
     }
-    pl.kv_stride = 2 * packed_elems(kvd, H);
+    pl.kv_stride = packed_elems(2 * kvd, H);  // a group of n layers: n * kv_stride (2 kvd is a multiple of 64)
     pl.kv = take((size_t)c.n_layers * pl.kv_stride);
     pl.fc = take(packed_elems(H, c.feat_dim));
     pl.lm = take(packed_elems(c.vocab, H));
@@ -170,20 +188,29 @@ extern "C" int dflash_pack_weights(dflash_handle* h, void* dst, size_t dst_bytes
     bf16_t* P = (bf16_t*)dst;
     const int H = c.hidden, F = c.ffn, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
     const PackLayout& pl = h->pl;
+    if ((2 * kvd) % 64) return fail(DFLASH_E_UNSUPPORTED, "2 * n_kv_heads * head_dim must be a multiple of 64");
     for (int l = 0; l < c.n_layers; ++l) {
         const dflash_layer_weights& w = h->layers[l];
-        HIP_TRY(launch_pack(w.wq, qd, H, P + pl.qkv[l], st));
-        HIP_TRY(launch_pack(w.wk, kvd, H, P + pl.qkv[l] + packed_elems(qd, H), st));
-        HIP_TRY(launch_pack(w.wv, kvd, H, P + pl.qkv[l] + packed_elems(qd, H) + packed_elems(kvd, H), st));
-        HIP_TRY(launch_pack(w.wo, H, qd, P + pl.o[l], st));
-        HIP_TRY(launch_pack(w.w_gate, F, H, P + pl.gu[l], st));
-        HIP_TRY(launch_pack(w.w_up, F, H, P + pl.gu[l] + packed_elems(F, H), st));
-        HIP_TRY(launch_pack(w.w_down, H, F, P + pl.down[l], st));
-        HIP_TRY(launch_pack(w.uk, kvd, H, P + pl.kv + l * pl.kv_stride, st));
-        HIP_TRY(launch_pack(w.uv, kvd, H, P + pl.kv + l * pl.kv_stride + packed_elems(kvd, H), st));
+        HIP_TRY(launch_pack(stack_rows({{w.wq, qd}, {w.wk, kvd}, {w.wv, kvd}}), qd + 2 * kvd, H, P + pl.qkv[l], st));
+        HIP_TRY(launch_pack(stack_rows({{w.wo, H}}), H, qd, P + pl.o[l], st));
+        HIP_TRY(launch_pack(stack_rows({{w.w_gate, F}, {w.w_up, F}}), 2 * F, H, P + pl.gu[l], st));
+        HIP_TRY(launch_pack(stack_rows({{w.w_down, H}}), H, F, P + pl.down[l], st));
     }
-    HIP_TRY(launch_pack(h->w.fc_w, H, c.feat_dim, P + pl.fc, st));
-    HIP_TRY(launch_pack(h->w.lm_head, c.vocab, H, P + pl.lm, st));
+    for (int l0 = 0; l0 < c.n_layers; l0 += MAX_LAYERS_PER_KV_GEMM) {  // the groups dflash_inject_ctx multiplies
+        const int nl = std::min(MAX_LAYERS_PER_KV_GEMM, c.n_layers - l0);
+        Segs s{};
+        for (int i = 0; i < nl; ++i) {
+            s.ptr[2 * i] = h->layers[l0 + i].uk;
+            s.ptr[2 * i + 1] = h->layers[l0 + i].uv;
+            s.start[2 * i] = 2 * i * kvd;
+            s.start[2 * i + 1] = (2 * i + 1) * kvd;
+        }
+        s.start[2 * nl] = 2 * nl * kvd;
+        s.n = 2 * nl;
+        HIP_TRY(launch_pack(s, 2 * nl * kvd, H, P + pl.kv + l0 * pl.kv_stride, st));
+    }
+    HIP_TRY(launch_pack(stack_rows({{h->w.fc_w, H}}), H, c.feat_dim, P + pl.fc, st));
+    HIP_TRY(launch_pack(stack_rows({{h->w.lm_head, c.vocab}}), c.vocab, H, P + pl.lm, st));
     h->packed = P;
     return DFLASH_OK;
 }
@@ -337,7 +364,6 @@ extern "C" size_t dflash_draft_workspace_bytes(const dflash_handle* h, int max_b
 }
 
 #define INJECT_ROWS 4096  // rows per internal chunk of dflash_inject_ctx (bounds the workspace)
-#define MAX_LAYERS_PER_KV_GEMM (DF_MAX_SEG / 2)
 
 struct InjectPlan {
     int rows;
@@ -727,7 +753,7 @@ extern "C" int dflash_linear(int dtype, int M, int N, int K, const void* x, int6
     hipStream_t st = (hipStream_t)stream;
     if (dtype == DFLASH_BF16) {
         void* wpk = (char*)ws + linear_part_bytes(dtype, M, N, K);
-        HIP_TRY(launch_pack(w, N, K, wpk, st));
+        HIP_TRY(launch_pack(stack_rows({{w, N}}), N, K, wpk, st));
         HIP_TRY(launch_gemm_bf16(p, x, (int)ldx, 0, M, wpk, N, K, (float*)ws, st));
     } else {
         HIP_TRY(launch_gemm_f32((const float*)x, (int)ldx, M, segs1(w, N), N, K, (float*)ws, st));

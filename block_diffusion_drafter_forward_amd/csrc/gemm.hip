@@ -17,28 +17,30 @@ namespace df {
 // ------------------------------------------------------------------------------------------------------
 // weight packing (once per weight matrix, into the fragment-major layout of gemm_core.h)
 // ------------------------------------------------------------------------------------------------------
-// One thread per 16-byte lane piece of the packed image: piece c is lane c % 64 of fragment c / 64.
-__global__ __launch_bounds__(256) void pack_frag(const bf16_t* __restrict__ src, int N, int K, bf16_t* __restrict__ dst,
-                                                 size_t pieces) {
-    const int KS = K / 32;
+// One thread per 16-byte lane piece of the packed image: piece c is lane c % 64 of fragment c / 64, whose
+// (n-tile, k-step) inverts the chunk-major fragment index.  Row n of the stacked matrix is row n - start[i]
+// of segment i; rows past N are zero.
+__global__ __launch_bounds__(256) void pack_frag(Segs src, int N, int K, bf16_t* __restrict__ dst, size_t pieces) {
+    const size_t G = packed_groups(N);
     for (size_t c = (size_t)blockIdx.x * 256 + threadIdx.x; c < pieces; c += (size_t)gridDim.x * 256) {
         const size_t f = c >> 6;
         const int l = (int)(c & 63);
-        const size_t t = f / KS;
-        const int s = (int)(f % KS);
+        const size_t rest = f >> 5;  // chunk * G + group
+        const size_t t = (rest % G) * 4 + ((f >> 3) & 3);
+        const int s = (int)(rest / G) * 8 + (int)(f & 7);
         const size_t n = t * 16 + (l & 15);
         const int k = s * 32 + (l >> 4) * 8;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (n < (size_t)N) v = ld16(src + n * K + k);
+        if (n < (size_t)N) v = ld16((const bf16_t*)seg_row(src, (int)n, K, 2) + k);
         *(u32x4*)(dst + c * 8) = v;
     }
 }
 
-hipError_t launch_pack(const void* src, int N, int K, void* dst, hipStream_t st) {
+hipError_t launch_pack(const Segs& src, int N, int K, void* dst, hipStream_t st) {
     const size_t pieces = packed_elems(N, K) / 8;
     const size_t blocks = (pieces + 255) / 256;
-    hipLaunchKernelGGL(pack_frag, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, st,
-                       (const bf16_t*)src, N, K, (bf16_t*)dst, pieces);
+    hipLaunchKernelGGL(pack_frag, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, st, src, N, K,
+                       (bf16_t*)dst, pieces);
     return hipGetLastError();
 }
 
@@ -65,12 +67,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict
     const int s = blockIdx.y;
     const int kb = s * 4 * kpw + wave * kpw;
     const int ke = min(K, kb + kpw);
-    const int KS = K / 32, tiles = (N + 15) / 16;
-
-    const bf16_t* wt[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-        wt[nt] = wp + (size_t)min(blockIdx.x * NT + nt, tiles - 1) * KS * DF_FRAG + lane * 8;
+    // this workgroup's four n-tiles are group blockIdx.x of the chunk-major packed matrix: per k-chunk one
+    // contiguous 32 KB block, n-tile nt at fragment 8 nt of it
+    const size_t chunk_stride = packed_groups(N) * 32 * DF_FRAG;
+    const bf16_t* wt = wp + (size_t)blockIdx.x * 32 * DF_FRAG + lane * 8;
     const bf16_t* xrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) xrow[mt] = x + (size_t)min(mt * 16 + r, M - 1) * ldx + g * 8;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) wf[nt][j] = ld16_nt(wt[nt] + (size_t)(kc / 32 + j) * DF_FRAG);
+            for (int nt = 0; nt < NT; ++nt) wf[nt][j] = ld16_nt(wt + (size_t)(kc / 256) * chunk_stride + (nt * 8 + j) * DF_FRAG);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 xf[mt][j] = ld16(xrow[mt] + kc + j * 32);

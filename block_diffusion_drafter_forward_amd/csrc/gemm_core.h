@@ -7,14 +7,23 @@
 // ------------------------------------------------------------------------------------------------------
 // packed ("fragment-major") weights
 // ------------------------------------------------------------------------------------------------------
-// A bfloat16 matrix W[N][K] (K a multiple of 32) is stored as ceil(N / 16) x (K / 32) fragments of 16 rows x
-// 32 k-values, fragment (t, s) at element offset (t * (K / 32) + s) * 512.  Inside a fragment, lane l of a
-// wave owns the 16 bytes at offset 8 l: row 16 t + (l % 16), k = 32 s + 8 (l / 16) .. + 7 -- exactly the
-// A operand of one 16x16x32 MFMA, so a wave fetches a whole fragment with one fully coalesced 1 KB load.
-// Rows past N (the last fragment row of a ragged N) are zero.  Stacking matrices along N (q/k/v, gate/up,
-// the per-layer K/V projections) is concatenation of their packed images when every N is a multiple of 16.
+// A bfloat16 matrix W[N][K] (K a multiple of 256) is stored as fragments of 16 rows x 32 k-values.  Inside a
+// fragment, lane l of a wave owns the 16 bytes at offset 8 l: row 16 t + (l % 16), k = 32 s + 8 (l / 16) ..
+// + 7 -- exactly the A operand of one 16x16x32 MFMA, so a wave fetches a whole fragment with one fully
+// coalesced 1 KB load.  The fragments are ordered chunk-major: the n-tiles are taken four at a time (group
+// g = t / 4 of 64 rows; N is padded with zero rows to whole groups) and K in chunks of 256 (eight
+// fragments), and fragment (t, s) sits at fragment index ((s / 8) * G + t / 4) * 32 + (t % 4) * 8 + s % 8,
+// G = ceil(N / 64).  The 32 KB one wave streams per k-chunk (four n-tiles x eight fragments) is then one
+// contiguous block, and the waves of neighbouring workgroups at the same chunk read neighbouring blocks:
+// measured on MI355X, this streams 6-37% faster than an n-tile-major order (the gain is largest for the
+// smallest matrices).  Matrices that one GEMM stacks along N are packed together as one matrix.
 #define DF_FRAG 512  // elements per fragment
-__host__ __device__ inline size_t packed_elems(int N, int K) { return (size_t)((N + 15) / 16) * (size_t)K * 16; }
+__host__ __device__ inline size_t packed_groups(int N) { return (size_t)((N + 63) / 64); }
+__host__ __device__ inline size_t packed_elems(int N, int K) { return packed_groups(N) * 64 * (size_t)K; }
+// fragment index of n-tile t, k-step s in a matrix of G groups
+__host__ __device__ inline size_t frag_index(size_t t, int s, size_t G) {
+    return (((size_t)(s >> 3) * G + (t >> 2)) * 4 + (t & 3)) * 8 + (s & 7);
+}
 
 // ------------------------------------------------------------------------------------------------------
 // LDS-tiled MFMA GEMM (bfloat16) for large M
@@ -40,17 +49,19 @@ static __device__ __forceinline__ void tiled_mainloop(const bf16_t* __restrict__
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int wn = wave >> 1, wm = wave & 1;
-    const int KS = K / 32, tiles = (N + 15) / 16;
+    const size_t G = packed_groups(N);
     // global -> register staging: each thread moves 4 pieces of 16 bytes of W and of x per k-tile.  Weight
-    // piece c = tid + 256 i is lane (c % 64) of fragment c / 64 = (n-tile, k-step) = ((c / 64) / 2, (c / 64) % 2).
+    // piece c = tid + 256 i is lane (c % 64) of fragment c / 64 = (n-tile, k-step) = ((c / 64) / 2, (c / 64) % 2)
+    // of the tile; n-tiles past the padded groups read the last padded tile (their columns are discarded).
     const bf16_t* wsrc[4];
     const bf16_t* xsrc[4];
-    int lrow[4], lcol[4];
+    int lrow[4], lcol[4], wks[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int c = tid + 256 * i, f = c >> 6;
-        const int t = min(n0 / 16 + (f >> 1), tiles - 1);
-        wsrc[i] = wp + ((size_t)t * KS + (f & 1)) * DF_FRAG + (c & 63) * 8;
+        const size_t t = min((size_t)(n0 / 16 + (f >> 1)), 4 * G - 1);
+        wsrc[i] = wp + frag_index(t, 0, G) * DF_FRAG + (c & 63) * 8;  // k-step 0; add the k-step part below
+        wks[i] = f & 1;
         lrow[i] = c >> 3;
         lcol[i] = (c & 7) * 8;
         xsrc[i] = x + (size_t)min(m0 + lrow[i], M - 1) * ldx + lcol[i];
@@ -64,7 +75,7 @@ static __device__ __forceinline__ void tiled_mainloop(const bf16_t* __restrict__
     if (kb < ke) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pw[i] = ld16_nt(wsrc[i] + (size_t)(kb / 32) * DF_FRAG);
+            pw[i] = ld16_nt(wsrc[i] + frag_index(0, kb / 32 + wks[i], G) * DF_FRAG);
 #pragma unroll
             for (int pl = 0; pl < XP; ++pl) px[pl][i] = ld16(xsrc[i] + pl * xplane + kb);
         }
@@ -81,7 +92,7 @@ static __device__ __forceinline__ void tiled_mainloop(const bf16_t* __restrict__
         if (k + TL_BK < ke) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pw[i] = ld16_nt(wsrc[i] + (size_t)((k + TL_BK) / 32) * DF_FRAG);
+                pw[i] = ld16_nt(wsrc[i] + frag_index(0, (k + TL_BK) / 32 + wks[i], G) * DF_FRAG);
 #pragma unroll
                 for (int pl = 0; pl < XP; ++pl) px[pl][i] = ld16(xsrc[i] + pl * xplane + k + TL_BK);
             }

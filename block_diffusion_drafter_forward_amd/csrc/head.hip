@@ -184,10 +184,9 @@ __global__ __launch_bounds__(64 * NW) void lm_head_bf16(const bf16_t* __restrict
     const int chunks = K / 256;
     const int kb = (wave * chunks / NW) * 256, ke = ((wave + 1) * chunks / NW) * 256;
 
-    const int KS = K / 32, tiles = (V + 15) / 16;
-    const bf16_t* wt[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) wt[nt] = W + (size_t)min(blockIdx.x * NT + nt, tiles - 1) * KS * DF_FRAG + lane * 8;
+    // group blockIdx.x of the chunk-major packed matrix: one contiguous 32 KB block per k-chunk
+    const size_t chunk_stride = packed_groups(V) * 32 * DF_FRAG;
+    const bf16_t* wt = W + (size_t)blockIdx.x * 32 * DF_FRAG + lane * 8;
     const bf16_t* zrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) zrow[mt] = z + (size_t)min(mt * 16 + r, M - 1) * K + g * 8;
@@ -207,7 +206,7 @@ __global__ __launch_bounds__(64 * NW) void lm_head_bf16(const bf16_t* __restrict
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) wf[nt][j] = ld16_nt(wt[nt] + (size_t)(kc / 32 + j) * DF_FRAG);
+            for (int nt = 0; nt < NT; ++nt) wf[nt][j] = ld16_nt(wt + (size_t)(kc / 256) * chunk_stride + (nt * 8 + j) * DF_FRAG);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 zf[mt][j] = ld16(zrow[mt] + kc + j * 32);

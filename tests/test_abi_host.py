@@ -182,17 +182,19 @@ def test_accept_and_linear_validation(D):
 
 
 def _packed_elems(n, k):
-    return -(-n // 16) * 16 * k
+    """Rows padded to whole 64-row groups (four 16-row fragment tiles)."""
+    return -(-n // 64) * 64 * k
 
 
 def test_packed_weight_store_size(D):
-    """The packed store holds every projection matrix once, each padded to whole 16-row fragments."""
+    """The packed store holds every projection matrix once; matrices one GEMM stacks ([wq; wk; wv], [w_gate;
+    w_up], the layers' [uk; uv]) are packed as one matrix, each padded to whole 64-row groups."""
     import workloads as W
     for s in (W.QWEN3_8B, W.SMALL_BF16, W.SMALL_GQA8):
         m = _create(D, s)
         qd, kvd, H, F = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim, s.hidden, s.ffn
-        per_layer = (_packed_elems(qd, H) + 4 * _packed_elems(kvd, H) + _packed_elems(H, qd) + 2 * _packed_elems(F, H)
-                     + _packed_elems(H, F))
+        per_layer = (_packed_elems(qd + 2 * kvd, H) + _packed_elems(2 * kvd, H) + _packed_elems(H, qd)
+                     + _packed_elems(2 * F, H) + _packed_elems(H, F))
         want = 2 * (s.n_layers * per_layer + _packed_elems(H, s.feat_dim) + _packed_elems(s.vocab, H))
         assert D.dflash_packed_weight_bytes(m.handle) == want
         m.close()
