@@ -131,16 +131,61 @@ def launch_bytes(name, s, batch, ctx_total):
     return 0
 
 
+def _oracle_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] + [1]))
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_sample(q_logits, p_logits, drafts, seed):
+    """The temperature-1 oracle on the host for the same inputs as the GPU leg: Gumbel-max sampling of the
+    16 drafter rows and the rejection-sampling verifier (fp64 NumPy)."""
+    from oracle import sampling as OS
+    t0 = time.perf_counter()
+    OS.sample_rows(q_logits, seed)
+    t1 = time.perf_counter()
+    OS.speculative_verify(drafts, q_logits[1:], p_logits, seed, 0)
+    t2 = time.perf_counter()
+    return {"value_sample_us": round((t1 - t0) * 1e6, 1), "value_verify_us": round((t2 - t1) * 1e6, 1),
+            "unit": "us per call", "cores": _oracle_cores(), "kind": "oracle",
+            "sample": "one request: Gumbel-max over the drafter's 16 rows, then one verification (fp64)"}
+
+
+def cpu_baseline_ddtree(logits_rows, budget, target_next):
+    """The DDTree oracle on the host for the same drafter logits: per-depth top-K log-probs, Algorithm 1 and
+    the verifier walk (fp64 NumPy; the heap in Python)."""
+    from oracle import ddtree as OD
+    K = min(budget, logits_rows.shape[-1], 1024)
+    t0 = time.perf_counter()
+    ids, lp = OD.topk_logprobs(logits_rows, K)
+    t1 = time.perf_counter()
+    nodes = OD.build_tree(lp, budget)
+    t2 = time.perf_counter()
+    toks = OD.tree_tokens(nodes, ids)
+    OD.verify_walk(toks, [p for _, _, p in nodes], target_next)
+    t3 = time.perf_counter()
+    return {"topk_us": round((t1 - t0) * 1e6, 1), "build_us": round((t2 - t1) * 1e6, 1),
+            "walk_us": round((t3 - t2) * 1e6, 1), "unit": "us per call", "cores": _oracle_cores(),
+            "kind": "oracle", "sample": f"one request, depths 1..{logits_rows.shape[0]}, budget {budget} (fp64)"}
+
+
+def cpu_baseline_tree_attn(q, k, v, parent, k_ctx, v_ctx, theta):
+    """The dense masked tree-attention oracle on the host for the same layer (fp64 NumPy)."""
+    from oracle import tree_attention as OT
+    t0 = time.perf_counter()
+    OT.tree_attention(q, k, v, parent, k_ctx, v_ctx, theta)
+    return {"value_us": round((time.perf_counter() - t0) * 1e6, 1), "unit": "us per call",
+            "cores": _oracle_cores(), "kind": "oracle", "sample": f"one request, {len(parent)} tree tokens (fp64)"}
+
+
 def cpu_baseline(wl, weights, n_new, cap_s):
     """The oracle (fp64 NumPy) on the host: one steady-state cycle on the same workload.  The oracle's own
     prefill of the context is done first and not timed; the timed sample is inject(n_new) + draft + accept."""
     import oracle as O
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = _oracle_cores()
     s = wl.shape
     kv = []
     for r in range(wl.batch):
@@ -295,10 +340,13 @@ def ddtree_bench(args):
         us_topk, us_build, us_walk = timed(topk), timed(build), timed(walk)
         walk()
         torch.cuda.synchronize()
+        cpu = None
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline_ddtree(logits[0, 1:].cpu().double().numpy(), budget, tgt[0])
         print(json.dumps({"ddtree": wl.name, "budget": budget, "K": K, "depth": L - 1, "nodes": int(nn[0]),
                           "draft_block_us": round(us_draft, 1), "draft_block_with_logits_us": round(us_draft_logits, 1),
                           "topk_us": round(us_topk, 1), "build_us": round(us_build, 1), "walk_us": round(us_walk, 1),
-                          "accepted_nodes": int(alen.cpu()[0]),
+                          "accepted_nodes": int(alen.cpu()[0]), "cpu_baseline": cpu,
                           "topk_logits_gbs": round(B * L * V * 4 / (us_topk * 1e-6) / 1e9, 1)}), flush=True)
 
 
@@ -365,7 +413,11 @@ def sample_bench(args):
         taus.append(tau.cpu().numpy().copy())
     us_cycle = timed(lambda: (draft_sample(True), verify()))
     verify_bytes = B * (2 * n + 1) * V * 4 + B * 2 * V * 4
-    print(json.dumps({"sample": wl.name, "batch": B, "block_len": L, "vocab": V,
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_sample(logits[0].cpu().double().numpy(), p[0].cpu().double().numpy(),
+                                  drafts[0].cpu().numpy(), seed[0])
+    print(json.dumps({"sample": wl.name, "cpu_baseline": cpu, "batch": B, "block_len": L, "vocab": V,
                       "draft_greedy_us": round(us_greedy, 1), "draft_sample_us": round(us_sample, 1),
                       "draft_sample_with_logits_us": round(us_sample_logits, 1),
                       "verify_sample_us": round(us_verify, 1),
@@ -429,10 +481,17 @@ def tree_attn_bench(args):
         us = e0.elapsed_time(e1) / args.steps * 1e3
         flops = 4.0 * T * nq * C * d
         nbytes = 2 * C * nkv * d * 2 + T * (nq + 2 * nkv) * d * 2 + T * nq * d * 2
+        cpu = None
+        if not args.no_cpu_baseline and T <= 257:
+            pages = pt[0, : C // 16].long()
+            kc = kp[pages].permute(0, 2, 1, 3).reshape(C, nkv, d)           # [page, head, slot, d] -> [pos, head, d]
+            vc = vp[pages].permute(0, 3, 1, 2).reshape(C, nkv, d)           # [page, head, d, slot] -> [pos, head, d]
+            f64 = lambda t: t.float().cpu().double().numpy()
+            cpu = cpu_baseline_tree_attn(f64(q[0]), f64(k[0]), f64(v[0]), par[0].cpu().numpy(), f64(kc), f64(vc), 1e6)
         print(json.dumps({"tree_attention": "qwen3-8b-attention-shape", "ctx": C, "nodes": budget, "tokens": T,
                           "us": round(us, 1), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
                           "mfma_frac_bf16": round(flops / (us * 1e-6) / 2.5e15, 3),
-                          "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}), flush=True)
+                          "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "cpu_baseline": cpu}), flush=True)
 
 
 def main():
