@@ -28,14 +28,16 @@ namespace df {
 
 static size_t ta_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Waves per context workgroup: the G query heads of a KV head times TA_WAVES / G token tiles, all served by
-// the same staged K/V.
+// Waves per context workgroup: the G query heads of a KV head times TA_WAVES / G wave slots, each slot
+// TA_QT token tiles, all served by the same staged K/V.  Two tiles per wave make every K (V) fragment read
+// from LDS feed two MFMAs: the kernel is bound by LDS reads, not by the matrix cores.
 #define TA_WAVES 8
+#define TA_QT 2
 
 TreePlan plan_tree(int batch, int max_tokens, int nq, int nkv, int max_ctx) {
     TreePlan p{};
     p.tiles = (max_tokens + 15) / 16;
-    const int tw = TA_WAVES / (nq / nkv);
+    const int tw = TA_WAVES / (nq / nkv) * TA_QT;  // tiles per workgroup
     p.stiles = (p.tiles + tw - 1) / tw;
     p.chunks = 0;
     p.chunk_tokens = 0;
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(256) void tree_prep(int T, const int32_t* __restric
 // ------------------------------------------------------------------------------------------------------
 // tree_ctx_bf16: the context part (MFMA)
 // ------------------------------------------------------------------------------------------------------
-// Wave w serves query head kv_head * G + w % G for token tile super_tile * TW + w / G.
+// Wave w serves query head kv_head * G + w % G for the TA_QT token tiles (super_tile * TW + w / G) * TA_QT + i.
 template <int G>
 __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __restrict__ qr, int Tpad, int tiles, int nq,
                                                         int nkv, const bf16_t* __restrict__ kpool,
@@ -207,6 +209,7 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
                                                         float* __restrict__ mlpart, uint32_t* err) {
     constexpr int D = TA_D;
     constexpr int TW = TA_WAVES / G;
+    constexpr int QT = TA_QT;
     constexpr int NT = 64 * TA_WAVES;
     constexpr int NPG = TA_SUB / 16;
     constexpr int PIECES = NPG * 512;
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
     __shared__ __attribute__((aligned(16))) bf16_t sv[NPG * D * TA_VLD];
     __shared__ int spg[TA_MAX_PAGES];
     // grid: KV head fastest, then super tile, chunk, request
-    const int stiles = (tiles + TW - 1) / TW;
+    const int stiles = (tiles + TW * QT - 1) / (TW * QT);
     int bid = blockIdx.x;
     const int kvh = bid % nkv;
     bid /= nkv;
@@ -227,8 +230,7 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int h = kvh * G + w % G;
-    const int tile = stile * TW + w / G;
-    const bool tile_ok = tile < tiles;  // the last super tile may reach past the tree
+    const int tile0 = (stile * TW + w / G) * QT;  // this wave's first tile; the last super tile may reach past the tree
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     const size_t page_elems = (size_t)16 * D;
 
@@ -288,17 +290,24 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
         }
     };
 
-    // Q^T operand: lane supplies query row r of the tile (token tile * 16 + r), 8 d-values per k-step
-    u32x4 qf[4];
-    {
-        const bf16_t* qp = qr + (((size_t)b * Tpad + (tile_ok ? tile : 0) * 16 + r) * nq + h) * D + g * 8;
+    // Q^T operands: lane supplies query row r of each tile (token tile * 16 + r), 8 d-values per k-step
+    u32x4 qf[QT][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qf[s] = tile_ok ? ld16(qp + s * 32) : u32x4{0u, 0u, 0u, 0u};
+    for (int qi = 0; qi < QT; ++qi) {
+        const bool ok = tile0 + qi < tiles;
+        const bf16_t* qp = qr + (((size_t)b * Tpad + (ok ? tile0 + qi : 0) * 16 + r) * nq + h) * D + g * 8;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[qi][s] = ok ? ld16(qp + s * 32) : u32x4{0u, 0u, 0u, 0u};
     }
-    f32x4 o[8];
+    f32x4 o[QT][8];
+    float m_run[QT], l_run[QT];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int qi = 0; qi < QT; ++qi) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[qi][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[qi] = -INFINITY;
+        l_run[qi] = 0.f;
+    }
 
     __syncthreads();  // page ids in LDS
     for (int j = tid; j < chunk_tokens / 16 && t0 + 16 * j < t1; j += NT) {
@@ -311,79 +320,96 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
         stash(ts);
         __syncthreads();
         if (ts + TA_SUB < t1) prefetch(ts + TA_SUB);
-        f32x4 sa[NPG];
+        f32x4 sa[QT][NPG];
 #pragma unroll
-        for (int e = 0; e < NPG; ++e) sa[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qi = 0; qi < QT; ++qi)
+#pragma unroll
+            for (int e = 0; e < NPG; ++e) sa[qi][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int e = 0; e < NPG; ++e) sa[e] = mfma16(ld16(sk + (e * 16 + r) * TA_KLD + g * 8 + s * 32), qf[s], sa[e]);
-        float x[NPG][4];
+            for (int e = 0; e < NPG; ++e) {
+                const u32x4 kf = ld16(sk + (e * 16 + r) * TA_KLD + g * 8 + s * 32);
 #pragma unroll
-        for (int e = 0; e < NPG; ++e)
+                for (int qi = 0; qi < QT; ++qi) sa[qi][e] = mfma16(kf, qf[qi][s], sa[qi][e]);
+            }
+        u32x4 pb[QT][NPG / 2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[e][i] = sa[e][i] * scale_log2;
-        if (ts + TA_SUB > t1) {
-            const int nk = t1 - ts;
+        for (int qi = 0; qi < QT; ++qi) {
+            float x[NPG][4];
 #pragma unroll
             for (int e = 0; e < NPG; ++e)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[e][i] = 16 * e + 4 * g + i < nk ? x[e][i] : -INFINITY;
-        }
-        float mx = -INFINITY;
+                for (int i = 0; i < 4; ++i) x[e][i] = sa[qi][e][i] * scale_log2;
+            if (ts + TA_SUB > t1) {
+                const int nk = t1 - ts;
 #pragma unroll
-        for (int e = 0; e < NPG; ++e)
+                for (int e = 0; e < NPG; ++e)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[e][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-        m_run = m_new;
-        float p[NPG][4];
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < NPG; ++e)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[e][i] = __builtin_amdgcn_exp2f(x[e][i] - m_ref);
-                psum += p[e][i];
+                    for (int i = 0; i < 4; ++i) x[e][i] = 16 * e + 4 * g + i < nk ? x[e][i] : -INFINITY;
             }
-        l_run = l_run * alpha + psum;
+            float mx = -INFINITY;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            o[dt][0] *= alpha; o[dt][1] *= alpha; o[dt][2] *= alpha; o[dt][3] *= alpha;
+            for (int e = 0; e < NPG; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[e][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(m_run[qi], mx);
+            const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run[qi] - m_ref);
+            m_run[qi] = m_new;
+            float p[NPG][4];
+            float psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < NPG; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[e][i] = __builtin_amdgcn_exp2f(x[e][i] - m_ref);
+                    psum += p[e][i];
+                }
+            l_run[qi] = l_run[qi] * alpha + psum;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                o[qi][dt][0] *= alpha; o[qi][dt][1] *= alpha; o[qi][dt][2] *= alpha; o[qi][dt][3] *= alpha;
+            }
+#pragma unroll
+            for (int hk = 0; hk < NPG / 2; ++hk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    pb[qi][hk][j] = f2bf2(p[2 * hk + (j >> 1)][2 * (j & 1)], p[2 * hk + (j >> 1)][2 * (j & 1) + 1]);
         }
-        // O^T += V^T P^T over 32-key slices, P as bfloat16
+        // O^T += V^T P^T over 32-key slices, P as bfloat16; each V^T fragment feeds every tile
 #pragma unroll
         for (int hk = 0; hk < NPG / 2; ++hk) {
             if (ts + 32 * hk >= t1) break;
-            u32x4 pb;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                pb[j] = f2bf2(p[2 * hk + (j >> 1)][2 * (j & 1)], p[2 * hk + (j >> 1)][2 * (j & 1) + 1]);
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 const int d = dt * 16 + r;
                 const u32x2 va = *(const u32x2*)(sv + ((2 * hk) * D + d) * TA_VLD + 4 * g);
                 const u32x2 vb = *(const u32x2*)(sv + ((2 * hk + 1) * D + d) * TA_VLD + 4 * g);
-                o[dt] = mfma16(u32x4{va[0], va[1], vb[0], vb[1]}, pb, o[dt]);
+                const u32x4 vf = u32x4{va[0], va[1], vb[0], vb[1]};
+#pragma unroll
+                for (int qi = 0; qi < QT; ++qi) o[qi][dt] = mfma16(vf, pb[qi][hk], o[qi][dt]);
             }
         }
     }
-    float l_tot = l_run;
-    l_tot += __shfl_xor(l_tot, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
-    if (!tile_ok) return;
-    const size_t base = ((((size_t)b * tiles + tile) * nq + h) * n_chunks + c) * 16 + r;
-    float* op = opart + base * D;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-        *(float4*)(op + dt * 16 + 4 * g) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (g == 0) {
-        mlpart[base * 2 + 0] = m_run;
-        mlpart[base * 2 + 1] = l_tot;
+    for (int qi = 0; qi < QT; ++qi) {
+        const int tile = tile0 + qi;
+        float l_tot = l_run[qi];
+        l_tot += __shfl_xor(l_tot, 16, 64);
+        l_tot += __shfl_xor(l_tot, 32, 64);
+        if (tile >= tiles) continue;
+        const size_t base = ((((size_t)b * tiles + tile) * nq + h) * n_chunks + c) * 16 + r;
+        float* op = opart + base * D;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+            *(float4*)(op + dt * 16 + 4 * g) = make_float4(o[qi][dt][0], o[qi][dt][1], o[qi][dt][2], o[qi][dt][3]);
+        if (g == 0) {
+            mlpart[base * 2 + 0] = m_run[qi];
+            mlpart[base * 2 + 1] = l_tot;
+        }
     }
 }
 
