@@ -12,8 +12,8 @@
 namespace df {
 
 #define HEAD_REC 20  // max, sumexp, 8 values, 8 ids (as int bits), sampled score and id (temperature 1 only)
-// Records are stored field-major per block row, hpart[(row * HEAD_REC + field) * groups + group], so that the
-// merge reads each field of consecutive groups with coalesced loads.
+// Records are stored per group, hpart[(group * rows + row) * HEAD_REC + field]: the records a workgroup of the
+// LM head writes are one contiguous block (80 bytes per block row), so its stores fill whole cache lines.
 
 // Vocabulary columns per record group: 64 for the skinny head (block rows <= 32), 128 for the tiled head.
 int head_group_width(int bf16, int M) { return (bf16 && M > 32) ? 128 : 64; }
@@ -147,18 +147,17 @@ __device__ void head_epilogue(const float (*lg)[C + 1], int rows, int row0, int 
         }
     }
     if (live && piece == 0) {
-        const size_t G = gridDim.x;  // record groups
-        float* dst = hpart + (size_t)(row0 + m) * HEAD_REC * G + group;
+        float* dst = hpart + ((size_t)group * Mtot + row0 + m) * HEAD_REC;
         dst[0] = mx;
-        dst[G] = se;
+        dst[1] = se;
 #pragma unroll
         for (int j = 0; j < DF_TOPK; ++j) {
-            dst[(2 + j) * G] = s.v[j];
-            dst[(2 + DF_TOPK + j) * G] = __int_as_float(s.id[j]);
+            dst[2 + j] = s.v[j];
+            dst[2 + DF_TOPK + j] = __int_as_float(s.id[j]);
         }
         if (sample) {
-            dst[(2 + 2 * DF_TOPK) * G] = bs;
-            dst[(3 + 2 * DF_TOPK) * G] = __int_as_float(bi);
+            dst[2 + 2 * DF_TOPK] = bs;
+            dst[3 + 2 * DF_TOPK] = __int_as_float(bi);
         }
     }
 }
@@ -380,17 +379,17 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
         t8 = -INFINITY;
         if (btok[m] < 0 || btok[m] >= V) set_err(err, DFLASH_DEVERR_TOKEN);
     }
-    const size_t G = n_groups;
-    const float* row = hpart + (size_t)m * HEAD_REC * G;  // field f of group gi at row[f * G + gi]
+    const size_t RS = (size_t)M * HEAD_REC;               // record stride between groups
+    const float* row = hpart + (size_t)m * HEAD_REC;      // field f of group gi at row[gi * RS + f]
     float mx = -INFINITY, th = -INFINITY;
     float sb = -INFINITY;  // temperature 1: best (perturbed score, id) over the records
     int sbi = 0x7FFFFFFF;
     for (int gi = t; gi < n_groups; gi += MERGE_THREADS) {
-        mx = fmaxf(mx, row[gi]);
-        th = fmaxf(th, row[(2 + DF_TOPK - 1) * G + gi]);
+        mx = fmaxf(mx, row[gi * RS]);
+        th = fmaxf(th, row[gi * RS + (2 + DF_TOPK - 1)]);
         if (sample) {
-            const float v = row[(2 + 2 * DF_TOPK) * G + gi];
-            const int id = __float_as_int(row[(3 + 2 * DF_TOPK) * G + gi]);
+            const float v = row[gi * RS + (2 + 2 * DF_TOPK)];
+            const int id = __float_as_int(row[gi * RS + (3 + 2 * DF_TOPK)]);
             if (df_better(v, id, sb, sbi)) {
                 sb = v;
                 sbi = id;
@@ -422,12 +421,12 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
     th = fmaxf(th1, t8);  // t8 was written before block_max's barriers
     float se = 0.f;
     for (int gi = t; gi < n_groups; gi += MERGE_THREADS) {
-        const float r0 = row[gi];
-        if (r0 != -INFINITY) se += row[G + gi] * expf(r0 - mx);
+        const float r0 = row[gi * RS];
+        if (r0 != -INFINITY) se += row[gi * RS + 1] * expf(r0 - mx);
         if (r0 >= th) {  // the record's best entry reaches the threshold: scan its list
             for (int j = 0; j < DF_TOPK; ++j) {
-                const float v = row[(2 + j) * G + gi];
-                const int id = __float_as_int(row[(2 + DF_TOPK + j) * G + gi]);
+                const float v = row[gi * RS + (2 + j)];
+                const int id = __float_as_int(row[gi * RS + (2 + DF_TOPK + j)]);
                 if (v < th) break;
                 if (id < V) {
                     const int k = atomicAdd(&cnt, 1);
@@ -462,8 +461,8 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
             int oid[DF_TOPK];
 #pragma unroll
             for (int j = 0; j < DF_TOPK; ++j) {
-                ov[j] = row[(2 + j) * G + gi];
-                oid[j] = __float_as_int(row[(2 + DF_TOPK + j) * G + gi]);
+                ov[j] = row[gi * RS + (2 + j)];
+                oid[j] = __float_as_int(row[gi * RS + (2 + DF_TOPK + j)]);
             }
             s.merge(ov, oid);
         }
