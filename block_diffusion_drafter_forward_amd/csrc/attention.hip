@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ opar
         __builtin_amdgcn_wave_barrier();
         const int cn = min(64, C1 - c0);
         const float* op = opart + ((base + c0) * 16 + row) * d;
-#pragma unroll 4
+#pragma unroll 16  // sixteen chunks' loads in flight per batch (the additions keep their order)
         for (int i = 0; i < cn; ++i) {
             const float wi = wsh[w][i];
             acc0 += wi * op[(size_t)i * 16 * d + lane];

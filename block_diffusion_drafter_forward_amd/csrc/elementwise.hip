@@ -15,7 +15,42 @@ namespace df {
 #define ROW_PASSES 4
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *(const float4*)p; }
+
+// Split-K sums in a fixed order (s = 0, 1, ..., S - 1, the same additions as a plain loop), with the loads of
+// up to SPLIT_BATCH splits issued before the first add so that they are in flight together.
+#define SPLIT_BATCH 8
+__device__ __forceinline__ float split_sum(const float* p, size_t stride, int S) {
+    float acc = 0.f;
+    for (int s0 = 0; s0 < S; s0 += SPLIT_BATCH) {
+        float v[SPLIT_BATCH];
+#pragma unroll
+        for (int u = 0; u < SPLIT_BATCH; ++u) v[u] = s0 + u < S ? p[(size_t)(s0 + u) * stride] : 0.f;
+#pragma unroll
+        for (int u = 0; u < SPLIT_BATCH; ++u)
+            if (s0 + u < S) acc += v[u];
+    }
+    return acc;
+}
 __device__ __forceinline__ void st4(float* p, float4 v) { *(float4*)p = v; }
+// float4 split sums starting from split 0 (no +0 first), batched like split_sum
+__device__ __forceinline__ float4 split_sum4(const float* p, size_t stride, int S) {
+    float4 acc = ld4(p);
+    for (int s0 = 1; s0 < S; s0 += SPLIT_BATCH) {
+        float4 v[SPLIT_BATCH];
+#pragma unroll
+        for (int u = 0; u < SPLIT_BATCH; ++u)
+            v[u] = s0 + u < S ? ld4(p + (size_t)(s0 + u) * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < SPLIT_BATCH; ++u)
+            if (s0 + u < S) {
+                acc.x += v[u].x;
+                acc.y += v[u].y;
+                acc.z += v[u].z;
+                acc.w += v[u].w;
+            }
+    }
+    return acc;
+}
 __device__ __forceinline__ float4 ld4(const bf16_t* p) {
     const uint2 b = *(const uint2*)p;
     return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u), __uint_as_float(b.y << 16),
@@ -104,8 +139,7 @@ __global__ __launch_bounds__(ROW_THREADS) void resid_norm(const float* __restric
     for (int q = 0; q < ROW_PASSES; ++q) {
         const int j = (threadIdx.x + q * ROW_THREADS) * 4;
         if (j >= H) break;
-        float4 a = ld4(part + (size_t)m * H + j);
-        for (int s = 1; s < S; ++s) a = add4(a, ld4(part + ((size_t)s * M + m) * H + j));
+        const float4 a = split_sum4(part + (size_t)m * H + j, (size_t)M * H, S);
         v[q] = add4(ld4(h + (size_t)m * H + j), a);
         st4(h + (size_t)m * H + j, v[q]);
         if (tap) st4(tap + (size_t)m * H + j, v[q]);
@@ -145,11 +179,8 @@ __global__ __launch_bounds__(256) void qkv_epilogue(const float* __restrict__ pa
     const int hd = (idx / half) % heads;
     const int m = idx / ((long)half * heads);
     const int c1 = hd * d + i, c2 = c1 + half;
-    float a = 0.f, c = 0.f;
-    for (int s = 0; s < S; ++s) {
-        a += part[((size_t)s * M + m) * N + c1];
-        c += part[((size_t)s * M + m) * N + c2];
-    }
+    const float a = split_sum(part + (size_t)m * N + c1, (size_t)M * N, S);
+    const float c = split_sum(part + (size_t)m * N + c2, (size_t)M * N, S);
     qkv_store(a, c, m, hd, i, B, L, nq, nkv, d, ctx_len, rf, q, kb, vbt);
 }
 
@@ -177,11 +208,8 @@ __global__ __launch_bounds__(256) void swiglu(const float* __restrict__ part, in
     if (idx >= (long)M * F) return;
     const int m = idx / F, j = idx % F;
     const size_t N = 2 * (size_t)F;
-    float g = 0.f, up = 0.f;
-    for (int s = 0; s < S; ++s) {
-        g += part[((size_t)s * M + m) * N + j];
-        up += part[((size_t)s * M + m) * N + F + j];
-    }
+    const float g = split_sum(part + (size_t)m * N + j, (size_t)M * N, S);
+    const float up = split_sum(part + (size_t)m * N + F + j, (size_t)M * N, S);
     put_act(a, (size_t)M * F, idx, swiglu_value(g, up));
 }
 
@@ -199,8 +227,7 @@ __global__ __launch_bounds__(256) void reduce_cast(const float* __restrict__ par
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (long)M * N) return;
     const int n = idx % N;
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += part[(size_t)s * M * N + idx];
+    float v = split_sum(part + idx, (size_t)M * N, S);
     if (bias) v += Act<T>::load(bias + n);
     put_act(out, (size_t)M * N, idx, v);
 }
@@ -264,14 +291,10 @@ __global__ __launch_bounds__(256) void kv_scatter(const float* __restrict__ part
     const int N = n_layers * 2 * nkv * d;
     const int ck = l * 2 * nkv * d + kh * d + i;
     const int cv = ck + nkv * d;
-    float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
-    for (int s = 0; s < S; ++s) {
-        const float* p = part + ((size_t)s * rows + j) * N;
-        k1 += p[ck];
-        k2 += p[ck + half];
-        v1 += p[cv];
-        v2 += p[cv + half];
-    }
+    const float* p = part + (size_t)j * N;
+    const size_t stride = (size_t)rows * N;
+    float k1 = split_sum(p + ck, stride, S), k2 = split_sum(p + ck + half, stride, S);
+    const float v1 = split_sum(p + cv, stride, S), v2 = split_sum(p + cv + half, stride, S);
     rope_pair(k1, k2, pos, i, rf);
     const size_t pg = ((size_t)(layer0 + l) * n_pages + page) * nkv + kh;
     T* kd = kpool + (pg * 16 + slot) * d;
