@@ -384,7 +384,30 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
     float mx = -INFINITY, th = -INFINITY;
     float sb = -INFINITY;  // temperature 1: best (perturbed score, id) over the records
     int sbi = 0x7FFFFFFF;
-    for (int gi = t; gi < n_groups; gi += MERGE_THREADS) {
+    // A record is five 16-byte words (80 bytes, 16-byte aligned): word 0 holds (max, sumexp, v0, v1), word 2
+    // (v6, v7, id0, id1), word 4 (id6, id7, sampled score, sampled id).  The first MERGE_GROUPS of a thread's groups are
+    // fetched with their loads in flight together, and their (max, sumexp) kept for the second pass.
+    constexpr int MERGE_GROUPS = 4;
+    float4 w0[MERGE_GROUPS];
+#pragma unroll
+    for (int u = 0; u < MERGE_GROUPS; ++u) {
+        const int gi = t + u * MERGE_THREADS;
+        w0[u] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+        float4 w2 = make_float4(0.f, -INFINITY, 0.f, 0.f), w4 = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+        if (gi < n_groups) {
+            const float4* rec = (const float4*)(row + gi * RS);
+            w0[u] = rec[0];
+            w2 = rec[2];
+            if (sample) w4 = rec[4];
+        }
+        mx = fmaxf(mx, w0[u].x);
+        th = fmaxf(th, w2.y);  // the record's 8th value
+        if (sample && gi < n_groups && df_better(w4.z, __float_as_int(w4.w), sb, sbi)) {  // fields 18, 19
+            sb = w4.z;
+            sbi = __float_as_int(w4.w);
+        }
+    }
+    for (int gi = t + MERGE_GROUPS * MERGE_THREADS; gi < n_groups; gi += MERGE_THREADS) {  // very large vocabularies
         mx = fmaxf(mx, row[gi * RS]);
         th = fmaxf(th, row[gi * RS + (2 + DF_TOPK - 1)]);
         if (sample) {
@@ -421,8 +444,19 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
     th = fmaxf(th1, t8);  // t8 was written before block_max's barriers
     float se = 0.f;
     for (int gi = t; gi < n_groups; gi += MERGE_THREADS) {
-        const float r0 = row[gi * RS];
-        if (r0 != -INFINITY) se += row[gi * RS + 1] * expf(r0 - mx);
+        const int u = (gi - t) / MERGE_THREADS;
+        float r0, r1;
+        if (u < MERGE_GROUPS) {  // cached from the first pass (u is uniform per iteration)
+            float4 c = w0[0];
+#pragma unroll
+            for (int q = 1; q < MERGE_GROUPS; ++q) c = u == q ? w0[q] : c;
+            r0 = c.x;
+            r1 = c.y;
+        } else {
+            r0 = row[gi * RS];
+            r1 = row[gi * RS + 1];
+        }
+        if (r0 != -INFINITY) se += r1 * expf(r0 - mx);
         if (r0 >= th) {  // the record's best entry reaches the threshold: scan its list
             for (int j = 0; j < DF_TOPK; ++j) {
                 const float v = row[gi * RS + (2 + j)];
