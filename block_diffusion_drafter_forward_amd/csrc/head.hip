@@ -165,7 +165,7 @@ __device__ void head_epilogue(const float (*lg)[C + 1], int rows, int row0, int 
 // ------------------------------------------------------------------------------------------------------
 // bfloat16 MFMA LM head: the GEMM core of the skinny kernel with the reductions as epilogue
 // ------------------------------------------------------------------------------------------------------
-// W is the packed (fragment-major) V x K matrix; z is an activation pair of bfloat16 planes (lo plane at
+// W is the packed (chunk-major) V x K matrix; z is an activation pair of bfloat16 planes (lo plane at
 // z + zplane): two MFMAs per weight fragment.  NW waves split K.  Four waves per workgroup keep two
 // workgroups resident per CU, so one streams weights while the other runs its reduction epilogue (measured
 // on MI355X: eight waves per workgroup, one workgroup per CU, is ~20% slower end to end).

@@ -17,9 +17,8 @@ struct GemmPlan {
     int kps;     // tiled: k-range per split (multiple of 64)
 };
 GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K);
-// Packs the row-major bfloat16 matrix src[N][K] (K a multiple of 32) into the fragment-major image of
-// gemm_core.h at dst (packed_elems(N, K) elements).
-// Packs the N x K matrix stacked from the row segments of src (chunk-major layout of gemm_core.h) into dst.
+// Packs the N x K bfloat16 matrix stacked from the row segments of src (row-major rows, K a multiple of 256)
+// into the chunk-major fragment layout of gemm_core.h at dst.
 hipError_t launch_pack(const Segs& src, int N, int K, void* dst, hipStream_t st);
 // bfloat16: wpacked is the packed N x K matrix.  xplane != 0: x is an activation pair of bfloat16 planes
 // (lo plane xplane elements after hi).
