@@ -589,10 +589,6 @@ extern "C" int dflash_inject_ctx(dflash_handle* h, int batch, int n_rows, const 
     float* part = (float*)(W + p.part);
     const int H = c.hidden, kvd = c.n_kv_heads * c.head_dim;
     const size_t E = elt(c);
-    {
-        Timed t(h, "clear_err", st);
-        HIP_TRY(launch_clear_err(err, st));
-    }
     for (int row0 = 0; row0 < n_rows; row0 += p.rows) {
         const int R = std::min(p.rows, n_rows - row0);
         const char* x = (const char*)feats + (size_t)row0 * feat_row_stride * E;
@@ -604,7 +600,8 @@ extern "C" int dflash_inject_ctx(dflash_handle* h, int batch, int n_rows, const 
         }
         {
             Timed t(h, "fuse_cast", st);
-            HIP_TRY(launch_reduce_cast(bf, part, fc.splits, R, H, h->w.fc_b, f, st));
+            // the first chunk's cast also clears the device error word (kv_scatter is the first kernel to set it)
+            HIP_TRY(launch_reduce_cast(bf, part, fc.splits, R, H, h->w.fc_b, f, row0 == 0 ? err : nullptr, st));
         }
         for (int l0 = 0; l0 < c.n_layers; l0 += MAX_LAYERS_PER_KV_GEMM) {
             const int nl = std::min(MAX_LAYERS_PER_KV_GEMM, c.n_layers - l0);
@@ -758,7 +755,7 @@ extern "C" int dflash_linear(int dtype, int M, int N, int K, const void* x, int6
     } else {
         HIP_TRY(launch_gemm_f32((const float*)x, (int)ldx, M, segs1(w, N), N, K, (float*)ws, st));
     }
-    HIP_TRY(launch_reduce_cast(0, (float*)ws, p.splits, M, N, nullptr, y, st));
+    HIP_TRY(launch_reduce_cast(0, (float*)ws, p.splits, M, N, nullptr, y, nullptr, st));
     return DFLASH_OK;
 }
 

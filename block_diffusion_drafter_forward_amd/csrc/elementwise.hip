@@ -221,9 +221,12 @@ hipError_t launch_swiglu(int bf16, const float* part, int S, int M, int F, void*
     return hipGetLastError();
 }
 
+// clear_err (nullable): the call's device error word, zeroed by block 0 (this kernel sets no flag itself).
 template <typename T>
 __global__ __launch_bounds__(256) void reduce_cast(const float* __restrict__ part, int S, int M, int N,
-                                                   const T* __restrict__ bias, T* __restrict__ out) {
+                                                   const T* __restrict__ bias, T* __restrict__ out,
+                                                   uint32_t* clear_err) {
+    if (clear_err && blockIdx.x == 0 && threadIdx.x == 0) *clear_err = 0u;
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (long)M * N) return;
     const int n = idx % N;
@@ -233,14 +236,15 @@ __global__ __launch_bounds__(256) void reduce_cast(const float* __restrict__ par
 }
 
 hipError_t launch_reduce_cast(int bf16, const float* part, int S, int M, int N, const void* bias, void* out,
-                              hipStream_t st) {
+                              uint32_t* clear_err, hipStream_t st) {
     const long n = (long)M * N;
     const dim3 grid((unsigned)((n + 255) / 256));
     if (bf16)
         hipLaunchKernelGGL(reduce_cast<bf16_t>, grid, dim3(256), 0, st, part, S, M, N, (const bf16_t*)bias,
-                           (bf16_t*)out);
+                           (bf16_t*)out, clear_err);
     else
-        hipLaunchKernelGGL(reduce_cast<float>, grid, dim3(256), 0, st, part, S, M, N, (const float*)bias, (float*)out);
+        hipLaunchKernelGGL(reduce_cast<float>, grid, dim3(256), 0, st, part, S, M, N, (const float*)bias, (float*)out,
+                           clear_err);
     return hipGetLastError();
 }
 

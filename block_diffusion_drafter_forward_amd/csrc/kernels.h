@@ -44,7 +44,7 @@ hipError_t launch_qkv_epilogue(int bf16, const float* part, int S, int B, int L,
 hipError_t launch_swiglu(int bf16, const float* part, int S, int M, int F, void* a, hipStream_t st);
 // out[m][n] = round(sum_s part[s][m][n] + bias[n]).
 hipError_t launch_reduce_cast(int bf16, const float* part, int S, int M, int N, const void* bias, void* out,
-                              hipStream_t st);
+                              uint32_t* clear_err, hipStream_t st);
 // Context K/V from the stacked [U_K^0; U_V^0; U_K^1; ...] partials, RoPE at each row's position, scatter into
 // the paged pool.  row0 = index of the first row of this chunk among all n_rows rows.
 // Columns of part cover layers layer0 .. layer0 + nl - 1.
