@@ -321,10 +321,10 @@ static DraftPlan plan_draft(const dflash_config& c, int batch, int max_ctx) {
     const int M = batch * c.block_len;
     const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
     p.M = M;
-    p.qkv = plan_gemm(bf, M, qd + 2 * kvd, c.hidden);
-    p.oproj = plan_gemm(bf, M, c.hidden, qd);
-    p.gateup = plan_gemm(bf, M, 2 * c.ffn, c.hidden);
-    p.down = plan_gemm(bf, M, c.hidden, c.ffn);
+    p.qkv = plan_gemm(bf, M, qd + 2 * kvd, c.hidden, true);
+    p.oproj = plan_gemm(bf, M, c.hidden, qd, true);
+    p.gateup = plan_gemm(bf, M, 2 * c.ffn, c.hidden, true);
+    p.down = plan_gemm(bf, M, c.hidden, c.ffn, true);
     p.attn = plan_attention(batch, c.n_q_heads, c.n_kv_heads, max_ctx);
     size_t part = (size_t)p.qkv.splits * M * (qd + 2 * kvd);
     part = std::max(part, (size_t)p.oproj.splits * M * c.hidden);

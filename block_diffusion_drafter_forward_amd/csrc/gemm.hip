@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ x, int
 // launch planning
 // ------------------------------------------------------------------------------------------------------
 
-GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K) {
+GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K, bool few_splits) {
     GemmPlan p{};
     if (!dtype_bf16) {
         p.kind = GEMM_F32;
@@ -224,14 +224,27 @@ GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K) {
     }
     if (M <= 32) {
         p.kind = M <= 16 ? GEMM_SKINNY1 : GEMM_SKINNY2;
-        // Each wave streams kpw of K for 64 columns (32 KB of packed weights per 256-wide chunk).  Measured
-        // on MI355X at the drafter's shapes (4096 x 4096 up to 24576 x 4096 and 4096 x 12288): one chunk per
-        // wave is best; only vocabulary-sized N (>= ~2000 workgroups even with four chunks) gains from
-        // longer ranges.
+        // Each wave streams kpw of K for 64 columns (32 KB of packed weights per 256-wide chunk), one chunk in
+        // flight at a time.  Longer ranges mean fewer waves in flight but fewer split partials for the
+        // consumer.  Measured on MI355X: one chunk per wave is best for the GEMM alone; vocabulary-sized N
+        // (>= ~2000 workgroups even with four chunks) gains from four.  With few_splits (the drafter layer's
+        // GEMMs, whose consumers are the row norms, the QKV epilogue and SwiGLU) the longest range of at
+        // most three chunks that splits K evenly and still gives 256 or more workgroups is best:
+        // gate/up 2 chunks, down 3, QKV and O 1, 7.8 us per drafter pass less than one chunk everywhere.  The
+        // injection GEMMs, whose consumers are elementwise, lose 3-5 us each with longer ranges.
         const int groups = (N + 63) / 64;
         auto wgs = [&](int kpw) { return groups * ((K + 4 * kpw - 1) / (4 * kpw)); };
         p.kpw = 256;
-        if (K % 1024 == 0 && wgs(1024) >= 2000) p.kpw = 1024;
+        if (K % 1024 == 0 && wgs(1024) >= 2000) {
+            p.kpw = 1024;
+        } else if (few_splits) {
+            for (int kpw : {768, 512}) {
+                if (K % (4 * kpw) == 0 && wgs(kpw) >= 256) {
+                    p.kpw = kpw;
+                    break;
+                }
+            }
+        }
         p.splits = (K + 4 * p.kpw - 1) / (4 * p.kpw);
         return p;
     }

@@ -16,7 +16,9 @@ struct GemmPlan {
     int kpw;     // skinny: k-range per wave (multiple of 256)
     int kps;     // tiled: k-range per split (multiple of 64)
 };
-GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K);
+// few_splits: prefer fewer, longer k-ranges per wave (set for the drafter layer's GEMMs, where it was measured
+// to pay off through cheaper split-K consumers).
+GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K, bool few_splits = false);
 // Packs the N x K bfloat16 matrix stacked from the row segments of src (row-major rows, K a multiple of 256)
 // into the chunk-major fragment layout of gemm_core.h at dst.
 hipError_t launch_pack(const Segs& src, int N, int K, void* dst, hipStream_t st);
