@@ -1,7 +1,7 @@
 // Block attention over [injected context ; block] (non-causal), grouped-query, paged context.
 //
-// Work split: one workgroup per (request, KV head, chunk).  Chunk 0 is the block's own 16-slot K/V page;
-// chunks 1..n are consecutive ranges of the request's cached context.  Wave w of the workgroup serves query
+// Work split: one workgroup per (request, KV head, chunk of the request's cached context); chunk 0 also
+// takes the block's own 16-slot K/V page, as its first round.  Wave w of the workgroup serves query
 // head kv_head * G + w (G = query heads per KV head), whose L block rows form one 16-row MFMA tile.  Per pair
 // of 16-key pages the wave computes S^T = K Q^T (keys in rows, so a lane's four scores belong to one query
 // row), updates an online softmax in the log2 domain, and accumulates O^T = V^T P^T.  Values are cached
@@ -23,10 +23,11 @@ AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx) {
     const int sub = attn_sub(n_q / n_kv);
     AttnPlan p{0, sub};
     if (max_ctx <= 0) return p;
-    // about one workgroup per CU over (request, KV head, chunk), chunks of whole staging rounds and at
-    // most AT_MAX_PAGES pages
+    // at most one workgroup per CU over (request, KV head, chunk): a CU that had to take a second
+    // workgroup would finish last (measured: 264 workgroups for 256 CUs ended ~3 us after the median);
+    // chunks of whole staging rounds and at most AT_MAX_PAGES pages
     const int units = batch * n_kv;
-    int want = (256 + units - 1) / units;
+    int want = 256 / units;
     const int max_chunks = (max_ctx + sub - 1) / sub;
     if (want > max_chunks) want = max_chunks;
     if (want < 1) want = 1;
@@ -36,10 +37,6 @@ AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx) {
     p.chunk_tokens = ct;
     p.n_chunks = (max_ctx + ct - 1) / ct;
     return p;
-}
-
-size_t attn_partial_floats(int batch, int nq, int n_chunks, int d) {
-    return (size_t)batch * nq * (n_chunks + 1) * 16 * (size_t)(d + 2);
 }
 
 
@@ -53,18 +50,18 @@ size_t attn_partial_floats(int batch, int nq, int n_chunks, int d) {
 // key and pages the table does not map are staged as zeros, so uninitialised cache memory can never reach
 // the MFMAs.
 // q and the block's own k / v are activation pairs (hi + lo bfloat16 planes); the cached K/V are plain
-// bfloat16.  The block chunk stages its hi page in page slot 0 and its lo page in slot 1 and multiplies
+// bfloat16.  The block round stages its hi page in page slot 0 and its lo page in slot 1 and multiplies
 // every pair of terms.
 #define AT_KLD (128 + 8)  // padded LDS row of a key (elements): 16 consecutive keys hit distinct banks
 #define AT_VLD (16 + 8)   // padded LDS row of one d within a page's transposed values
 
 template <int G, int SUB>
-__global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kb,
+__global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kb,
                                                     const bf16_t* __restrict__ vbt, const bf16_t* __restrict__ kpool,
                                                     const bf16_t* __restrict__ vpool, int layer, int n_pages,
                                                     const int32_t* __restrict__ pt, int max_pages,
                                                     const int32_t* __restrict__ ctx_len, int max_ctx,
-                                                    int chunk_tokens, int n_chunks, int L, int nq, int nkv,
+                                                    int chunk_tokens, int L, int nq, int nkv,
                                                     float* __restrict__ opart, float* __restrict__ mlpart,
                                                     uint32_t* err) {
     constexpr int D = 128;
@@ -79,27 +76,30 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int h = kvh * G + w;
-    const int C1 = n_chunks + 1;
+    const int C1 = gridDim.x;  // partial slots per (request, head): one per workgroup of the head
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     const size_t page_elems = (size_t)16 * D;
 
+    // context keys [t0, t1) of chunk c; chunk 0 also takes the block's own keys, as one extra round run first
+    // (no workgroup of its own for 16 keys)
     int t0 = 0, t1 = 0;
-    const bool block_chunk = (c == 0);
-    if (!block_chunk) {
+    {
         // page ids of the chunk (-1 past the table), loaded before the context length is known
-        const int pg0 = (c - 1) * (chunk_tokens / 16);
+        const int pg0 = c * (chunk_tokens / 16);
         for (int j = tid; j < chunk_tokens / 16; j += NT)
             spg[j] = pg0 + j < max_pages ? pt[(size_t)b * max_pages + pg0 + j] : -1;
         int ctx = ctx_len[b];
         if (ctx > max_ctx || ctx < 0) {
-            if (c == 1 && tid == 0) set_err(err, DFLASH_DEVERR_POS);
+            if (c == 0 && tid == 0) set_err(err, DFLASH_DEVERR_POS);
             ctx = ctx < 0 ? 0 : max_ctx;
         }
-        t0 = (c - 1) * chunk_tokens;
+        t0 = c * chunk_tokens;
         t1 = min(ctx, t0 + chunk_tokens);
-    } else {
-        t1 = L;
     }
+    const int nb = c == 0 ? 1 : 0;                            // block rounds
+    const int R = nb + (t0 < t1 ? (t1 - t0 + SUB - 1) / SUB : 0);  // rounds of this workgroup
+    auto is_blk = [&](int rr) { return rr < nb; };
+    auto ts_of = [&](int rr) { return rr < nb ? 0 : t0 + (rr - nb) * SUB; };
 
     const size_t bplane = (size_t)gridDim.z * nkv * page_elems;  // hi -> lo plane of the block's k / v
     const size_t qplane = (size_t)gridDim.z * L * nq * D;          // hi -> lo plane of q
@@ -108,18 +108,20 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
     // the per-thread offsets are compile-time constants and only the page bases change per sub-chunk.
     constexpr int PPP = 512 / NT;  // pieces per page per thread
     u32x4 pf[PPT];
-    uint32_t okmask = 0;
+    uint32_t okm = 0u;
     // Page slot e of the sub-chunk starting at key ts: its K and V^T bases always name readable memory (an
     // unmapped or out-of-range slot reads page 0 of the layer) and bit e of okmask says whether the slot
     // holds data.  Loads are issued unconditionally and the unmapped slots zeroed at stash time, so no
     // load has to wait for another.
-    auto prefetch = [&](int ts) {
-        okmask = 0;
+    auto prefetch = [&](int rr) {
+        const bool blk = is_blk(rr);
+        const int ts = ts_of(rr);
+        uint32_t okmask = 0;
 #pragma unroll
         for (int e = 0; e < NPG; ++e) {
             size_t kofs, vofs;
             bool ok;
-            if (block_chunk) {
+            if (blk) {
                 kofs = vofs = ((size_t)b * nkv + kvh) * page_elems + (e < 2 ? e : 0) * bplane;
                 ok = e < 2;
             } else {
@@ -129,21 +131,24 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
                 kofs = vofs = (((size_t)layer * n_pages + (ok ? page : 0)) * nkv + kvh) * page_elems;
             }
             okmask |= (ok ? 1u : 0u) << e;
-            const bf16_t* kbase = (block_chunk ? kb : kpool) + kofs;
-            const bf16_t* vbase = (block_chunk ? vbt : vpool) + vofs;
+            const bf16_t* kbase = (blk ? kb : kpool) + kofs;
+            const bf16_t* vbase = (blk ? vbt : vpool) + vofs;
 #pragma unroll
             for (int u = 0; u < PPP; ++u) {
                 const int qq = tid + u * NT;
                 pf[e * PPP + u] = ld16((qq < 256 ? kbase : vbase) + (qq & 255) * 8);
             }
         }
+        okm = okmask;
     };
-    auto stash = [&](int ts) {
-        okmask = __builtin_amdgcn_readfirstlane(okmask);  // the same in every lane: keep the branches scalar
+    auto stash = [&](int rr) {
+        const bool blk = is_blk(rr);
+        const int ts = ts_of(rr);
+        const uint32_t okmask = __builtin_amdgcn_readfirstlane(okm);  // the same in every lane: scalar branches
 #pragma unroll
         for (int e = 0; e < NPG; ++e) {
             const bool ok = (okmask >> e) & 1u;
-            const int nvalid = block_chunk ? L : t1 - (ts + 16 * e);
+            const int nvalid = blk ? L : t1 - (ts + 16 * e);
 #pragma unroll
             for (int u = 0; u < PPP; ++u) {
                 const int qq = tid + u * NT;
@@ -187,23 +192,24 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
     float m_run = -INFINITY, l_run = 0.f;
 
     __syncthreads();  // page ids in LDS
-    if (!block_chunk) {
-        // flag pages the chunk needs that lie beyond the table or outside the pool (their slots read as zero)
-        for (int j = tid; j < chunk_tokens / 16 && t0 + 16 * j < t1; j += NT) {
-            if ((t0 >> 4) + j >= max_pages) set_err(err, DFLASH_DEVERR_POS);
-            else if (spg[j] < 0 || spg[j] >= n_pages) set_err(err, DFLASH_DEVERR_PAGE);
-        }
+    // flag pages the chunk needs that lie beyond the table or outside the pool (their slots read as zero)
+    for (int j = tid; j < chunk_tokens / 16 && t0 + 16 * j < t1; j += NT) {
+        if ((t0 >> 4) + j >= max_pages) set_err(err, DFLASH_DEVERR_POS);
+        else if (spg[j] < 0 || spg[j] >= n_pages) set_err(err, DFLASH_DEVERR_PAGE);
     }
-    if (t0 < t1) prefetch(t0);
-    for (int ts = t0; ts < t1; ts += SUB) {
-        const int ts_staged = ts;
+    // round rr: the block's keys, or a sub-chunk of context keys starting at ts; the next round's loads are
+    // issued before the MFMAs of this one
+    if (R > 0) prefetch(0);
+    for (int rr = 0; rr < R; ++rr) {
+        const bool blk = is_blk(rr);
+        const int ts = ts_of(rr);
         __syncthreads();
-        stash(ts_staged);
+        stash(rr);
         __syncthreads();
-        if (ts + SUB < t1) prefetch(ts + SUB);
+        if (rr + 1 < R) prefetch(rr + 1);
         // scores S^T[key][query]: lane holds keys 4g+i of each page for query r
         float x[NPG][4];
-        if (block_chunk) {
+        if (blk) {
             // the block's keys: (K_hi + K_lo)(Q_hi + Q_lo)^T, keys in page slot 0 only
             f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
         // O^T += V^T P^T over the sub-chunk's 32-key slices; P enters as two bfloat16 terms (hi + lo)
 #pragma unroll
         for (int hk = 0; hk < NPG / 2; ++hk) {
-            if (ts + 32 * hk >= t1) break;  // uniform: the rest of the sub-chunk is masked
+            if (ts + 32 * hk >= (blk ? L : t1)) break;  // uniform: the rest of the round is masked
             u32x4 phi, plo;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(64 * G) void attn_bf16(const bf16_t* __restrict__ q
                 phi[j] = h2;
                 plo[j] = f2bf2(v0 - __uint_as_float(h2 << 16), v1 - __uint_as_float(h2 & 0xFFFF0000u));
             }
-            if (block_chunk) {
+            if (blk) {
                 // (V_hi + V_lo)^T over the block's keys (page slot 0 of the operand; slot 1 holds the lo plane)
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) {
@@ -347,6 +353,7 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ opar
     const int row = (item / nq) % L;
     const int b = item / (nq * L);
     const size_t base = ((size_t)b * nq + h) * C1;
+    const size_t base_o = ((size_t)(b * L + row) * nq + h) * d, plane = (size_t)B * L * nq * d;
     float M = -INFINITY;
     for (int c = lane; c < C1; c += 64) M = fmaxf(M, mlpart[((base + c) * 16 + row) * 2]);
     M = wave_max(M);
@@ -372,7 +379,6 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ opar
         __builtin_amdgcn_wave_barrier();
     }
     lsum = wave_sum(lsum);
-    const size_t base_o = ((size_t)(b * L + row) * nq + h) * d, plane = (size_t)B * L * nq * d;
     put_act(o, plane, base_o + lane, acc0 / lsum);
     put_act(o, plane, base_o + lane + 64, acc1 / lsum);
 }
@@ -454,12 +460,12 @@ hipError_t launch_attention(int bf16, const AttnPlan& p, int B, int L, int nq, i
                             int max_ctx, float* opart, float* mlpart, uint32_t* err, hipStream_t st) {
     if (bf16) {
         const int G = nq / nkv;
-        const dim3 grid(p.n_chunks + 1, nkv, B);
+        const dim3 grid(attn_slots(p), nkv, B);
         if (p.chunk_tokens % attn_sub(G) || p.chunk_tokens > 16 * AT_MAX_PAGES) return hipErrorInvalidValue;
 #define DF_ATTN(GG)                                                                                                \
     hipLaunchKernelGGL((attn_bf16<GG, 64>), grid, dim3(64 * GG), 0, st, (const bf16_t*)q, (const bf16_t*)kb,            \
                        (const bf16_t*)vbt, (const bf16_t*)kpool, (const bf16_t*)vpool, layer, n_pages, page_table, \
-                       max_pages, ctx_len, max_ctx, p.chunk_tokens, p.n_chunks, L, nq, nkv, opart, mlpart, err)
+                       max_pages, ctx_len, max_ctx, p.chunk_tokens, L, nq, nkv, opart, mlpart, err)
         switch (G) {
             case 1: DF_ATTN(1); break;
             case 2: DF_ATTN(2); break;
@@ -482,10 +488,10 @@ hipError_t launch_attn_merge(int bf16, const AttnPlan& p, int B, int L, int nq, 
     const long n = (long)B * L * nq;  // one wave each (d == 128)
     const dim3 grid((unsigned)((n + 3) / 4));
     if (bf16)
-        hipLaunchKernelGGL(attn_merge<bf16_t>, grid, dim3(256), 0, st, opart, mlpart, B, L, nq, d, p.n_chunks + 1,
+        hipLaunchKernelGGL(attn_merge<bf16_t>, grid, dim3(256), 0, st, opart, mlpart, B, L, nq, d, attn_slots(p),
                            (bf16_t*)o);
     else
-        hipLaunchKernelGGL(attn_merge<float>, grid, dim3(256), 0, st, opart, mlpart, B, L, nq, d, p.n_chunks + 1,
+        hipLaunchKernelGGL(attn_merge<float>, grid, dim3(256), 0, st, opart, mlpart, B, L, nq, d, attn_slots(p),
                            (float*)o);
     return hipGetLastError();
 }

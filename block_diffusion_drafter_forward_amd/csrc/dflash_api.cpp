@@ -340,7 +340,7 @@ static DraftPlan plan_draft(const dflash_config& c, int batch, int max_ctx) {
     p.o = cv.take((size_t)M * qd * ACT);
     p.a = cv.take((size_t)M * c.ffn * ACT);
     p.part = cv.take(part * 4);
-    const size_t C1 = (size_t)p.attn.n_chunks + 1;
+    const size_t C1 = (size_t)attn_slots(p.attn);
     if (bf) {
         p.opart = cv.take((size_t)batch * c.n_q_heads * C1 * 16 * c.head_dim * 4);
         p.ml = cv.take((size_t)batch * c.n_q_heads * C1 * 16 * 2 * 4);
