@@ -463,7 +463,7 @@ hipError_t launch_attention(int bf16, const AttnPlan& p, int B, int L, int nq, i
         const dim3 grid(attn_slots(p), nkv, B);
         if (p.chunk_tokens % attn_sub(G) || p.chunk_tokens > 16 * AT_MAX_PAGES) return hipErrorInvalidValue;
 #define DF_ATTN(GG)                                                                                                \
-    hipLaunchKernelGGL((attn_bf16<GG, 64>), grid, dim3(64 * GG), 0, st, (const bf16_t*)q, (const bf16_t*)kb,            \
+    DF_LAUNCH((attn_bf16<GG, 64>), grid, dim3(64 * GG), 0, st, (const bf16_t*)q, (const bf16_t*)kb,            \
                        (const bf16_t*)vbt, (const bf16_t*)kpool, (const bf16_t*)vpool, layer, n_pages, page_table, \
                        max_pages, ctx_len, max_ctx, p.chunk_tokens, L, nq, nkv, opart, mlpart, err)
         switch (G) {

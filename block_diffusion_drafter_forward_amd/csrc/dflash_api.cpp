@@ -228,6 +228,8 @@ extern "C" void dflash_destroy(dflash_handle* h) {
 // ---------------------------------------------------------------------------------------------------------
 // profiling
 // ---------------------------------------------------------------------------------------------------------
+thread_local LaunchTiming* df::df_launch_timing = nullptr;
+
 static hipEvent_t take_event(dflash_handle* h) {
     if (!h->event_pool.empty()) {
         hipEvent_t e = h->event_pool.back();
@@ -239,10 +241,14 @@ static hipEvent_t take_event(dflash_handle* h) {
     return e;
 }
 
+// One profiled launch.  The start event is recorded before the launch; a launcher that takes the events
+// (DF_LAUNCH) records both again around the kernel itself, otherwise the stop event is recorded after the
+// launch.
 struct Timed {
     dflash_handle* h;
     hipStream_t st;
     ProfEntry e{};
+    LaunchTiming lt{};
     bool on;
     Timed(dflash_handle* h_, const char* name, hipStream_t s, int N = 0, int K = 0)
         : h(h_), st(s), on(h_ && h_->profiling) {
@@ -252,10 +258,15 @@ struct Timed {
         e.start = take_event(h);
         e.stop = take_event(h);
         if (e.start) (void)hipEventRecord(e.start, st);
+        if (e.start && e.stop) {
+            lt = LaunchTiming{e.start, e.stop, false};
+            df_launch_timing = &lt;
+        }
     }
     ~Timed() {
         if (!on) return;
-        if (e.stop) (void)hipEventRecord(e.stop, st);
+        df_launch_timing = nullptr;
+        if (e.stop && !lt.used) (void)hipEventRecord(e.stop, st);
         if (e.start && e.stop) h->pending.push_back(e);
     }
 };

@@ -269,21 +269,21 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, const void* x, int ldx, size_t xp
     switch (p.kind) {
         case GEMM_SKINNY1:
             if (split)
-                hipLaunchKernelGGL((gemm_skinny_bf16<1, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
+                DF_LAUNCH((gemm_skinny_bf16<1, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
             else
-                hipLaunchKernelGGL((gemm_skinny_bf16<1, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
+                DF_LAUNCH((gemm_skinny_bf16<1, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
             break;
         case GEMM_SKINNY2:
             if (split)
-                hipLaunchKernelGGL((gemm_skinny_bf16<2, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
+                DF_LAUNCH((gemm_skinny_bf16<2, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
             else
-                hipLaunchKernelGGL((gemm_skinny_bf16<2, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
+                DF_LAUNCH((gemm_skinny_bf16<2, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
             break;
         case GEMM_TILED:
             if (split)
-                hipLaunchKernelGGL((gemm_tiled_bf16<true>), gt, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kps, part);
+                DF_LAUNCH((gemm_tiled_bf16<true>), gt, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kps, part);
             else
-                hipLaunchKernelGGL((gemm_tiled_bf16<false>), gt, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kps, part);
+                DF_LAUNCH((gemm_tiled_bf16<false>), gt, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kps, part);
             break;
         default:
             return hipErrorInvalidValue;

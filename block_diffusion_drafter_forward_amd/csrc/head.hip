@@ -322,16 +322,16 @@ hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V
     const RngKey key{(uint32_t)seed, (uint32_t)(seed >> 32)};
     const size_t zplane = (size_t)M * K;
     if (bf16 && M > 32)
-        hipLaunchKernelGGL(lm_head_tiled_bf16, dim3(grid.x, (M + TL_BM - 1) / TL_BM), dim3(256), 0, st,
+        DF_LAUNCH(lm_head_tiled_bf16, dim3(grid.x, (M + TL_BM - 1) / TL_BM), dim3(256), 0, st,
                            (const bf16_t*)z, zplane, M, (const bf16_t*)wlm, V, K, hpart, logits_dbg, key, sample);
     else if (!bf16)
         hipLaunchKernelGGL(lm_head_f32, grid, dim3(256), 0, st, (const float*)z, M, (const float*)wlm, V, K, hpart,
                            logits_dbg, key, sample);
     else if (M <= 16)
-        hipLaunchKernelGGL((lm_head_bf16<1, 4>), grid, dim3(256), 0, st, (const bf16_t*)z, zplane, M,
+        DF_LAUNCH((lm_head_bf16<1, 4>), grid, dim3(256), 0, st, (const bf16_t*)z, zplane, M,
                            (const bf16_t*)wlm, V, K, hpart, logits_dbg, key, sample);
     else
-        hipLaunchKernelGGL((lm_head_bf16<2, 4>), grid, dim3(256), 0, st, (const bf16_t*)z, zplane, M,
+        DF_LAUNCH((lm_head_bf16<2, 4>), grid, dim3(256), 0, st, (const bf16_t*)z, zplane, M,
                            (const bf16_t*)wlm, V, K, hpart, logits_dbg, key, sample);
     return hipGetLastError();
 }

@@ -1,12 +1,33 @@
 // Host-side launchers of the gfx950 kernels (one translation unit per kernel family).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "common.h"
 
 namespace df {
+
+// Per-kernel timing (the library's profiling mode): the host layer points df_launch_timing at a pair of
+// events around one launch; a launcher that supports it hands them to hipExtLaunchKernelGGL, which records
+// the kernel's own start and end (without the dispatch latency an event pair around the launch also
+// measures), and marks them used.  Launchers without it leave the events to the host layer's records.
+struct LaunchTiming {
+    hipEvent_t start, stop;
+    bool used;
+};
+extern thread_local LaunchTiming* df_launch_timing;
+#define DF_LAUNCH(kernel, grid, block, shmem, st, ...)                                                     \
+    do {                                                                                                   \
+        LaunchTiming* lt_ = df_launch_timing;                                                              \
+        if (lt_ && !lt_->used) {                                                                           \
+            lt_->used = true;                                                                              \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, lt_->start, lt_->stop, 0, __VA_ARGS__);  \
+        } else {                                                                                           \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);                               \
+        }                                                                                                  \
+    } while (0)
 
 // ---- GEMM ------------------------------------------------------------------------------------------------
 enum GemmKind { GEMM_SKINNY1 = 0, GEMM_SKINNY2 = 1, GEMM_TILED = 2, GEMM_F32 = 3 };
