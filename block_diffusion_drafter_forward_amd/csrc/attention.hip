@@ -23,11 +23,15 @@ AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx) {
     const int sub = attn_sub(n_q / n_kv);
     AttnPlan p{0, sub};
     if (max_ctx <= 0) return p;
-    // at most one workgroup per CU over (request, KV head, chunk): a CU that had to take a second
-    // workgroup would finish last (measured: 264 workgroups for 256 CUs ended ~3 us after the median);
-    // chunks of whole staging rounds and at most AT_MAX_PAGES pages
+    // one workgroup per CU over (request, KV head, chunk): a CU that had to take a second workgroup would
+    // finish last (measured: 264 workgroups for 256 CUs ended ~3 us after the median); chunks of whole
+    // staging rounds and at most AT_MAX_PAGES pages
     const int units = batch * n_kv;
     int want = 256 / units;
+    // Long contexts: two workgroups per CU, twice the loads in flight, each chunk still eight or more
+    // rounds long (measured on MI355X at 32768 tokens, 8 KV heads: 64 chunks instead of 32, -30 us per
+    // pass; at 4096 tokens one-round chunks are slower than two-round ones).
+    if (want > 0 && (long)max_ctx >= (long)want * sub * 8) want = 512 / units;
     const int max_chunks = (max_ctx + sub - 1) / sub;
     if (want > max_chunks) want = max_chunks;
     if (want < 1) want = 1;
