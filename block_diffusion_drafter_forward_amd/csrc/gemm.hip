@@ -47,25 +47,25 @@ hipError_t launch_pack(const Segs& src, int N, int K, void* dst, hipStream_t st)
 // ------------------------------------------------------------------------------------------------------
 // skinny MFMA GEMM (bfloat16), M <= 16 * MT, packed weights
 // ------------------------------------------------------------------------------------------------------
-// Workgroup = 4 waves on the same 64 output columns (4 n-tiles of 16); wave w takes the k-range
-// [k0 + w * kpw, k0 + (w + 1) * kpw) of the workgroup's split.  Per 256-wide k-chunk a wave loads, for each
+// Workgroup = W waves (4, or 8: see plan_gemm) on the same 64 output columns (4 n-tiles of 16); wave w takes
+// the k-range [k0 + w * kpw, k0 + (w + 1) * kpw) of the workgroup's split.  Per 256-wide k-chunk a wave loads, for each
 // n-tile, eight packed weight fragments (one coalesced 1 KB load each: the A operand, row = lane % 16,
 // k = 32 j + 8 (lane / 16)) and the matching eight 16-byte pieces of its activation row (B operand), then
 // issues 8 MFMAs per (n-tile, m-tile).  With SPLIT the activation is a pair of bfloat16 planes (x = hi + lo,
 // lo plane at x + xplane) and every weight fragment meets both: two MFMAs, one weight load; at one m-tile
 // the hi and lo products go to separate accumulators so that the two MFMAs do not wait on each other.
-template <int MT, bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict__ x, int ldx, size_t xplane, int M,
-                                                        const bf16_t* __restrict__ wp, int N, int K, int kpw,
-                                                        float* __restrict__ part) {
+template <int MT, bool SPLIT, int W>
+__global__ __launch_bounds__(64 * W) void gemm_skinny_bf16(const bf16_t* __restrict__ x, int ldx, size_t xplane, int M,
+                                                           const bf16_t* __restrict__ wp, int N, int K, int kpw,
+                                                           float* __restrict__ part) {
     constexpr int NT = 4;
     constexpr bool SEP = SPLIT && MT == 1;
-    __shared__ f32x4 red[4][NT * MT][64];
+    __shared__ f32x4 red[W][NT * MT][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * 64;
     const int s = blockIdx.y;
-    const int kb = s * 4 * kpw + wave * kpw;
+    const int kb = s * W * kpw + wave * kpw;
     const int ke = min(K, kb + kpw);
     // this workgroup's four n-tiles are group blockIdx.x of the chunk-major packed matrix: per k-chunk one
     // contiguous 32 KB block, n-tile nt at fragment 8 nt of it
@@ -124,12 +124,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict
         }
     __syncthreads();
 
-    for (int e = threadIdx.x; e < NT * MT * 64; e += 256) {
+    for (int e = threadIdx.x; e < NT * MT * 64; e += 64 * W) {
         const int t = e >> 6, l = e & 63;
         const int nt = t / MT, mt = t % MT;
         f32x4 v = red[0][t][l];
 #pragma unroll
-        for (int q = 1; q < 4; ++q) {
+        for (int q = 1; q < W; ++q) {
             f32x4 u = red[q][t][l];
             v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
         }
@@ -246,6 +246,18 @@ GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K, bool few_splits) {
             }
         }
         p.splits = (K + 4 * p.kpw - 1) / (4 * p.kpw);
+        p.waves = 4;
+        // Eight-wave workgroups, one chunk per wave, where that gives one generation of 192 to 256
+        // workgroups (at most one per CU) and four-wave ones would leave some CUs with two: measured on
+        // MI355X for the QKV shape (6144 x 4096: 192 instead of 384 workgroups), 11.4 us instead of 12.0 in
+        // isolation, and half the split partials for its epilogue.
+        if (few_splits && M <= 16 && p.kpw == 256 && K % 2048 == 0) {  // (two m-tiles would spill)
+            const int w8 = groups * (K / 2048);
+            if (w8 >= 192 && w8 <= 256 && wgs(256) % 256 != 0) {
+                p.waves = 8;
+                p.splits = K / 2048;
+            }
+        }
         return p;
     }
     p.kind = GEMM_TILED;
@@ -268,17 +280,20 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, const void* x, int ldx, size_t xp
     const bf16_t* wp = (const bf16_t*)wpacked;
     switch (p.kind) {
         case GEMM_SKINNY1:
-            if (split)
-                DF_LAUNCH((gemm_skinny_bf16<1, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
-            else
-                DF_LAUNCH((gemm_skinny_bf16<1, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
+        case GEMM_SKINNY2: {
+            const dim3 block(64 * p.waves);
+#define DF_SKINNY(MT, SP, W) DF_LAUNCH((gemm_skinny_bf16<MT, SP, W>), gs, block, 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part)
+            const int mt = p.kind == GEMM_SKINNY1 ? 1 : 2;
+            if (p.waves == 8) {
+                if (mt != 1) return hipErrorInvalidValue;
+                if (split) DF_SKINNY(1, true, 8); else DF_SKINNY(1, false, 8);
+            } else {
+                if (mt == 1) { if (split) DF_SKINNY(1, true, 4); else DF_SKINNY(1, false, 4); }
+                else { if (split) DF_SKINNY(2, true, 4); else DF_SKINNY(2, false, 4); }
+            }
+#undef DF_SKINNY
             break;
-        case GEMM_SKINNY2:
-            if (split)
-                DF_LAUNCH((gemm_skinny_bf16<2, true>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
-            else
-                DF_LAUNCH((gemm_skinny_bf16<2, false>), gs, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part);
-            break;
+        }
         case GEMM_TILED:
             if (split)
                 DF_LAUNCH((gemm_tiled_bf16<true>), gt, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kps, part);

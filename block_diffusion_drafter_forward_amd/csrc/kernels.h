@@ -35,6 +35,7 @@ struct GemmPlan {
     int kind;
     int splits;  // number of float32 partial products written (grid split of K)
     int kpw;     // skinny: k-range per wave (multiple of 256)
+    int waves;   // skinny: waves per workgroup (4 or 8)
     int kps;     // tiled: k-range per split (multiple of 64)
 };
 // few_splits: prefer fewer, longer k-ranges per wave (set for the drafter layer's GEMMs, where it was measured
