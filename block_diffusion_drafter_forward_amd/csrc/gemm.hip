@@ -157,7 +157,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict_
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int wn = wave >> 1, wm = wave & 1;
-    const int n0 = blockIdx.x * TL_BN, m0 = blockIdx.y * TL_BM, s = blockIdx.z;
+    int tx, ty;
+    if (!xcd_tile(blockIdx.x, (N + TL_BN - 1) / TL_BN, (M + TL_BM - 1) / TL_BM, tx, ty)) return;
+    const int n0 = tx * TL_BN, m0 = ty * TL_BM, s = blockIdx.y;
     const int kb = s * kps, ke = min(K, kb + kps);
     f32x4 acc[4][4];
     tiled_mainloop<SPLIT>(x, ldx, xplane, M, wp, N, K, n0, m0, kb, ke, sw, sx, acc);
@@ -275,7 +277,7 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, const void* x, int ldx, size_t xp
                             int N, int K, float* part, hipStream_t st) {
     const bool split = xplane != 0;
     const dim3 gs((N + 63) / 64, p.splits);
-    const dim3 gt((N + TL_BN - 1) / TL_BN, (M + TL_BM - 1) / TL_BM, p.splits);
+    const dim3 gt(xcd_tile_count((N + TL_BN - 1) / TL_BN, (M + TL_BM - 1) / TL_BM), p.splits);
     const bf16_t* xb = (const bf16_t*)x;
     const bf16_t* wp = (const bf16_t*)wpacked;
     switch (p.kind) {

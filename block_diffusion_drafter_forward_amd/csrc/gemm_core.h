@@ -32,6 +32,19 @@ __host__ __device__ inline size_t frag_index(size_t t, int s, size_t G) {
 // next k-tile is fetched into registers while the current one is consumed from LDS (one barrier pair per
 // k-tile).  The weight tile is 16 packed fragments, copied to LDS as they are (conflict-free 1 KB reads per
 // MFMA operand); activation rows are padded to 72 elements in LDS to spread the 16-byte reads over the banks.
+// Tile (x = n-tile, y = m-tile) of workgroup `bid` of a one-dimensional grid of xcd_tile_count(gx, gy)
+// workgroups.  Workgroups are dispatched to the eight XCDs round-robin, so workgroups i and i + 8 run on the
+// same XCD at about the same time: the m-tiles of one n-tile are placed 8 apart, and the second one finds the
+// weight tile in that XCD's L2 instead of reading it from HBM again.  Returns false for the padding
+// workgroups of the last column of eight.
+__device__ __forceinline__ bool xcd_tile(int bid, int gx, int gy, int& x, int& y) {
+    const int rest = bid >> 3;
+    y = rest % gy;
+    x = (rest / gy) * 8 + (bid & 7);
+    return x < gx;
+}
+__host__ __device__ inline int xcd_tile_count(int gx, int gy) { return (gx + 7) / 8 * 8 * gy; }
+
 #define TL_BN 128
 #define TL_BM 128
 #define TL_BK 64

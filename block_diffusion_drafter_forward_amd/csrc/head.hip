@@ -297,7 +297,9 @@ __global__ __launch_bounds__(256) void lm_head_tiled_bf16(const bf16_t* __restri
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int wn = wave >> 1, wm = wave & 1;
-    const int n0 = blockIdx.x * TL_BN, m0 = blockIdx.y * TL_BM;
+    int tx, ty;
+    if (!xcd_tile(blockIdx.x, (V + TL_BN - 1) / TL_BN, (M + TL_BM - 1) / TL_BM, tx, ty)) return;
+    const int n0 = tx * TL_BN, m0 = ty * TL_BM;
     f32x4 acc[4][4];
     tiled_mainloop<true>(z, K, zplane, M, W, V, K, n0, m0, 0, K, sw, sx, acc);
     __syncthreads();  // staging buffers are dead from here on: reuse them for the logits tile
@@ -313,7 +315,7 @@ __global__ __launch_bounds__(256) void lm_head_tiled_bf16(const bf16_t* __restri
             lg[m][n + 3] = acc[a][b][3];
         }
     __syncthreads();
-    head_epilogue<128, 128>(lg, min(128, M - m0), m0, M, n0, V, blockIdx.x, hpart, logits_dbg, key, sample);
+    head_epilogue<128, 128>(lg, min(128, M - m0), m0, M, n0, V, tx, hpart, logits_dbg, key, sample);
 }
 
 hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V, int K, float* hpart,
@@ -322,7 +324,7 @@ hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V
     const RngKey key{(uint32_t)seed, (uint32_t)(seed >> 32)};
     const size_t zplane = (size_t)M * K;
     if (bf16 && M > 32)
-        DF_LAUNCH(lm_head_tiled_bf16, dim3(grid.x, (M + TL_BM - 1) / TL_BM), dim3(256), 0, st,
+        DF_LAUNCH(lm_head_tiled_bf16, dim3(xcd_tile_count(grid.x, (M + TL_BM - 1) / TL_BM)), dim3(256), 0, st,
                            (const bf16_t*)z, zplane, M, (const bf16_t*)wlm, V, K, hpart, logits_dbg, key, sample);
     else if (!bf16)
         hipLaunchKernelGGL(lm_head_f32, grid, dim3(256), 0, st, (const float*)z, M, (const float*)wlm, V, K, hpart,
