@@ -265,7 +265,14 @@ GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K, bool few_splits) {
     p.kind = GEMM_TILED;
     const int tiles = ((N + TL_BN - 1) / TL_BN) * ((M + TL_BM - 1) / TL_BM);
     const int kt = (K + TL_BK - 1) / TL_BK;
-    int splits = tiles >= 256 ? 1 : (384 + tiles - 1) / tiles;
+    // The tiled kernel is MFMA-bound at serving sizes, so what counts is an even share per CU: below 512
+    // tiles, split K (powers of two) until every split has at most 32 k-tiles and there are 256 or more
+    // workgroups.  Measured on MI355X at M = 256 (Qwen3-8B shapes): gate/up 2 splits, QKV 4, O 4, down 8,
+    // 200 us per drafter pass less than aiming at ~384 workgroups; more splits cost more in partial traffic
+    // than they gain in balance.
+    int splits = 1;
+    if (tiles < 512)
+        while (splits < 16 && (kt > 32 * splits || tiles * splits < 256)) splits *= 2;
     if (splits > kt / 4) splits = kt / 4 > 0 ? kt / 4 : 1;
     int kps_tiles = (kt + splits - 1) / splits;
     p.kps = kps_tiles * TL_BK;
