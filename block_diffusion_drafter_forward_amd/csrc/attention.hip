@@ -19,10 +19,16 @@ namespace df {
 // with 128-key chunks beat 128-key rounds (fewer registers, two rounds to overlap load and compute).
 static int attn_sub(int) { return 64; }
 
-AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx) {
+AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx, int n_layers) {
     const int sub = attn_sub(n_q / n_kv);
-    AttnPlan p{0, sub};
+    AttnPlan p{0, sub, 0};
     if (max_ctx <= 0) return p;
+    // The weights are streamed with non-temporal loads, so a pass's cached K/V that fit in the 256 MB Infinity
+    // Cache stay there from one pass to the next and are read with ordinary loads; larger caches are streamed
+    // non-temporally like the weights (measured on MI355X: LLaMA-3.1-8B shape at 32768 tokens, 671 MB of K/V
+    // per pass, -14 us per pass; Qwen3-8B shape at 4096 tokens, 84 MB, +7 us if streamed).
+    const double kv_bytes = (double)n_layers * batch * max_ctx * n_kv * 128 * 2 * 2;
+    p.stream_kv = kv_bytes > 128.0 * (1 << 20) ? 1 : 0;
     // one workgroup per CU over (request, KV head, chunk): a CU that had to take a second workgroup would
     // finish last (measured: 264 workgroups for 256 CUs ended ~3 us after the median); chunks of whole
     // staging rounds and at most AT_MAX_PAGES pages
@@ -59,7 +65,7 @@ AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx) {
 #define AT_KLD (128 + 8)  // padded LDS row of a key (elements): 16 consecutive keys hit distinct banks
 #define AT_VLD (16 + 8)   // padded LDS row of one d within a page's transposed values
 
-template <int G, int SUB>
+template <int G, int SUB, bool NTKV>
 __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kb,
                                                     const bf16_t* __restrict__ vbt, const bf16_t* __restrict__ kpool,
                                                     const bf16_t* __restrict__ vpool, int layer, int n_pages,
@@ -140,7 +146,8 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
 #pragma unroll
             for (int u = 0; u < PPP; ++u) {
                 const int qq = tid + u * NT;
-                pf[e * PPP + u] = ld16((qq < 256 ? kbase : vbase) + (qq & 255) * 8);
+                const bf16_t* src = (qq < 256 ? kbase : vbase) + (qq & 255) * 8;
+                pf[e * PPP + u] = NTKV ? ld16_nt(src) : ld16(src);
             }
         }
         okm = okmask;
@@ -466,10 +473,15 @@ hipError_t launch_attention(int bf16, const AttnPlan& p, int B, int L, int nq, i
         const int G = nq / nkv;
         const dim3 grid(attn_slots(p), nkv, B);
         if (p.chunk_tokens % attn_sub(G) || p.chunk_tokens > 16 * AT_MAX_PAGES) return hipErrorInvalidValue;
-#define DF_ATTN(GG)                                                                                                \
-    DF_LAUNCH((attn_bf16<GG, 64>), grid, dim3(64 * GG), 0, st, (const bf16_t*)q, (const bf16_t*)kb,            \
-                       (const bf16_t*)vbt, (const bf16_t*)kpool, (const bf16_t*)vpool, layer, n_pages, page_table, \
-                       max_pages, ctx_len, max_ctx, p.chunk_tokens, L, nq, nkv, opart, mlpart, err)
+#define DF_ATTN_NT(GG, NT)                                                                                         \
+    DF_LAUNCH((attn_bf16<GG, 64, NT>), grid, dim3(64 * GG), 0, st, (const bf16_t*)q, (const bf16_t*)kb,        \
+              (const bf16_t*)vbt, (const bf16_t*)kpool, (const bf16_t*)vpool, layer, n_pages, page_table,       \
+              max_pages, ctx_len, max_ctx, p.chunk_tokens, L, nq, nkv, opart, mlpart, err)
+#define DF_ATTN(GG)                 \
+    if (p.stream_kv)                \
+        DF_ATTN_NT(GG, true);       \
+    else                            \
+        DF_ATTN_NT(GG, false)
         switch (G) {
             case 1: DF_ATTN(1); break;
             case 2: DF_ATTN(2); break;
@@ -478,6 +490,7 @@ hipError_t launch_attention(int bf16, const AttnPlan& p, int B, int L, int nq, i
             default: return hipErrorInvalidValue;
         }
 #undef DF_ATTN
+#undef DF_ATTN_NT
     } else {
         // writes o (float32) straight into opart's storage; no merge step
         hipLaunchKernelGGL(attn_f32, dim3(L, nq, B), dim3(64), 0, st, (const float*)q, (const float*)kb,

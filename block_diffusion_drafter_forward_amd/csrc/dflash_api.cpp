@@ -336,7 +336,7 @@ static DraftPlan plan_draft(const dflash_config& c, int batch, int max_ctx) {
     p.oproj = plan_gemm(bf, M, c.hidden, qd, true);
     p.gateup = plan_gemm(bf, M, 2 * c.ffn, c.hidden, true);
     p.down = plan_gemm(bf, M, c.hidden, c.ffn, true);
-    p.attn = plan_attention(batch, c.n_q_heads, c.n_kv_heads, max_ctx);
+    p.attn = plan_attention(batch, c.n_q_heads, c.n_kv_heads, max_ctx, c.n_layers);
     size_t part = (size_t)p.qkv.splits * M * (qd + 2 * kvd);
     part = std::max(part, (size_t)p.oproj.splits * M * c.hidden);
     part = std::max(part, (size_t)p.gateup.splits * M * 2 * c.ffn);

@@ -85,10 +85,11 @@ hipError_t launch_copy(void* dst, const void* src, size_t n16, hipStream_t st);
 struct AttnPlan {
     int n_chunks;      // context chunks (chunk 0 also takes the block's own keys)
     int chunk_tokens;  // multiple of the kernel's staging round (64 or 128 keys)
+    int stream_kv;     // cached K/V read with non-temporal loads (the pass's K/V exceed half the Infinity Cache)
 };
 // workgroups (and partial slots) per (request, KV head): one per chunk, one without context
 inline int attn_slots(const AttnPlan& p) { return p.n_chunks > 0 ? p.n_chunks : 1; }
-AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx);
+AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx, int n_layers);
 hipError_t launch_attention(int bf16, const AttnPlan& p, int B, int L, int nq, int nkv, int d, const void* q,
                             const void* kb, const void* vbt, const void* kpool, const void* vpool, int layer,
                             int n_pages, const int32_t* page_table, int max_pages, const int32_t* ctx_len,
