@@ -63,7 +63,11 @@ AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx, int n_layers)
 // bfloat16.  The block round stages its hi page in page slot 0 and its lo page in slot 1 and multiplies
 // every pair of terms.
 #define AT_KLD (128 + 8)  // padded LDS row of a key (elements): 16 consecutive keys hit distinct banks
-#define AT_VLD (16 + 8)   // padded LDS row of one d within a page's transposed values
+// Values in LDS: one row per (32-key slice hk, d) holding the slice's two pages interleaved by groups of four
+// slots, [g][page 2 hk + pp][4 slots] (g = slot / 4), so that the 16 bytes a lane needs for the V^T operand
+// (slots 4g..4g+3 of both pages) are one aligned LDS read; rows padded to 80 bytes spread a wave's reads over
+// the banks.
+#define AT_SVLD (32 + 8)
 
 template <int G, int SUB, bool NTKV>
 __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kb,
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
     constexpr int PIECES = NPG * 512;    // 16-byte pieces per sub-chunk: per page 256 of K and 256 of V^T
     constexpr int PPT = PIECES / NT;
     __shared__ __attribute__((aligned(16))) bf16_t sk[SUB * AT_KLD];
-    __shared__ __attribute__((aligned(16))) bf16_t sv[NPG * D * AT_VLD];
+    __shared__ __attribute__((aligned(16))) bf16_t sv[(NPG / 2) * D * AT_SVLD];
     __shared__ int spg[AT_MAX_PAGES];
     const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -179,7 +183,11 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
                             v[j] &= m;
                         }
                     }
-                    *(u32x4*)(sv + (e * D + (q2 >> 1)) * AT_VLD + (q2 & 1) * 8) = v;
+                    // piece q2 = slots 8 h .. 8 h + 7 of row d: groups g = 2 h and 2 h + 1
+                    const int half = q2 & 1;
+                    bf16_t* row = sv + ((e >> 1) * D + (q2 >> 1)) * AT_SVLD + (e & 1) * 4;
+                    *(u32x2*)(row + (2 * half) * 8) = u32x2{v[0], v[1]};
+                    *(u32x2*)(row + (2 * half + 1) * 8) = u32x2{v[2], v[3]};
                 }
             }
         }
@@ -306,31 +314,30 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
                 phi[j] = h2;
                 plo[j] = f2bf2(v0 - __uint_as_float(h2 << 16), v1 - __uint_as_float(h2 & 0xFFFF0000u));
             }
-            if (blk) {
-                // (V_hi + V_lo)^T over the block's keys (page slot 0 of the operand; slot 1 holds the lo plane)
+            // four d-tiles' operands at a time, then their MFMAs term by term (independent accumulators back to
+            // back; each tile still adds its terms in the same order)
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) {
-                    const int d = dt * 16 + r;
-                    const u32x2 vh = *(const u32x2*)(sv + (0 * D + d) * AT_VLD + 4 * g);
-                    const u32x2 vl = *(const u32x2*)(sv + (1 * D + d) * AT_VLD + 4 * g);
-                    const u32x4 fh = u32x4{vh[0], vh[1], 0u, 0u};
-                    const u32x4 fl = u32x4{vl[0], vl[1], 0u, 0u};
-                    o[dt] = mfma16(fh, phi, o[dt]);
-                    o[dt] = mfma16(fh, plo, o[dt]);
-                    o[dt] = mfma16(fl, phi, o[dt]);
-                    o[dt] = mfma16(fl, plo, o[dt]);
+            for (int d0 = 0; d0 < 8; d0 += 4) {
+                u32x4 vf[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) vf[u] = ld16(sv + (hk * D + (d0 + u) * 16 + r) * AT_SVLD + g * 8);
+                if (blk) {
+                    // (V_hi + V_lo)^T over the block's keys: the hi plane is page 0 of the slice, the lo plane page 1
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const u32x4 f = t < 2 ? u32x4{vf[u][0], vf[u][1], 0u, 0u} : u32x4{vf[u][2], vf[u][3], 0u, 0u};
+                            o[d0 + u] = mfma16(f, (t & 1) ? plo : phi, o[d0 + u]);
+                        }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) o[d0 + u] = mfma16(vf[u], phi, o[d0 + u]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) o[d0 + u] = mfma16(vf[u], plo, o[d0 + u]);
                 }
-                break;
             }
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const int d = dt * 16 + r;
-                const u32x2 va = *(const u32x2*)(sv + ((2 * hk) * D + d) * AT_VLD + 4 * g);
-                const u32x2 vb = *(const u32x2*)(sv + ((2 * hk + 1) * D + d) * AT_VLD + 4 * g);
-                const u32x4 vf = u32x4{va[0], va[1], vb[0], vb[1]};
-                o[dt] = mfma16(vf, phi, o[dt]);
-                o[dt] = mfma16(vf, plo, o[dt]);
-            }
+            if (blk) break;
         }
     }
 
