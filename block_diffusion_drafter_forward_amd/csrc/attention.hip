@@ -1,7 +1,8 @@
 // Block attention over [injected context ; block] (non-causal), grouped-query, paged context.
 //
 // Work split: one workgroup per (request, KV head, chunk of the request's cached context); chunk 0 also
-// takes the block's own 16-slot K/V page, as its first round.  Wave w of the workgroup serves query
+// takes the block's own 16 keys, straight from registers while its first context round is in flight.  Wave
+// w of the workgroup serves query
 // head kv_head * G + w (G = query heads per KV head), whose L block rows form one 16-row MFMA tile.  Per pair
 // of 16-key pages the wave computes S^T = K Q^T (keys in rows, so a lane's four scores belong to one query
 // row), updates an online softmax in the log2 domain, and accumulates O^T = V^T P^T.  Values are cached
@@ -60,8 +61,9 @@ AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx, int n_layers)
 // key and pages the table does not map are staged as zeros, so uninitialised cache memory can never reach
 // the MFMAs.
 // q and the block's own k / v are activation pairs (hi + lo bfloat16 planes); the cached K/V are plain
-// bfloat16.  The block round stages its hi page in page slot 0 and its lo page in slot 1 and multiplies
-// every pair of terms.
+// bfloat16.  The block's keys are attended first (every pair of hi / lo terms), from operands each lane
+// loads itself at the start, so they add no staging round: chunk 0 then takes as many rounds as the
+// other chunks, and its block step overlaps the wait for its first context round.
 #define AT_KLD (128 + 8)  // padded LDS row of a key (elements): 16 consecutive keys hit distinct banks
 // Values in LDS: one row per (32-key slice hk, d) holding the slice's two pages interleaved by groups of four
 // slots, [g][page 2 hk + pp][4 slots] (g = slot / 4), so that the 16 bytes a lane needs for the V^T operand
@@ -94,14 +96,63 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     const size_t page_elems = (size_t)16 * D;
 
-    // context keys [t0, t1) of chunk c; chunk 0 also takes the block's own keys, as one extra round run first
-    // (no workgroup of its own for 16 keys)
+    const size_t qplane = (size_t)gridDim.z * L * nq * D;         // hi -> lo plane of q
+    const size_t bplane = (size_t)gridDim.z * nkv * page_elems;  // hi -> lo plane of the block's k / v
+    // The chunk's page ids are requested first and only they are waited for before the first K/V round is
+    // issued; q and, in chunk 0, the block's own k / v (requested once the ids are in LDS) arrive meanwhile.
+    constexpr int PGT = (AT_MAX_PAGES + NT - 1) / NT;  // page ids per thread
+    const int npg = chunk_tokens / 16, pg0 = c * npg;
+    int pgv[PGT];
+#pragma unroll
+    for (int u = 0; u < PGT; ++u) {
+        const int j = tid + u * NT;
+        // every load is issued (from a clamped index) so that the waits below count exactly these loads
+        pgv[u] = pt[(size_t)b * max_pages + min(pg0 + j, max_pages - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the page-id loads ahead of the q loads
+    // Q^T operand: lane supplies query row r (zero beyond L), eight d-values per 32-wide k-step
+    u32x4 qf[4], ql[4];
+    {
+        const bool ok = r < L;
+        const bf16_t* qp = q + ((size_t)(b * L + (ok ? r : 0)) * nq + h) * D + g * 8;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            qf[s] = ld16(qp + s * 32);  // unconditional loads (row 0 for rows past L), zeroed below
+            ql[s] = ld16(qp + qplane + s * 32);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {
+                qf[s][w4] = ok ? qf[s][w4] : 0u;
+                ql[s][w4] = ok ? ql[s][w4] : 0u;
+            }
+    }
+#pragma unroll
+    for (int u = 0; u < PGT; ++u) {
+        const int j = tid + u * NT;
+        // (stored for every j < AT_MAX_PAGES, -1 past the chunk: an unconditional use keeps the load where it is)
+        if (NT * PGT <= AT_MAX_PAGES || j < AT_MAX_PAGES) spg[j] = j < npg && pg0 + j < max_pages ? pgv[u] : -1;
+    }
+    // chunk 0: the block's K operand (lane: key slot r, d = 32 s + 8 g ..) and V^T operand (lane: d = 16 dt + r,
+    // slots 4 g .. 4 g + 3), hi and lo planes
+    u32x4 bk[2][4];
+    u32x2 bv[2][8];
+    if (c == 0) {
+        const bf16_t* kr = kb + (((size_t)b * nkv + kvh) * 16 + r) * D + g * 8;
+        const bf16_t* vr = vbt + ((size_t)b * nkv + kvh) * page_elems + (size_t)r * 16 + 4 * g;
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) bk[pl][s] = ld16(kr + pl * bplane + s * 32);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) bv[pl][dt] = *(const u32x2*)(vr + pl * bplane + (size_t)dt * 16 * 16);
+        }
+    }
+
+    // context keys [t0, t1) of chunk c
     int t0 = 0, t1 = 0;
     {
-        // page ids of the chunk (-1 past the table), loaded before the context length is known
-        const int pg0 = c * (chunk_tokens / 16);
-        for (int j = tid; j < chunk_tokens / 16; j += NT)
-            spg[j] = pg0 + j < max_pages ? pt[(size_t)b * max_pages + pg0 + j] : -1;
         int ctx = ctx_len[b];
         if (ctx > max_ctx || ctx < 0) {
             if (c == 0 && tid == 0) set_err(err, DFLASH_DEVERR_POS);
@@ -110,13 +161,9 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
         t0 = c * chunk_tokens;
         t1 = min(ctx, t0 + chunk_tokens);
     }
-    const int nb = c == 0 ? 1 : 0;                            // block rounds
-    const int R = nb + (t0 < t1 ? (t1 - t0 + SUB - 1) / SUB : 0);  // rounds of this workgroup
-    auto is_blk = [&](int rr) { return rr < nb; };
-    auto ts_of = [&](int rr) { return rr < nb ? 0 : t0 + (rr - nb) * SUB; };
+    const int R = t0 < t1 ? (t1 - t0 + SUB - 1) / SUB : 0;  // context rounds of this workgroup
+    auto ts_of = [&](int rr) { return t0 + rr * SUB; };
 
-    const size_t bplane = (size_t)gridDim.z * nkv * page_elems;  // hi -> lo plane of the block's k / v
-    const size_t qplane = (size_t)gridDim.z * L * nq * D;          // hi -> lo plane of q
     // Staging: a page is 512 16-byte pieces (256 of K, then 256 of V^T), and piece j of either half sits at
     // element 8 j of its page, so thread tid moves pieces tid, tid + NT, ... of every page of the sub-chunk:
     // the per-thread offsets are compile-time constants and only the page bases change per sub-chunk.
@@ -128,25 +175,17 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
     // holds data.  Loads are issued unconditionally and the unmapped slots zeroed at stash time, so no
     // load has to wait for another.
     auto prefetch = [&](int rr) {
-        const bool blk = is_blk(rr);
         const int ts = ts_of(rr);
         uint32_t okmask = 0;
 #pragma unroll
         for (int e = 0; e < NPG; ++e) {
-            size_t kofs, vofs;
-            bool ok;
-            if (blk) {
-                kofs = vofs = ((size_t)b * nkv + kvh) * page_elems + (e < 2 ? e : 0) * bplane;
-                ok = e < 2;
-            } else {
-                const int tp = ts + 16 * e;
-                const int page = tp < t1 ? spg[(tp - t0) >> 4] : -1;
-                ok = page >= 0 && page < n_pages;
-                kofs = vofs = (((size_t)layer * n_pages + (ok ? page : 0)) * nkv + kvh) * page_elems;
-            }
+            const int tp = ts + 16 * e;
+            const int page = tp < t1 ? spg[(tp - t0) >> 4] : -1;
+            const bool ok = page >= 0 && page < n_pages;
+            const size_t ofs = (((size_t)layer * n_pages + (ok ? page : 0)) * nkv + kvh) * page_elems;
             okmask |= (ok ? 1u : 0u) << e;
-            const bf16_t* kbase = (blk ? kb : kpool) + kofs;
-            const bf16_t* vbase = (blk ? vbt : vpool) + vofs;
+            const bf16_t* kbase = kpool + ofs;
+            const bf16_t* vbase = vpool + ofs;
 #pragma unroll
             for (int u = 0; u < PPP; ++u) {
                 const int qq = tid + u * NT;
@@ -157,13 +196,12 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
         okm = okmask;
     };
     auto stash = [&](int rr) {
-        const bool blk = is_blk(rr);
         const int ts = ts_of(rr);
         const uint32_t okmask = __builtin_amdgcn_readfirstlane(okm);  // the same in every lane: scalar branches
 #pragma unroll
         for (int e = 0; e < NPG; ++e) {
             const bool ok = (okmask >> e) & 1u;
-            const int nvalid = blk ? L : t1 - (ts + 16 * e);
+            const int nvalid = t1 - (ts + 16 * e);
 #pragma unroll
             for (int u = 0; u < PPP; ++u) {
                 const int qq = tid + u * NT;
@@ -193,17 +231,6 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
         }
     };
 
-    // Q^T operand: lane supplies query row r (zero beyond L), eight d-values per 32-wide k-step
-    u32x4 qf[4], ql[4];
-    {
-        const bool ok = r < L;
-        const bf16_t* qp = q + ((size_t)(b * L + (ok ? r : 0)) * nq + h) * D + g * 8;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            qf[s] = ok ? ld16(qp + s * 32) : u32x4{0u, 0u, 0u, 0u};
-            ql[s] = ok ? ld16(qp + qplane + s * 32) : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
 
     f32x4 o[8];
 #pragma unroll
@@ -216,11 +243,60 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
         if ((t0 >> 4) + j >= max_pages) set_err(err, DFLASH_DEVERR_POS);
         else if (spg[j] < 0 || spg[j] >= n_pages) set_err(err, DFLASH_DEVERR_PAGE);
     }
-    // round rr: the block's keys, or a sub-chunk of context keys starting at ts; the next round's loads are
-    // issued before the MFMAs of this one
-    if (R > 0) prefetch(0);
+    prefetch(0);  // always issued (a chunk without keys reads page 0, never stashed): the block step below waits only for its own loads
+    if (c == 0) {
+        // the block's keys (L of the 16 slots): S = (K_hi + K_lo)(Q_hi + Q_lo)^T in one accumulator chain, then
+        // the first online-softmax step, then O^T = (V_hi + V_lo)^T P^T with P = P_hi + P_lo; values of slots
+        // past L are zeroed (they may hold anything)
+        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                sa = mfma16(bk[pl][s], qf[s], sa);
+                sa = mfma16(bk[pl][s], ql[s], sa);
+            }
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = 4 * g + i < L ? sa[i] * scale_log2 : -INFINITY;
+        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // L >= 1, so every row has a finite maximum
+        m_run = mx;
+        float p4[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p4[i] = __builtin_amdgcn_exp2f(x[i] - mx);
+            psum += p4[i];
+        }
+        l_run = psum;
+        u32x4 phi = u32x4{0u, 0u, 0u, 0u}, plo = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float v0 = p4[2 * j], v1 = p4[2 * j + 1];
+            const uint32_t h2 = f2bf2(v0, v1);
+            phi[j] = h2;
+            plo[j] = f2bf2(v0 - __uint_as_float(h2 << 16), v1 - __uint_as_float(h2 & 0xFFFF0000u));
+        }
+        uint32_t vm[2];
+#pragma unroll
+        for (int wd = 0; wd < 2; ++wd) {
+            const int s0 = 4 * g + 2 * wd;
+            vm[wd] = (s0 < L ? 0x0000FFFFu : 0u) | (s0 + 1 < L ? 0xFFFF0000u : 0u);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const u32x2 v = bv[t >> 1][dt];
+                o[dt] = mfma16(u32x4{v[0] & vm[0], v[1] & vm[1], 0u, 0u}, (t & 1) ? plo : phi, o[dt]);
+            }
+    }
+    // round rr: the sub-chunk of context keys starting at ts; the next round's loads are issued before the
+    // MFMAs of this one
     for (int rr = 0; rr < R; ++rr) {
-        const bool blk = is_blk(rr);
         const int ts = ts_of(rr);
         __syncthreads();
         stash(rr);
@@ -228,53 +304,32 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
         if (rr + 1 < R) prefetch(rr + 1);
         // scores S^T[key][query]: lane holds keys 4g+i of each page for query r
         float x[NPG][4];
-        if (blk) {
-            // the block's keys: (K_hi + K_lo)(Q_hi + Q_lo)^T, keys in page slot 0 only
-            f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
+        // every page's tile first (independent MFMA chains; hi and lo query terms in separate
+        // accumulators), then scale, and mask only in a sub-chunk that runs past the chunk's end
+        f32x4 sh[NPG], sl[NPG];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const bf16_t* kr = sk + (e * 16 + r) * AT_KLD + g * 8;
+        for (int e = 0; e < NPG; ++e) {
+            sh[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sl[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const u32x4 kf = ld16(kr + s * 32);
-                    sa = mfma16(kf, qf[s], sa);
-                    sa = mfma16(kf, ql[s], sa);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[0][i] = 4 * g + i < L ? sa[i] * scale_log2 : -INFINITY;
-#pragma unroll
-                for (int e = 1; e < NPG; ++e) x[e][i] = -INFINITY;
-            }
-        } else {
-            // every page's tile first (independent MFMA chains; hi and lo query terms in separate
-            // accumulators), then scale, and mask only in a sub-chunk that runs past the chunk's end
-            f32x4 sh[NPG], sl[NPG];
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int e = 0; e < NPG; ++e) {
-                sh[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-                sl[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const u32x4 kf = ld16(sk + (e * 16 + r) * AT_KLD + g * 8 + s * 32);
+                sh[e] = mfma16(kf, qf[s], sh[e]);
+                sl[e] = mfma16(kf, ql[s], sl[e]);
             }
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+        for (int e = 0; e < NPG; ++e)
 #pragma unroll
-                for (int e = 0; e < NPG; ++e) {
-                    const u32x4 kf = ld16(sk + (e * 16 + r) * AT_KLD + g * 8 + s * 32);
-                    sh[e] = mfma16(kf, qf[s], sh[e]);
-                    sl[e] = mfma16(kf, ql[s], sl[e]);
-                }
+            for (int i = 0; i < 4; ++i) x[e][i] = (sh[e][i] + sl[e][i]) * scale_log2;
+        if (ts + SUB > t1) {
+            const int nk = t1 - ts;
 #pragma unroll
             for (int e = 0; e < NPG; ++e)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[e][i] = (sh[e][i] + sl[e][i]) * scale_log2;
-            if (ts + SUB > t1) {
-                const int nk = t1 - ts;
-#pragma unroll
-                for (int e = 0; e < NPG; ++e)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) x[e][i] = 16 * e + 4 * g + i < nk ? x[e][i] : -INFINITY;
-            }
+                for (int i = 0; i < 4; ++i) x[e][i] = 16 * e + 4 * g + i < nk ? x[e][i] : -INFINITY;
         }
         float mx = -INFINITY;
 #pragma unroll
@@ -305,7 +360,7 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
         // O^T += V^T P^T over the sub-chunk's 32-key slices; P enters as two bfloat16 terms (hi + lo)
 #pragma unroll
         for (int hk = 0; hk < NPG / 2; ++hk) {
-            if (ts + 32 * hk >= (blk ? L : t1)) break;  // uniform: the rest of the round is masked
+            if (ts + 32 * hk >= t1) break;  // uniform: the rest of the round is masked
             u32x4 phi, plo;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -321,23 +376,11 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
                 u32x4 vf[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) vf[u] = ld16(sv + (hk * D + (d0 + u) * 16 + r) * AT_SVLD + g * 8);
-                if (blk) {
-                    // (V_hi + V_lo)^T over the block's keys: the hi plane is page 0 of the slice, the lo plane page 1
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
+                for (int u = 0; u < 4; ++u) o[d0 + u] = mfma16(vf[u], phi, o[d0 + u]);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const u32x4 f = t < 2 ? u32x4{vf[u][0], vf[u][1], 0u, 0u} : u32x4{vf[u][2], vf[u][3], 0u, 0u};
-                            o[d0 + u] = mfma16(f, (t & 1) ? plo : phi, o[d0 + u]);
-                        }
-                } else {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) o[d0 + u] = mfma16(vf[u], phi, o[d0 + u]);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) o[d0 + u] = mfma16(vf[u], plo, o[d0 + u]);
-                }
+                for (int u = 0; u < 4; ++u) o[d0 + u] = mfma16(vf[u], plo, o[d0 + u]);
             }
-            if (blk) break;
         }
     }
 
