@@ -12,6 +12,12 @@
 namespace df {
 
 #define HEAD_REC 20  // max, sumexp, 8 values, 8 ids (as int bits), sampled score and id (temperature 1 only)
+// Field order: the first 16-byte word holds what the merge's first pass needs, (max, sumexp, 8th value,
+// sampled score); then values 1..7 and the sampled id; then the 8 ids.
+__host__ __device__ constexpr int hr_val(int j) { return j == DF_TOPK - 1 ? 2 : 4 + j; }  // value j (best first)
+__host__ __device__ constexpr int hr_id(int j) { return 12 + j; }                          // id j
+#define HR_SSC 3   // sampled score
+#define HR_SID 11  // sampled id
 // Records are stored per group, hpart[(group * rows + row) * HEAD_REC + field]: the records a workgroup of the
 // LM head writes are one contiguous block (80 bytes per block row), so its stores fill whole cache lines.
 
@@ -152,12 +158,12 @@ __device__ void head_epilogue(const float (*lg)[C + 1], int rows, int row0, int 
         dst[1] = se;
 #pragma unroll
         for (int j = 0; j < DF_TOPK; ++j) {
-            dst[2 + j] = s.v[j];
-            dst[2 + DF_TOPK + j] = __int_as_float(s.id[j]);
+            dst[hr_val(j)] = s.v[j];
+            dst[hr_id(j)] = __int_as_float(s.id[j]);
         }
         if (sample) {
-            dst[2 + 2 * DF_TOPK] = bs;
-            dst[3 + 2 * DF_TOPK] = __int_as_float(bi);
+            dst[HR_SSC] = bs;
+            dst[HR_SID] = __int_as_float(bi);
         }
     }
 }
@@ -386,35 +392,44 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
     float mx = -INFINITY, th = -INFINITY;
     float sb = -INFINITY;  // temperature 1: best (perturbed score, id) over the records
     int sbi = 0x7FFFFFFF;
-    // A record is five 16-byte words (80 bytes, 16-byte aligned): word 0 holds (max, sumexp, v0, v1), word 2
-    // (v6, v7, id0, id1), word 4 (id6, id7, sampled score, sampled id).  The first MERGE_GROUPS of a thread's groups are
-    // fetched with their loads in flight together, and their (max, sumexp) kept for the second pass.
+    // A record is five 16-byte words (80 bytes, 16-byte aligned); word 0 holds (max, sumexp, 8th value, sampled
+    // score) and word 2 ends with the sampled id.  The first MERGE_GROUPS of a thread's groups are fetched with
+    // their loads in flight together (one word each, two at temperature 1), and their (max, sumexp) kept for the
+    // second pass.
     constexpr int MERGE_GROUPS = 4;
+    // (every load is issued, a thread past the last group reading group 0, so that all are in flight before the
+    // first is used)
     float4 w0[MERGE_GROUPS];
+    int sid[MERGE_GROUPS];
 #pragma unroll
     for (int u = 0; u < MERGE_GROUPS; ++u) {
         const int gi = t + u * MERGE_THREADS;
-        w0[u] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
-        float4 w2 = make_float4(0.f, -INFINITY, 0.f, 0.f), w4 = make_float4(-INFINITY, 0.f, 0.f, 0.f);
-        if (gi < n_groups) {
-            const float4* rec = (const float4*)(row + gi * RS);
-            w0[u] = rec[0];
-            w2 = rec[2];
-            if (sample) w4 = rec[4];
+        w0[u] = *(const float4*)(row + (size_t)(gi < n_groups ? gi : 0) * RS);
+    }
+    if (sample) {
+#pragma unroll
+        for (int u = 0; u < MERGE_GROUPS; ++u) {
+            const int gi = t + u * MERGE_THREADS;
+            sid[u] = __float_as_int(row[(size_t)(gi < n_groups ? gi : 0) * RS + HR_SID]);
         }
+    }
+#pragma unroll
+    for (int u = 0; u < MERGE_GROUPS; ++u) {
+        const bool ok = t + u * MERGE_THREADS < n_groups;
+        if (!ok) w0[u] = make_float4(-INFINITY, 0.f, -INFINITY, -INFINITY);
         mx = fmaxf(mx, w0[u].x);
-        th = fmaxf(th, w2.y);  // the record's 8th value
-        if (sample && gi < n_groups && df_better(w4.z, __float_as_int(w4.w), sb, sbi)) {  // fields 18, 19
-            sb = w4.z;
-            sbi = __float_as_int(w4.w);
+        th = fmaxf(th, w0[u].z);  // the record's 8th value
+        if (sample && ok && df_better(w0[u].w, sid[u], sb, sbi)) {
+            sb = w0[u].w;
+            sbi = sid[u];
         }
     }
     for (int gi = t + MERGE_GROUPS * MERGE_THREADS; gi < n_groups; gi += MERGE_THREADS) {  // very large vocabularies
         mx = fmaxf(mx, row[gi * RS]);
-        th = fmaxf(th, row[gi * RS + (2 + DF_TOPK - 1)]);
+        th = fmaxf(th, row[gi * RS + hr_val(DF_TOPK - 1)]);
         if (sample) {
-            const float v = row[gi * RS + (2 + 2 * DF_TOPK)];
-            const int id = __float_as_int(row[gi * RS + (3 + 2 * DF_TOPK)]);
+            const float v = row[gi * RS + HR_SSC];
+            const int id = __float_as_int(row[gi * RS + HR_SID]);
             if (df_better(v, id, sb, sbi)) {
                 sb = v;
                 sbi = id;
@@ -461,8 +476,8 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
         if (r0 != -INFINITY) se += r1 * expf(r0 - mx);
         if (r0 >= th) {  // the record's best entry reaches the threshold: scan its list
             for (int j = 0; j < DF_TOPK; ++j) {
-                const float v = row[gi * RS + (2 + j)];
-                const int id = __float_as_int(row[gi * RS + (2 + DF_TOPK + j)]);
+                const float v = row[gi * RS + hr_val(j)];
+                const int id = __float_as_int(row[gi * RS + hr_id(j)]);
                 if (v < th) break;
                 if (id < V) {
                     const int k = atomicAdd(&cnt, 1);
@@ -497,8 +512,8 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
             int oid[DF_TOPK];
 #pragma unroll
             for (int j = 0; j < DF_TOPK; ++j) {
-                ov[j] = row[gi * RS + (2 + j)];
-                oid[j] = __float_as_int(row[gi * RS + (2 + DF_TOPK + j)]);
+                ov[j] = row[gi * RS + hr_val(j)];
+                oid[j] = __float_as_int(row[gi * RS + hr_id(j)]);
             }
             s.merge(ov, oid);
         }
