@@ -31,6 +31,25 @@ __device__ __forceinline__ float split_sum(const float* p, size_t stride, int S)
     }
     return acc;
 }
+// The same sums for NP columns (offsets col[c] from p) at once: every column's loads of a batch are issued
+// before the first add.
+template <int NP>
+__device__ __forceinline__ void split_sums(const float* p, const int (&col)[NP], size_t stride, int S, float (&acc)[NP]) {
+#pragma unroll
+    for (int c = 0; c < NP; ++c) acc[c] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += SPLIT_BATCH) {
+        float v[NP][SPLIT_BATCH];
+#pragma unroll
+        for (int u = 0; u < SPLIT_BATCH; ++u)
+#pragma unroll
+            for (int c = 0; c < NP; ++c) v[c][u] = s0 + u < S ? p[(size_t)(s0 + u) * stride + col[c]] : 0.f;
+#pragma unroll
+        for (int u = 0; u < SPLIT_BATCH; ++u)
+            if (s0 + u < S)
+#pragma unroll
+                for (int c = 0; c < NP; ++c) acc[c] += v[c][u];
+    }
+}
 __device__ __forceinline__ void st4(float* p, float4 v) { *(float4*)p = v; }
 // float4 split sums starting from split 0 (no +0 first), batched like split_sum
 __device__ __forceinline__ float4 split_sum4(const float* p, size_t stride, int S) {
@@ -72,16 +91,17 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) { return make_float4(
 __device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
 
 // u = RMSNorm(v) * g for the row values held in registers (u stored as an activation pair)
+// (gv: the gains of this thread's columns, loaded with the row values)
 template <typename T>
-__device__ __forceinline__ void norm_store(const float4 (&v)[ROW_PASSES], float ss, int H, const T* __restrict__ gain,
-                                           float eps, T* __restrict__ urow, size_t plane, float* red) {
+__device__ __forceinline__ void norm_store(const float4 (&v)[ROW_PASSES], const float4 (&gv)[ROW_PASSES], float ss,
+                                           int H, float eps, T* __restrict__ urow, size_t plane, float* red) {
     ss = block_sum(ss, red);
     const float rs = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
     for (int q = 0; q < ROW_PASSES; ++q) {
         const int j = (threadIdx.x + q * ROW_THREADS) * 4;
         if (j >= H) break;
-        const float4 g = ld4(gain + j);
+        const float4 g = gv[q];
         st4_act(urow + j, plane,
                 make_float4(v[q].x * rs * g.x, v[q].y * rs * g.y, v[q].z * rs * g.z, v[q].w * rs * g.w));
     }
@@ -101,18 +121,19 @@ __global__ __launch_bounds__(ROW_THREADS) void embed_norm(const int32_t* __restr
     int t = tok[m];
     if (t < 0 || t >= V) t = 0;
     const T* e = embed + (size_t)t * H;
-    float4 v[ROW_PASSES];
+    float4 v[ROW_PASSES], gv[ROW_PASSES];
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < ROW_PASSES; ++q) {
         const int j = (threadIdx.x + q * ROW_THREADS) * 4;
         if (j >= H) break;
+        gv[q] = ld4(gain + j);
         v[q] = ld4(e + j);
         st4(h + (size_t)m * H + j, v[q]);
         if (tap) st4(tap + (size_t)m * H + j, v[q]);
         ss += dot4(v[q]);
     }
-    norm_store(v, ss, H, gain, eps, u + (size_t)m * H, (size_t)gridDim.x * H, red);
+    norm_store(v, gv, ss, H, eps, u + (size_t)m * H, (size_t)gridDim.x * H, red);
 }
 
 hipError_t launch_embed_norm(int bf16, const int32_t* tok, int M, int V, const void* embed, const void* gain, int H,
@@ -133,19 +154,22 @@ __global__ __launch_bounds__(ROW_THREADS) void resid_norm(const float* __restric
                                                           T* __restrict__ u, float* __restrict__ tap) {
     __shared__ float red[ROW_THREADS / 64];
     const int m = blockIdx.x;
-    float4 v[ROW_PASSES];
+    float4 v[ROW_PASSES], gv[ROW_PASSES];
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < ROW_PASSES; ++q) {
         const int j = (threadIdx.x + q * ROW_THREADS) * 4;
         if (j >= H) break;
+        // the residual and the gains are requested with the splits: one round trip
+        gv[q] = ld4(gain + j);
+        const float4 hv = ld4(h + (size_t)m * H + j);
         const float4 a = split_sum4(part + (size_t)m * H + j, (size_t)M * H, S);
-        v[q] = add4(ld4(h + (size_t)m * H + j), a);
+        v[q] = add4(hv, a);
         st4(h + (size_t)m * H + j, v[q]);
         if (tap) st4(tap + (size_t)m * H + j, v[q]);
         ss += dot4(v[q]);
     }
-    norm_store(v, ss, H, gain, eps, u + (size_t)m * H, (size_t)M * H, red);
+    norm_store(v, gv, ss, H, eps, u + (size_t)m * H, (size_t)M * H, red);
 }
 
 hipError_t launch_resid_norm(int bf16, const float* part, int S, int M, int H, float* h, const void* gain, float eps,
@@ -162,7 +186,7 @@ hipError_t launch_resid_norm(int bf16, const float* part, int S, int M, int H, f
 // ------------------------------------------------------------------------------------------------------
 // QKV epilogue
 // ------------------------------------------------------------------------------------------------------
-// One thread per (block row m, head, rotary pair i): sums the splits of columns i and i + d/2, applies the
+// One thread per (block row m = grid y, head, rotary pair i): sums the splits of columns i and i + d/2, applies the
 // rotation at position ctx_len[b] + row to q and k heads, rounds, and stores q row-major, the block's keys as
 // a 16-slot page [b][kv head][slot][d] and its values transposed [b][kv head][d][slot].
 template <typename T>
@@ -173,22 +197,26 @@ __global__ __launch_bounds__(256) void qkv_epilogue(const float* __restrict__ pa
     const int heads = nq + 2 * nkv;
     const int M = B * L;
     const int N = heads * d;
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (long)M * heads * half) return;
-    const int i = idx % half;
-    const int hd = (idx / half) % heads;
-    const int m = idx / ((long)half * heads);
+    const int x = blockIdx.x * 256 + threadIdx.x;  // (32-bit index arithmetic: no 64-bit division)
+    if (x >= heads * half) return;
+    const int i = x % half;
+    const int hd = x / half;
+    const int m = blockIdx.y;
     const int c1 = hd * d + i, c2 = c1 + half;
-    const float a = split_sum(part + (size_t)m * N + c1, (size_t)M * N, S);
-    const float c = split_sum(part + (size_t)m * N + c2, (size_t)M * N, S);
-    qkv_store(a, c, m, hd, i, B, L, nq, nkv, d, ctx_len, rf, q, kb, vbt);
+    // the context length and the frequency are requested before the splits and first used after them
+    const int ctx = ctx_len[m / L];
+    const float inv = rf.inv[i];
+    const int col[2] = {c1, c2};
+    float sum[2];
+    split_sums<2>(part + (size_t)m * N, col, (size_t)M * N, S, sum);
+    qkv_store(sum[0], sum[1], m, hd, i, B, L, nq, nkv, d, ctx + m % L, rf.on != 0, inv, q, kb, vbt);
 }
 
 hipError_t launch_qkv_epilogue(int bf16, const float* part, int S, int B, int L, int nq, int nkv, int d,
                                const int32_t* ctx_len, const RopeFreq& rf, void* q, void* kb, void* vbt,
                                hipStream_t st) {
-    const long n = (long)B * L * (nq + 2 * nkv) * (d / 2);
-    const dim3 grid((unsigned)((n + 255) / 256));
+    const int n = (nq + 2 * nkv) * (d / 2);
+    const dim3 grid((unsigned)((n + 255) / 256), (unsigned)(B * L));
     if (bf16)
         hipLaunchKernelGGL(qkv_epilogue<bf16_t>, grid, dim3(256), 0, st, part, S, B, L, nq, nkv, d, ctx_len, rf,
                            (bf16_t*)q, (bf16_t*)kb, (bf16_t*)vbt);
@@ -204,18 +232,18 @@ hipError_t launch_qkv_epilogue(int bf16, const float* part, int S, int B, int L,
 template <typename T>
 __global__ __launch_bounds__(256) void swiglu(const float* __restrict__ part, int S, int M, int F,
                                               T* __restrict__ a) {
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (long)M * F) return;
-    const int m = idx / F, j = idx % F;
+    const int j = blockIdx.x * 256 + threadIdx.x, m = blockIdx.y;  // column, row (grid y)
+    if (j >= F) return;
+    const size_t idx = (size_t)m * F + j;
     const size_t N = 2 * (size_t)F;
-    const float g = split_sum(part + (size_t)m * N + j, (size_t)M * N, S);
-    const float up = split_sum(part + (size_t)m * N + F + j, (size_t)M * N, S);
-    put_act(a, (size_t)M * F, idx, swiglu_value(g, up));
+    const int col[2] = {j, F + j};
+    float sum[2];
+    split_sums<2>(part + (size_t)m * N, col, (size_t)M * N, S, sum);
+    put_act(a, (size_t)M * F, idx, swiglu_value(sum[0], sum[1]));
 }
 
 hipError_t launch_swiglu(int bf16, const float* part, int S, int M, int F, void* a, hipStream_t st) {
-    const long n = (long)M * F;
-    const dim3 grid((unsigned)((n + 255) / 256));
+    const dim3 grid((unsigned)((F + 255) / 256), (unsigned)M);
     if (bf16) hipLaunchKernelGGL(swiglu<bf16_t>, grid, dim3(256), 0, st, part, S, M, F, (bf16_t*)a);
     else hipLaunchKernelGGL(swiglu<float>, grid, dim3(256), 0, st, part, S, M, F, (float*)a);
     return hipGetLastError();
@@ -226,19 +254,20 @@ template <typename T>
 __global__ __launch_bounds__(256) void reduce_cast(const float* __restrict__ part, int S, int M, int N,
                                                    const T* __restrict__ bias, T* __restrict__ out,
                                                    uint32_t* clear_err) {
-    if (clear_err && blockIdx.x == 0 && threadIdx.x == 0) *clear_err = 0u;
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (long)M * N) return;
-    const int n = idx % N;
+    if (clear_err && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *clear_err = 0u;
+    const int n = blockIdx.x * 256 + threadIdx.x;  // column; the row is grid y
+    if (n >= N) return;
+    const size_t idx = (size_t)blockIdx.y * N + n;
+    T braw{};
+    if (bias) braw = bias[n];  // requested before the splits, converted after them
     float v = split_sum(part + idx, (size_t)M * N, S);
-    if (bias) v += Act<T>::load(bias + n);
+    if (bias) v += Act<T>::load(&braw);
     put_act(out, (size_t)M * N, idx, v);
 }
 
 hipError_t launch_reduce_cast(int bf16, const float* part, int S, int M, int N, const void* bias, void* out,
                               uint32_t* clear_err, hipStream_t st) {
-    const long n = (long)M * N;
-    const dim3 grid((unsigned)((n + 255) / 256));
+    const dim3 grid((unsigned)((N + 255) / 256), (unsigned)M);
     if (bf16)
         hipLaunchKernelGGL(reduce_cast<bf16_t>, grid, dim3(256), 0, st, part, S, M, N, (const bf16_t*)bias,
                            (bf16_t*)out, clear_err);
@@ -262,13 +291,20 @@ __global__ __launch_bounds__(256) void kv_scatter(const float* __restrict__ part
                                                   T* __restrict__ kpool, T* __restrict__ vpool, RopeFreq rf,
                                                   uint32_t* err) {
     const int half = d >> 1;
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (long)rows * n_layers * nkv * half) return;
-    const int i = idx % half;
-    const int kh = (idx / half) % nkv;
-    const int l = (idx / ((long)half * nkv)) % n_layers;
-    const int j = idx / ((long)half * nkv * n_layers);
+    const int x = blockIdx.x * 256 + threadIdx.x;  // (layer, kv head, rotary pair); the row is grid y
+    if (x >= n_layers * nkv * half) return;
+    const int i = x % half;
+    const int kh = (x / half) % nkv;
+    const int l = x / (half * nkv);
+    const int j = blockIdx.y;
     const int R = row0 + j;
+    // the split sums first (they depend only on the row), so that their loads overlap the request's lookup
+    const int N = n_layers * 2 * nkv * d;
+    const int ck = l * 2 * nkv * d + kh * d + i;
+    const int cv = ck + nkv * d;
+    const int col[4] = {ck, ck + half, cv, cv + half};
+    float sum[4];
+    split_sums<4>(part + (size_t)j * N, col, (size_t)rows * N, S, sum);
     if (R >= off[batch]) return;  // padding rows: computed, not stored
     int lo = 0, hi = batch - 1;
     while (lo < hi) {  // last r with off[r] <= R
@@ -292,13 +328,8 @@ __global__ __launch_bounds__(256) void kv_scatter(const float* __restrict__ part
         if (i == 0 && kh == 0 && l == 0) set_err(err, DFLASH_DEVERR_PAGE);
         return;
     }
-    const int N = n_layers * 2 * nkv * d;
-    const int ck = l * 2 * nkv * d + kh * d + i;
-    const int cv = ck + nkv * d;
-    const float* p = part + (size_t)j * N;
-    const size_t stride = (size_t)rows * N;
-    float k1 = split_sum(p + ck, stride, S), k2 = split_sum(p + ck + half, stride, S);
-    const float v1 = split_sum(p + cv, stride, S), v2 = split_sum(p + cv + half, stride, S);
+    float k1 = sum[0], k2 = sum[1];
+    const float v1 = sum[2], v2 = sum[3];
     rope_pair(k1, k2, pos, i, rf);
     const size_t pg = ((size_t)(layer0 + l) * n_pages + page) * nkv + kh;
     T* kd = kpool + (pg * 16 + slot) * d;
@@ -313,8 +344,8 @@ hipError_t launch_kv_scatter(int bf16, const float* part, int S, int rows, int r
                              int nkv, int d, int batch, const int32_t* row_offsets, const int32_t* start_pos,
                              const int32_t* page_table, int max_pages, int n_pages, void* kpool, void* vpool,
                              const RopeFreq& rf, uint32_t* err, hipStream_t st) {
-    const long n = (long)rows * n_layers * nkv * (d / 2);
-    const dim3 grid((unsigned)((n + 255) / 256));
+    const int n = n_layers * nkv * (d / 2);
+    const dim3 grid((unsigned)((n + 255) / 256), (unsigned)rows);
     if (bf16)
         hipLaunchKernelGGL(kv_scatter<bf16_t>, grid, dim3(256), 0, st, part, S, rows, row0, layer0, n_layers, nkv, d,
                            batch,

@@ -5,35 +5,36 @@
 #include "common.h"
 
 // ---- rotary embedding and the q / block K / block V^T stores ----------------------------------------------
-__device__ __forceinline__ void rope_pair(float& a, float& b, int pos, int i, const RopeFreq& rf) {
-    if (!rf.on) return;
-    const float ang = (float)pos * rf.inv[i];
+__device__ __forceinline__ void rope_pair_inv(float& a, float& b, int pos, float inv) {
+    const float ang = (float)pos * inv;
     float sn, cs;
     sincosf(ang, &sn, &cs);
     const float x1 = a, x2 = b;
     a = x1 * cs - x2 * sn;
     b = x2 * cs + x1 * sn;
 }
+__device__ __forceinline__ void rope_pair(float& a, float& b, int pos, int i, const RopeFreq& rf) {
+    if (rf.on) rope_pair_inv(a, b, pos, rf.inv[i]);
+}
 
 // Rotary pair i (head columns i and i + d/2) of stacked head hd (q heads, then k, then v) for block row m:
-// rotation at position ctx_len[b] + row for q and k; q stored row-major [m][nq][d], the block's keys as a
-// 16-slot page [b][kv head][slot][d] and its values transposed [b][kv head][d][slot].
+// rotation at position pos (= ctx_len[b] + row) with inverse frequency inv (rope: rotation on) for q and k; q
+// stored row-major [m][nq][d], the block's keys as a 16-slot page [b][kv head][slot][d] and its values
+// transposed [b][kv head][d][slot].
 template <typename T>
 __device__ __forceinline__ void qkv_store(float a, float c, int m, int hd, int i, int B, int L, int nq, int nkv,
-                                          int d, const int32_t* __restrict__ ctx_len, const RopeFreq& rf, T* q, T* kb,
-                                          T* vbt) {
+                                          int d, int pos, bool rope, float inv, T* q, T* kb, T* vbt) {
     const int half = d >> 1;
     const int b = m / L, row = m % L;
-    const int pos = ctx_len[b] + row;
     const size_t qplane = (size_t)B * L * nq * d, bplane = (size_t)B * nkv * 16 * d;
     if (hd < nq) {
-        rope_pair(a, c, pos, i, rf);
+        if (rope) rope_pair_inv(a, c, pos, inv);
         const size_t o = (size_t)m * nq * d + hd * d + i;
         put_act(q, qplane, o, a);
         put_act(q, qplane, o + half, c);
     } else if (hd < nq + nkv) {
         const int kh = hd - nq;
-        rope_pair(a, c, pos, i, rf);
+        if (rope) rope_pair_inv(a, c, pos, inv);
         const size_t o = (((size_t)b * nkv + kh) * 16 + row) * d + i;
         put_act(kb, bplane, o, a);
         put_act(kb, bplane, o + half, c);
