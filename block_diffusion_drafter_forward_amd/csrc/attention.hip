@@ -2,13 +2,13 @@
 //
 // Work split: one workgroup per (request, KV head, chunk of the request's cached context); chunk 0 also
 // takes the block's own 16 keys, straight from registers while its first context round is in flight.  Wave
-// w of the workgroup serves query
-// head kv_head * G + w (G = query heads per KV head), whose L block rows form one 16-row MFMA tile.  Per pair
-// of 16-key pages the wave computes S^T = K Q^T (keys in rows, so a lane's four scores belong to one query
-// row), updates an online softmax in the log2 domain, and accumulates O^T = V^T P^T.  Values are cached
-// transposed inside each page ([d][slot]) so that the V^T operand is two 8-byte loads per lane, and the
-// probabilities enter the MFMA as P = P_hi + P_lo (two bfloat16 terms), which keeps them float32-exact.
-// Each chunk writes (m, l, O) partials; attn_merge combines the chunks in a fixed order.
+// w of the workgroup serves query head kv_head * G + w (G = query heads per KV head), whose L block rows form
+// one 16-row MFMA tile.  Per pair of 16-key pages the wave computes S^T = K Q^T (keys in rows, so a lane's
+// four scores belong to one query row), updates an online softmax in the log2 domain, and accumulates
+// O^T = V^T P^T.  Values are cached transposed inside each page ([d][slot]) and staged so that a lane's V^T
+// operand is one 16-byte LDS read; the probabilities enter the MFMA as P = P_hi + P_lo (two bfloat16 terms),
+// which keeps them float32-exact.  Each chunk writes (m, l, O) partials; attn_merge combines the chunks in a
+// fixed order.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,7 +27,7 @@ AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx, int n_layers)
     // The weights are streamed with non-temporal loads, so a pass's cached K/V that fit in the 256 MB Infinity
     // Cache stay there from one pass to the next and are read with ordinary loads; larger caches are streamed
     // non-temporally like the weights (measured on MI355X: LLaMA-3.1-8B shape at 32768 tokens, 671 MB of K/V
-    // per pass, -14 us per pass; Qwen3-8B shape at 4096 tokens, 84 MB, +7 us if streamed).
+    // per pass, -8.5 us per pass; Qwen3-8B shape at 4096 tokens, 84 MB, +6.6 us if streamed).
     const double kv_bytes = (double)n_layers * batch * max_ctx * n_kv * 128 * 2 * 2;
     p.stream_kv = kv_bytes > 128.0 * (1 << 20) ? 1 : 0;
     // one workgroup per CU over (request, KV head, chunk): a CU that had to take a second workgroup would
