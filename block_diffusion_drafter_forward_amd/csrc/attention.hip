@@ -106,8 +106,9 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
 #pragma unroll
     for (int u = 0; u < PGT; ++u) {
         const int j = tid + u * NT;
-        // every load is issued (from a clamped index) so that the waits below count exactly these loads
-        pgv[u] = pt[(size_t)b * max_pages + min(pg0 + j, max_pages - 1)];
+        // every load is issued (from a clamped index; without a page table, from ctx_len) so that the waits
+        // below count exactly these loads
+        pgv[u] = *(max_pages > 0 ? pt + (size_t)b * max_pages + min(pg0 + j, max_pages - 1) : ctx_len);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the page-id loads ahead of the q loads
     // Q^T operand: lane supplies query row r (zero beyond L), eight d-values per 32-wide k-step
@@ -171,9 +172,9 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
     u32x4 pf[PPT];
     uint32_t okm = 0u;
     // Page slot e of the sub-chunk starting at key ts: its K and V^T bases always name readable memory (an
-    // unmapped or out-of-range slot reads page 0 of the layer) and bit e of okmask says whether the slot
-    // holds data.  Loads are issued unconditionally and the unmapped slots zeroed at stash time, so no
-    // load has to wait for another.
+    // unmapped or out-of-range slot, or a round past the chunk, reads the block's own k / v page, which every
+    // call has) and bit e of okmask says whether the slot holds data.  Loads are issued unconditionally and
+    // the unmapped slots zeroed at stash time, so no load has to wait for another.
     auto prefetch = [&](int rr) {
         const int ts = ts_of(rr);
         uint32_t okmask = 0;
@@ -184,8 +185,8 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
             const bool ok = page >= 0 && page < n_pages;
             const size_t ofs = (((size_t)layer * n_pages + (ok ? page : 0)) * nkv + kvh) * page_elems;
             okmask |= (ok ? 1u : 0u) << e;
-            const bf16_t* kbase = kpool + ofs;
-            const bf16_t* vbase = vpool + ofs;
+            const bf16_t* kbase = ok ? kpool + ofs : kb;
+            const bf16_t* vbase = ok ? vpool + ofs : vbt;
 #pragma unroll
             for (int u = 0; u < PPP; ++u) {
                 const int qq = tid + u * NT;
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
         if ((t0 >> 4) + j >= max_pages) set_err(err, DFLASH_DEVERR_POS);
         else if (spg[j] < 0 || spg[j] >= n_pages) set_err(err, DFLASH_DEVERR_PAGE);
     }
-    prefetch(0);  // always issued (a chunk without keys reads page 0, never stashed): the block step below waits only for its own loads
+    prefetch(0);  // always issued (a chunk without keys reads the block page, never stashed): the block step below waits only for its own loads
     if (c == 0) {
         // the block's keys (L of the 16 slots): S = (K_hi + K_lo)(Q_hi + Q_lo)^T in one accumulator chain, then
         // the first online-softmax step, then O^T = (V_hi + V_lo)^T P^T with P = P_hi + P_lo; values of slots
