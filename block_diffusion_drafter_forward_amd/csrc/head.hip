@@ -356,17 +356,6 @@ hipError_t launch_lm_head(int bf16, const void* z, int M, const void* wlm, int V
 // over all records takes over.  The result does not depend on the gathering order: deterministic.
 #define MERGE_THREADS 1024
 #define MERGE_CAP 1024
-__device__ __forceinline__ float block_max(float v, float* red) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    v = wave_max(v);
-    __syncthreads();
-    if (lane == 0) red[w] = v;
-    __syncthreads();
-    float t = -INFINITY;
-    for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
-    return t;
-}
-
 __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_groups, int top_k, int sample,
                                                             const float* __restrict__ hpart,
                                                             const int32_t* __restrict__ btok,
@@ -375,16 +364,15 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
     __shared__ float cv[MERGE_CAP];
     __shared__ int cid[MERGE_CAP];
     __shared__ float red[MERGE_THREADS / 64];
+    __shared__ float rmx[MERGE_THREADS / 64], rth[MERGE_THREADS / 64];
     __shared__ float outv[DF_TOPK];
     __shared__ int outi[DF_TOPK];
     __shared__ float sbest[MERGE_THREADS / 64];
     __shared__ int sbid[MERGE_THREADS / 64];
     __shared__ int cnt;
-    __shared__ float t8;
-    const int m = blockIdx.x, t = threadIdx.x;
+    const int m = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
     if (t == 0) {
         cnt = 0;
-        t8 = -INFINITY;
         if (btok[m] < 0 || btok[m] >= V) set_err(err, DFLASH_DEVERR_TOKEN);
     }
     const size_t RS = (size_t)M * HEAD_REC;               // record stride between groups
@@ -450,15 +438,36 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
             sbid[t >> 6] = sbi;
         }
     }
-    mx = block_max(mx, red);  // leaves the wave maxima in red until the next block reduction
-    if (t < MERGE_THREADS / 64) {
-        const float x = red[t];
+    // One block reduction (one barrier) for the maximum and bound (a); every wave then finds bound (b), the
+    // 8th largest wave maximum (ties by wave index), on its first sixteen lanes.
+    constexpr int NW = MERGE_THREADS / 64;
+    float wm = mx, wt = th;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        wm = fmaxf(wm, __shfl_xor(wm, o, DF_WAVE));
+        wt = fmaxf(wt, __shfl_xor(wt, o, DF_WAVE));
+    }
+    if (lane == 0) {
+        rmx[wv] = wm;
+        rth[wv] = wt;
+    }
+    __syncthreads();
+    mx = rmx[0];
+    float ta = rth[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+        mx = fmaxf(mx, rmx[i]);
+        ta = fmaxf(ta, rth[i]);
+    }
+    float t8 = -INFINITY;
+    if (lane < NW) {
+        const float x = rmx[lane];
         int rank = 0;
-        for (int j = 0; j < MERGE_THREADS / 64; ++j) rank += (red[j] > x || (red[j] == x && j < t)) ? 1 : 0;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) rank += (rmx[j] > x || (rmx[j] == x && j < lane)) ? 1 : 0;
         if (rank == DF_TOPK - 1) t8 = x;
     }
-    const float th1 = block_max(th, red);
-    th = fmaxf(th1, t8);  // t8 was written before block_max's barriers
+    th = fmaxf(ta, wave_max(t8));
     float se = 0.f;
     for (int gi = t; gi < n_groups; gi += MERGE_THREADS) {
         const int u = (gi - t) / MERGE_THREADS;
@@ -519,13 +528,12 @@ __global__ __launch_bounds__(MERGE_THREADS) void head_merge(int M, int V, int n_
         }
 #pragma unroll 1
         for (int o = 1; o < DF_WAVE; o <<= 1) s.merge_lane_xor(o);
-        const int lane = t & 63, w = t >> 6;
         __syncthreads();
         if (lane == 0) {
 #pragma unroll
             for (int j = 0; j < DF_TOPK; ++j) {
-                cv[w * DF_TOPK + j] = s.v[j];
-                cid[w * DF_TOPK + j] = s.id[j];
+                cv[wv * DF_TOPK + j] = s.v[j];
+                cid[wv * DF_TOPK + j] = s.id[j];
             }
         }
         __syncthreads();
