@@ -244,7 +244,9 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
         if ((t0 >> 4) + j >= max_pages) set_err(err, DFLASH_DEVERR_POS);
         else if (spg[j] < 0 || spg[j] >= n_pages) set_err(err, DFLASH_DEVERR_PAGE);
     }
-    prefetch(0);  // always issued (a chunk without keys reads the block page, never stashed): the block step below waits only for its own loads
+    // always issued (a chunk without keys reads the block page and never stashes it), so that the block step
+    // below waits only for its own loads
+    prefetch(0);
     if (c == 0) {
         // the block's keys (L of the 16 slots): S = (K_hi + K_lo)(Q_hi + Q_lo)^T in one accumulator chain, then
         // the first online-softmax step, then O^T = (V_hi + V_lo)^T P^T with P = P_hi + P_lo; values of slots

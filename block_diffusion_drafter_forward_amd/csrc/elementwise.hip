@@ -34,7 +34,8 @@ __device__ __forceinline__ float split_sum(const float* p, size_t stride, int S)
 // The same sums for NP columns (offsets col[c] from p) at once: every column's loads of a batch are issued
 // before the first add.
 template <int NP>
-__device__ __forceinline__ void split_sums(const float* p, const int (&col)[NP], size_t stride, int S, float (&acc)[NP]) {
+__device__ __forceinline__ void split_sums(const float* p, const int (&col)[NP], size_t stride, int S,
+                                           float (&acc)[NP]) {
 #pragma unroll
     for (int c = 0; c < NP; ++c) acc[c] = 0.f;
     for (int s0 = 0; s0 < S; s0 += SPLIT_BATCH) {
@@ -186,9 +187,9 @@ hipError_t launch_resid_norm(int bf16, const float* part, int S, int M, int H, f
 // ------------------------------------------------------------------------------------------------------
 // QKV epilogue
 // ------------------------------------------------------------------------------------------------------
-// One thread per (block row m = grid y, head, rotary pair i): sums the splits of columns i and i + d/2, applies the
-// rotation at position ctx_len[b] + row to q and k heads, rounds, and stores q row-major, the block's keys as
-// a 16-slot page [b][kv head][slot][d] and its values transposed [b][kv head][d][slot].
+// One thread per (block row m = grid y, head, rotary pair i): sums the splits of columns i and i + d/2,
+// applies the rotation at position ctx_len[b] + row to q and k heads, rounds, and stores q row-major, the
+// block's keys as a 16-slot page [b][kv head][slot][d] and its values transposed [b][kv head][d][slot].
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_epilogue(const float* __restrict__ part, int S, int B, int L, int nq,
                                                     int nkv, int d, const int32_t* __restrict__ ctx_len, RopeFreq rf,
