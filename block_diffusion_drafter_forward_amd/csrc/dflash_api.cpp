@@ -381,16 +381,37 @@ struct InjectPlan {
     size_t err, f, part, total;
 };
 
-static InjectPlan plan_inject(const dflash_config& c, int n_rows) {
-    InjectPlan p{};
+// Float32 split partials one chunk of R rows writes: the fusion GEMM's and the widest KV GEMM's.  plan_gemm
+// may give a short chunk more splits than a long one (fewer tiles, so K is split further), so the product is
+// not monotonic in R.
+static size_t inject_part_floats(const dflash_config& c, int R) {
     const int bf = is_bf16(c);
+    const int kvd = c.n_kv_heads * c.head_dim;
+    const GemmPlan fc = plan_gemm(bf, R, c.hidden, c.feat_dim);
+    size_t need = (size_t)fc.splits * R * c.hidden;
+    // every layer group's KV GEMM (the last group may be narrower, hence split further)
+    for (int l0 = 0; l0 < c.n_layers; l0 += MAX_LAYERS_PER_KV_GEMM) {
+        const int nl = std::min(MAX_LAYERS_PER_KV_GEMM, c.n_layers - l0);
+        const GemmPlan kv = plan_gemm(bf, R, nl * 2 * kvd, c.hidden);
+        need = std::max(need, (size_t)kv.splits * R * nl * 2 * kvd);
+    }
+    return need;
+}
+
+// Workspace of a dflash_inject_ctx call of n_rows rows: chunks of INJECT_ROWS rows and a shorter last chunk
+// (exact = 1), or of any call of at most n_rows rows, i.e. any chunk length up to min(n_rows, INJECT_ROWS)
+// (exact = 0, what dflash_inject_workspace_bytes reports).
+static InjectPlan plan_inject(const dflash_config& c, int n_rows, bool exact) {
+    InjectPlan p{};
     const int R = n_rows < INJECT_ROWS ? n_rows : INJECT_ROWS;
     p.rows = R;
-    const int kvd = c.n_kv_heads * c.head_dim;
-    const int nl = c.n_layers < MAX_LAYERS_PER_KV_GEMM ? c.n_layers : MAX_LAYERS_PER_KV_GEMM;
-    GemmPlan fc = plan_gemm(bf, R, c.hidden, c.feat_dim);
-    GemmPlan kv = plan_gemm(bf, R, nl * 2 * kvd, c.hidden);
-    size_t part = std::max((size_t)fc.splits * R * c.hidden, (size_t)kv.splits * R * nl * 2 * kvd);
+    size_t part = 0;
+    if (exact) {
+        part = inject_part_floats(c, R);
+        if (n_rows % R) part = std::max(part, inject_part_floats(c, n_rows % R));
+    } else {
+        for (int r = 1; r <= R; ++r) part = std::max(part, inject_part_floats(c, r));
+    }
     Carve cv;
     p.err = cv.take(256);
     p.f = cv.take((size_t)R * c.hidden * ACT);
@@ -401,8 +422,7 @@ static InjectPlan plan_inject(const dflash_config& c, int n_rows) {
 
 extern "C" size_t dflash_inject_workspace_bytes(const dflash_handle* h, int max_rows) {
     if (!h || max_rows < 1) return 0;
-    // the plan of the largest chunk bounds every chunk (smaller chunks need no more)
-    return plan_inject(h->cfg, max_rows).total;
+    return plan_inject(h->cfg, max_rows, false).total;
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -473,9 +493,14 @@ static int draft_impl(dflash_handle* h, int batch, const int32_t* block_tokens, 
     const int qd = nq * d, kvd = nkv * d;
     const size_t tap_stride = (size_t)M * H;
     float* tap = dbg ? dbg->hidden : nullptr;
-    const void* kpool = kv ? kv->k : nullptr;
-    const void* vpool = kv ? kv->v : nullptr;
-    const int n_pages = kv ? kv->n_pages : 0;
+    const void* kpool = max_ctx > 0 && kv ? kv->k : nullptr;
+    const void* vpool = max_ctx > 0 && kv ? kv->v : nullptr;
+    // Without context the attention kernels read no page table and no pool, whatever the caller passed.
+    const int n_pages = max_ctx > 0 && kv ? kv->n_pages : 0;
+    if (max_ctx == 0) {
+        page_table = nullptr;
+        max_pages = 0;
+    }
 
     {
         Timed t(h, "embed_norm", st);
@@ -587,7 +612,7 @@ extern "C" int dflash_inject_ctx(dflash_handle* h, int batch, int n_rows, const 
     if (is_bf16(c) ? (feat_row_stride % 8) : (feat_row_stride % 4))
         return fail(DFLASH_E_ARG, "feat_row_stride must keep rows 16-byte aligned");
     if (max_pages < 1 || kv->n_pages < 1) return fail(DFLASH_E_ARG, "max_pages and n_pages must be >= 1");
-    const InjectPlan p = plan_inject(c, n_rows);
+    const InjectPlan p = plan_inject(c, n_rows, true);
     if (ws_bytes < p.total) return fail(DFLASH_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, p.total);
     if (((uintptr_t)ws) & 255) return fail(DFLASH_E_ARG, "workspace must be 256-byte aligned");
     if (is_bf16(c) && !h->packed) return fail(DFLASH_E_ARG, "bfloat16 weights are not packed (dflash_pack_weights)");

@@ -337,3 +337,75 @@ def test_tree_attention_validation(D, over, code):
                                    a["k"], a["v"], a["kp"], a["vp"], a["n_pages"], a["pt"], a["max_pages"], a["ctx"],
                                    a["max_ctx"], a["theta"], a["out"], a["ws"], a["ws_bytes"], None) == code
     assert D.dflash_last_error()
+
+
+def test_inject_workspace_covers_every_chunk(D):
+    """A call of n rows runs chunks of 4096 rows and a shorter last chunk, and a short chunk may be split
+    further along K than a long one.  The size dflash_inject_workspace_bytes(h, n) reports must pass the call's
+    own capacity check for every row count up to n (here up to two whole chunks).  The call then stops at the
+    missing weight store (-1, "packed"), which proves the capacity check passed."""
+    import workloads as W
+    kv = D.dflash_kv(0x40, 0x50, 8)
+    for s in (W.QWEN3_8B, W.QWEN3_4B, W.SMALL_BF16):
+        m = _create(D, s)
+        try:
+            prev = 0
+            sizes = {}
+            for n in list(range(1, 65)) + list(range(100, 2 * 4096 + 1, 37)) + [4095, 4096, 4097, 5096, 8192]:
+                ws = D.dflash_inject_workspace_bytes(m.handle, n)
+                sizes[n] = ws
+                rc = D.dflash_inject_ctx(m.handle, 1, n, 0x10, s.feat_dim, 0x20, 0x30, 0x40, 8, kv, 0x100000, ws,
+                                         None)
+                assert rc == D.DFLASH_E_ARG and "packed" in D.dflash_last_error(), (s, n, rc)
+            for n in sorted(sizes):
+                assert sizes[n] >= prev, (s, n)   # a bound for every call of at most n rows
+                prev = sizes[n]
+            assert sizes[8192] == sizes[4096]         # chunks never exceed 4096 rows
+        finally:
+            m.close()
+
+
+def test_no_context_ignores_page_table(D):
+    """max_ctx = 0: no page table or pool is read, so NULL is accepted whatever max_pages says (the call then
+    stops at the missing weight store, after every shape check)."""
+    m = _create(D, _shape())
+    try:
+        rc = _draft(D, m.handle, max_ctx=0, page_table=None, max_pages=8, kv=None)
+        assert rc == D.DFLASH_E_ARG and "packed" in D.dflash_last_error()
+        rc = _draft(D, m.handle, max_ctx=0, page_table=None, max_pages=0, kv=None)
+        assert rc == D.DFLASH_E_ARG and "packed" in D.dflash_last_error()
+    finally:
+        m.close()
+
+
+def _min_inject_ws(D, m, n, kv):
+    """Smallest workspace (multiple of 256) that passes the capacity check of an n-row call."""
+    lo, hi = 0, D.dflash_inject_workspace_bytes(m.handle, n) // 256
+    while lo < hi:
+        mid = (lo + hi) // 2
+        rc = D.dflash_inject_ctx(m.handle, 1, n, 0x10, m.shape.feat_dim, 0x20, 0x30, 0x40, 8, kv, 0x100000, mid * 256,
+                                 None)
+        if rc == D.DFLASH_E_CAPACITY:
+            lo = mid + 1
+        else:
+            hi = mid
+    return lo * 256
+
+
+def test_inject_short_last_chunk_needs_its_own_split_partials(D):
+    """4096 + 1000 rows: the 1000-row chunk has fewer output tiles, so its fusion GEMM splits K further and
+    writes more float32 partials than a whole 4096-row chunk.  A workspace sized for one whole chunk must be
+    refused for that call instead of being overrun."""
+    import workloads as W
+    kv = D.dflash_kv(0x40, 0x50, 8)
+    m = _create(D, W.QWEN3_8B)
+    try:
+        one_chunk = _min_inject_ws(D, m, 4096, kv)
+        with_tail = _min_inject_ws(D, m, 4096 + 1000, kv)
+        assert with_tail > one_chunk
+        rc = D.dflash_inject_ctx(m.handle, 1, 4096 + 1000, 0x10, m.shape.feat_dim, 0x20, 0x30, 0x40, 8, kv, 0x100000,
+                                 one_chunk, None)
+        assert rc == D.DFLASH_E_CAPACITY
+        assert D.dflash_inject_workspace_bytes(m.handle, 4096 + 1000) >= with_tail
+    finally:
+        m.close()
