@@ -23,14 +23,18 @@ Readings (where the page leaves a step open):
   * the depth-d distribution is the drafter's block row d (rows 1 .. block_len-1; row 0 holds the anchor),
     so a block of length L gives trees of depth at most L - 1;
   * ties in sigma pop in creation order (the sibling of a popped tuple is created before its child);
-  * a node's score is computed as the parent's score plus the node's own log-probability (the page's
-    sibling update, sigma - log q(rank) + log q(rank + 1), is the same quantity);
+  * scores follow the page's update rules: the next sibling of a popped tuple scores sigma - log q_d(rank) +
+    log q_d(rank + 1), the first child sigma + log q_{d+1}(rank 1).  A parity run against a float32 kernel
+    that scores a node as its parent's score plus its own log-probability (the same quantity in exact
+    arithmetic) can ask for that summation order (score="path_sum") together with dtype=np.float32, to take
+    the kernel's float32 decisions; the fp64 default is the page's order;
   * the tree's node i is the i-th pop; its parent is the node index of its prefix without the last token
     (-1 for a depth-1 node, whose parent is the root = the bonus token).
 
-Arithmetic is float64 unless a caller asks otherwise: which prefixes enter the tree is decided by
-comparisons of float sums, so a parity test against a float32 kernel passes dtype=np.float32 to take those
-decisions in the kernel's precision.
+Arithmetic is float64 in the page's order unless a caller asks otherwise.  Which prefixes enter the tree is
+decided by comparisons of float sums: a parity test compares a float32 kernel with this fp64 pop order on
+every pop whose fp64 margin exceeds float32 error (build_tree(..., with_gaps=True) reports the margins), and
+may also replay the kernel's own float32 decisions (dtype=np.float32, score="path_sum").
 """
 from __future__ import annotations
 
@@ -51,18 +55,25 @@ def topk_logprobs(logits: np.ndarray, k: int):
     return ids, np.take_along_axis(lg, ids, axis=-1) - lse[..., None]
 
 
-def build_tree(logp: np.ndarray, budget: int, dtype=np.float64):
+def build_tree(logp: np.ndarray, budget: int, dtype=np.float64, score: str = "incremental",
+               with_gaps: bool = False):
     """Algorithm 1 of [DDT] §3.4.4 on sorted per-depth log-probabilities.
 
     logp: [D, K], row d-1 = log q_d of the depth-d ranks 1..K, each row non-increasing.
     Returns the pops in order as a list of (ranks, sigma, parent): ranks is a 0-based rank tuple (rank 0 is
     the page's rank 1), sigma its log-probability score, parent the node index of ranks[:-1] (-1: root).
+    score="incremental" (default) scores a sibling by the page's update sigma - log q_d(rank) + log q_d(rank+1);
+    score="path_sum" scores it as the parent's score + log q_d(rank+1) (see the module docstring).
+    with_gaps=True also returns, per pop, the popped score minus the best score left in the heap (inf if
+    none): how far that pop was from a different decision.
     """
+    if score not in ("incremental", "path_sum"):
+        raise ValueError(score)
     lq = np.asarray(logp, dtype=dtype)
     D, K = lq.shape
-    nodes = []
+    nodes, gaps = [], []
     if budget < 1 or D < 1 or K < 1:
-        return nodes
+        return (nodes, gaps) if with_gaps else nodes
     seq = itertools.count()
     # heap entries: (-sigma, creation order, ranks, parent node index, parent sigma)
     zero = dtype(0)
@@ -70,16 +81,20 @@ def build_tree(logp: np.ndarray, budget: int, dtype=np.float64):
     while heap and len(nodes) < budget:
         neg, _, ranks, parent, psig = heapq.heappop(heap)
         sigma = -neg
+        gaps.append(float(sigma) - float(-heap[0][0]) if heap else np.inf)
         me = len(nodes)
         nodes.append((ranks, sigma, parent))
-        d = len(ranks)
-        if ranks[-1] + 1 < K:       # next sibling: same prefix, next rank at this depth
-            s = dtype(psig + lq[d - 1, ranks[-1] + 1])
-            heapq.heappush(heap, (-s, next(seq), ranks[:-1] + (ranks[-1] + 1,), parent, psig))
-        if d < D:                    # first child: best token at the next depth
+        d, r = len(ranks), ranks[-1]
+        if r + 1 < K:       # next sibling: same prefix, next rank at this depth
+            if score == "incremental":
+                s = dtype(dtype(sigma - lq[d - 1, r]) + lq[d - 1, r + 1])
+            else:
+                s = dtype(psig + lq[d - 1, r + 1])
+            heapq.heappush(heap, (-s, next(seq), ranks[:-1] + (r + 1,), parent, psig))
+        if d < D:           # first child: best token at the next depth
             s = dtype(sigma + lq[d, 0])
             heapq.heappush(heap, (-s, next(seq), ranks + (0,), me, sigma))
-    return nodes
+    return (nodes, gaps) if with_gaps else nodes
 
 
 def tree_tokens(nodes, ids: np.ndarray):

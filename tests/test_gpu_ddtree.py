@@ -1,7 +1,13 @@
 """DDTree kernels against the oracle ([DDT] = "Accelerating Speculative Decoding with Block Diffusion Draft
-Trees"): the wide top-K (ids exact, log-probs to float32 rounding, ties by id), the best-first tree (node for
-node, with the oracle's tree decisions taken in float32 like the kernel's), the verifier walk (exact), and the
-whole chain on a drafter pass."""
+Trees"): the wide top-K (ids exact, log-probs to float32 rounding, ties by id), the best-first tree, the
+verifier walk (exact), and the whole chain on a drafter pass.
+
+The tree is checked against the fp64 oracle, which follows Algorithm 1's update rules ([DDT] §3.4.4):
+node for node up to the first pop whose fp64 margin (popped score minus the best score left in the heap) is
+within float32 error, and beyond it by what Proposition 2 fixes -- the same number of nodes, every node of
+the fp64 top-B above the guard band present, no node below it, prefix-closed, distinct and popped in
+non-increasing order.  As a secondary check the kernel's float32 decisions are replayed (float32 path sums)
+and compared score bit for score bit."""
 import numpy as np
 import pytest
 
@@ -66,6 +72,46 @@ def _build_gpu(torch, D, ids, lp, budget):
     return tok.cpu().numpy(), par.cpu().numpy(), dep.cpu().numpy(), lq.cpu().numpy(), n.cpu().numpy()
 
 
+def check_tree_fp64(tok, par, dep, n, ids, lp, budget):
+    """The GPU tree of one request against the fp64 oracle on the same float32 log-probabilities.  Returns
+    the number of leading pops compared node for node."""
+    lp64 = lp.astype(np.float64)
+    Dd, K = lp64.shape
+    nodes, gaps = T.build_tree(lp64, budget, with_gaps=True)
+    assert n == len(nodes)
+    # rank tuples and exact scores of the GPU's nodes
+    rank_of = [{int(t): r for r, t in enumerate(ids[d])} for d in range(Dd)]
+    ranks, sig = [], np.empty(n)
+    for i in range(n):
+        p, d = int(par[i]), int(dep[i])
+        assert -1 <= p < i and 1 <= d <= Dd and d == (1 if p < 0 else int(dep[p]) + 1)
+        tup = (() if p < 0 else ranks[p]) + (rank_of[d - 1][int(tok[i])],)
+        ranks.append(tup)
+        sig[i] = sum(lp64[j, r] for j, r in enumerate(tup))
+    # A float32 path sum of d <= Dd non-positive terms errs by at most d * 2^-24 |sigma| (every partial sum is
+    # smaller in magnitude than the node's score); two compared scores together by twice that.  Scores of
+    # the popped nodes and of the candidates they were compared with lie above the lowest one seen here
+    # minus the largest single drop.
+    low = min(sig.min(), min(s for _, s, _ in nodes)) - np.abs(lp64).max()
+    eps = Dd * 2.0 ** -23 * (abs(low) + 1.0)
+    want_tok = T.tree_tokens(nodes, ids)
+    amb = [i for i, g in enumerate(gaps) if g <= eps]
+    head = amb[0] + 1 if amb else n          # pops 0..amb[0] are decided before any ambiguous choice
+    np.testing.assert_array_equal(tok[:head], want_tok[:head])
+    np.testing.assert_array_equal(par[:head], [p for _, _, p in nodes[:head]])
+    np.testing.assert_array_equal(dep[:head], [len(r) for r, _, _ in nodes[:head]])
+    # Proposition 2: the B best prefixes, up to the guard band around the B-th score
+    assert len(set(ranks)) == n
+    assert np.all(np.diff(sig) <= eps)
+    sig_b = float(nodes[-1][1])
+    have = set(ranks)
+    for r, s, _ in nodes:
+        if s > sig_b + eps:
+            assert r in have, (r, s, sig_b)
+    assert sig.min() >= sig_b - eps
+    return head
+
+
 @pytest.mark.parametrize("depth,K,budget", [(15, 64, 1), (15, 64, 16), (15, 256, 256), (15, 1024, 1000),
                                             (6, 512, 2047), (3, 3, 100), (1, 50, 64), (16, 8, 512)])
 def test_ddtree_build_matches_oracle(depth, K, budget):
@@ -75,7 +121,10 @@ def test_ddtree_build_matches_oracle(depth, K, budget):
     ids, lp = _sorted_logprobs(rng, batch, depth, K)
     tok, par, dep, lq, n = _build_gpu(torch, D, ids, lp, budget)
     for b in range(batch):
-        nodes = T.build_tree(lp[b], budget, dtype=np.float32)
+        head = check_tree_fp64(tok[b], par[b], dep[b], int(n[b]), ids[b], lp[b], budget)
+        assert head >= min(int(n[b]), 8)
+        # secondary: the kernel's own float32 decisions, replayed, score bit for score bit
+        nodes = T.build_tree(lp[b], budget, dtype=np.float32, score="path_sum")
         assert n[b] == len(nodes) == min(budget, sum(K ** d for d in range(1, depth + 1)))
         np.testing.assert_array_equal(tok[b, :n[b]], T.tree_tokens(nodes, ids[b]))
         np.testing.assert_array_equal(par[b, :n[b]], [p for _, _, p in nodes])
@@ -147,7 +196,10 @@ def test_ddtree_chain_on_a_drafter_pass():
     for b in range(B):
         want_ids, want_lp = T.topk_logprobs(lg[b], K)
         np.testing.assert_array_equal(ids[b].cpu().numpy(), want_ids)
-        nodes = T.build_tree(lp[b, 1:].cpu().numpy(), budget, dtype=np.float32)
+        lpb = lp[b, 1:].cpu().numpy()
+        check_tree_fp64(tok[b].cpu().numpy(), par[b].cpu().numpy(), dep[b].cpu().numpy(), int(n[b].item()),
+                        want_ids[1:], lpb, budget)
+        nodes = T.build_tree(lpb, budget, dtype=np.float32, score="path_sum")
         assert n[b].item() == len(nodes)
         np.testing.assert_array_equal(tok[b, :len(nodes)].cpu().numpy(), T.tree_tokens(nodes, want_ids[1:]))
         np.testing.assert_array_equal(par[b, :len(nodes)].cpu().numpy(), [p for _, _, p in nodes])
