@@ -36,10 +36,14 @@
  *     (DFLASH_DEVERR_*).  Each call clears that word first.  Read it after synchronising.
  *   - One handle per stream: calls on one handle must not overlap.
  *
- * Numerics (bfloat16 drafters): GEMMs accumulate in float32; the residual stream is float32; tensors that
- * are stored between kernels (fused feature, cached K/V, normalised activations, q/k/v after RoPE,
- * attention output, SwiGLU output, final normalised state) are rounded to bfloat16 (nearest, ties to
- * even).  Logits are float32 and never written to memory except through the optional debug tap.
+ * Numerics (bfloat16 drafters): weights, input features and the cached K/V are bfloat16; the cached K/V
+ * are rounded to bfloat16 (nearest, ties to even) once, when injected.  GEMMs accumulate in float32 and
+ * the residual stream is float32.  Every other tensor the pass keeps between kernels (fused feature f,
+ * normalised activations, q/k/v after RoPE, attention output, SwiGLU output, final normalised state) is
+ * transient and keeps about float32 precision: it is stored as two bfloat16 planes, hi = bf16(v) and
+ * lo = bf16(v - hi) (relative error <= 2^-17), and each plane meets the bfloat16 weights in its own MFMA.
+ * Attention probabilities enter the PV product as such a pair too.  Logits are float32 and never written
+ * to memory except through the optional debug tap.  Float32 drafters compute and store float32 throughout.
  */
 #ifndef DFLASH_H
 #define DFLASH_H

@@ -44,7 +44,7 @@ def make(wl):
     ctx = wl.ctx_lens()
     kv = []
     for r in range(wl.batch):
-        kv.append(O.inject(weights, s, wl.features(r, int(ctx[r])), 0))
+        kv.append(O.inject(weights, s, wl.features(r, int(ctx[r])), 0, fc_b=weights.get("fc_b")))
         print(f"  {wl.name}: inject request {r} ({ctx[r]} tokens) done at {time.time() - t0:.0f} s", flush=True)
     out = O.draft_block(weights, s, kv, wl.block_tokens(), 8)
     logits = out["logits"]
@@ -79,7 +79,7 @@ def make(wl):
 
 
 def main():
-    names = sys.argv[1:] or [w.name for w in W.CONFIGS]
+    names = sys.argv[1:] or [w.name for w in W.CONFIGS + W.FULL_EXTRA]
     for n in names:
         make(W.by_name(n))
 

@@ -4,7 +4,9 @@ one drafter pass with top-8, then acceptance.
 
 Checked: greedy tokens (top-2 gap > 1e-2) and top-8 ids (top-9 gaps > 1e-2) bit-exact; top-8 log-probs and
 48 sampled logits per row within 3e-2 + 2e-2 |ref| (float32 drafter: 1e-4 relative); acceptance lengths
-exact; sampled cached K/V rows within the bound of the reduced-shape test; a clean device error word.  The
+exact; sampled cached K/V rows within one bfloat16 step (the bound of the reduced-shape test); a clean
+device error word.  Besides the five benchmark workloads, a Qwen3-8B-shaped case with a fusion bias and
+4096 + 1000 context rows (one inject call, a whole chunk and a short last chunk).  The
 temperature-1 pass is checked on the same inputs: identical logits and top-k, and each sampled token equal to
 the oracle's Gumbel-max sample on the kernel's logits.
 """
@@ -30,7 +32,7 @@ def _expected(name):
         return {k: z[k] for k in z.files}
 
 
-@pytest.mark.parametrize("name", [w.name for w in W.CONFIGS])
+@pytest.mark.parametrize("name", [w.name for w in W.CONFIGS + W.FULL_EXTRA])
 def test_full_size_parity(name):
     import torch
     from block_diffusion_drafter_forward_amd import session as S
@@ -85,7 +87,7 @@ def test_full_size_parity(name):
             for got, want in ((O.to_f64(k), exp["kv_k"][l, r].astype(np.float64)),
                               (O.to_f64(v), exp["kv_v"][l, r].astype(np.float64))):
                 rms = np.sqrt(np.mean(want ** 2, axis=-1, keepdims=True))
-                bound = (2.0 ** -5 * np.abs(want) + 2.0 ** -8 * rms) if s.bf16 else 1e-5 * (np.abs(want) + rms)
+                bound = (2.0 ** -7 * np.abs(want) + 2.0 ** -10 * rms) if s.bf16 else 1e-5 * (np.abs(want) + rms)
                 assert np.all(np.abs(got - want) <= bound)
 
     # temperature 1 at the same size: the sampled pass computes the same logits and top-k, and each row's token

@@ -6,12 +6,13 @@ Criteria:
 * logits and log-probs within |err| <= 3e-2 + 2e-2 |ref| (float32 drafters: 1e-4 relative);
 * acceptance lengths exact: the GPU kernel on the GPU drafts equals the oracle's rule on the same drafts,
   and end-to-end tau equals the oracle tau when no guarded row precedes the first mismatch;
-* cached K/V: at least 99% of entries bit-identical to the oracle's bfloat16 value.  The rest differ
-  where the float32 (GPU) and fp64 (oracle) sums land on different sides of a rounding boundary: one
-  bfloat16 step of the value, a small absolute error where the value is a cancelled sum, or a few steps
-  where an element of the fused feature f (|f| up to ~11, one step up to 2^-4) rounded the other way and
-  U_K / U_V carry that step into the row.  Every entry stays within 2^-5 |ref| + 2^-8 rms(row); a wrong
-  position, head, layer or page breaks that by orders of magnitude.
+* cached K/V: at least 99% of entries bit-identical to the oracle's bfloat16 value, and every entry within
+  one bfloat16 step, 2^-7 |ref| + 2^-10 rms(row).  The fused feature f is not rounded on either side (the
+  GPU keeps it as a pair of bfloat16 planes, about float32 precision), so the only rounding is the cache's
+  own: where the float32 (GPU) and fp64 (oracle) values of U_K f or U_V f fall on different sides of a
+  bfloat16 rounding boundary the two differ by one step, and the rms term covers cancelled sums whose
+  value is far below the row's scale.  A wrong position, head, layer, page or bias breaks the bound by
+  orders of magnitude.
 """
 import numpy as np
 import pytest
@@ -54,7 +55,7 @@ def run_case(wl):
     kv = []
     for r in range(B):
         feats = wl.features(r, int(g.ctx[r]))
-        kv.append(O.inject(weights, s, feats, 0))
+        kv.append(O.inject(weights, s, feats, 0, fc_b=weights.get("fc_b")))
     ref = O.draft_block(weights, s, kv, wl.block_tokens(), wl.top_k, return_taps=True)
     return wl, s, g, gpu, ref, kv, weights
 
@@ -90,7 +91,7 @@ def test_injected_cache_matches_oracle(case):
                 if s.bf16:
                     total += got.size
                     mismatched += int((got != want).sum())
-                    bound = 2.0 ** -5 * np.abs(want) + 2.0 ** -8 * rms
+                    bound = 2.0 ** -7 * np.abs(want) + 2.0 ** -10 * rms
                     assert np.all(np.abs(got - want) <= bound), np.abs(got - want).max()
                 else:
                     assert np.all(np.abs(got - want) <= 1e-5 * (np.abs(want) + rms))

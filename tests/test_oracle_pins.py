@@ -92,6 +92,21 @@ def test_bf16_round_matches_torch_on_float32_values():
     assert np.array_equal(O.bf16_round(x32.astype(np.float64)), ref)
 
 
+def test_to_f64_decodes_every_bfloat16_pattern_like_torch():
+    """to_f64 reads every bfloat16 value the parity tests compare: all 65536 bit patterns against torch's own
+    bfloat16 decoding (NaN patterns as NaN, both zeros with their signs, subnormals, infinities)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = O.to_f64(bits)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert got.dtype == np.float64
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2 * 127
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+    assert got[0x3F80] == 1.0 and got[0xC000] == -2.0 and got[0x0001] == 2.0 ** -133
+    assert got[0x7F80] == np.inf and got[0xFF80] == -np.inf
+
+
 def test_bf16_round_ties_and_direct_rounding():
     one = 1.0
     assert O.bf16_round(np.array([one + 2.0 ** -8]))[0] == 1.0                     # tie -> even
@@ -257,6 +272,17 @@ def test_fuse_and_inject_are_linear_maps_of_the_features():
         assert np.allclose(kv[0][1][0].reshape(-1), w["l0.uv"] @ w["fc_w"][:, j], atol=1e-14)
     b = rng.normal(size=cfg.hidden)
     assert np.allclose(O.fuse(np.zeros((2, cfg.feat_dim)), w["fc_w"], b, False), b)
+    # the bias enters f, before U_K / U_V: zero features give every context token K = U_K b, V = U_V b
+    # (RoPE off), and features and bias add
+    kv0 = O.inject(w, cfg, np.zeros((3, cfg.feat_dim)), 0, fc_b=b)
+    for l in range(cfg.n_layers):
+        for j in range(3):
+            assert np.allclose(kv0[l][0][j].reshape(-1), w[f"l{l}.uk"] @ b, atol=1e-14)
+            assert np.allclose(kv0[l][1][j].reshape(-1), w[f"l{l}.uv"] @ b, atol=1e-14)
+    e = np.zeros((1, cfg.feat_dim))
+    e[0, 7] = 1.0
+    kvb = O.inject(w, cfg, e, 0, fc_b=b)
+    assert np.allclose(kvb[1][1][0].reshape(-1), w["l1.uv"] @ (w["fc_w"][:, 7] + b), atol=1e-14)
     # the fused feature is transient: not rounded even on the bfloat16 path; the cached K/V are
     x = rng.normal(size=(3, cfg.feat_dim))
     assert np.allclose(O.fuse(x, w["fc_w"], None, True), x @ w["fc_w"].T, atol=1e-14)

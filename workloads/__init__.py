@@ -171,6 +171,7 @@ class Workload:
     accept_p_range: Optional[tuple]
     top_k: int = 8
     ctx_fixed: Optional[tuple] = None   # explicit per-request context lengths (edge cases)
+    fc_bias: bool = False               # give the fusion projection a bias fc_b [hidden], N(0, 1)
 
     # ---------------- seeds ----------------
     @property
@@ -197,6 +198,8 @@ class Workload:
                 (f"l{l}.w_down", (s.hidden, s.ffn), "mat"),
             ]
         specs += [("final_norm", (s.hidden,), "gain"), ("lm_head", (s.vocab, s.hidden), "mat")]
+        if self.fc_bias:  # last, so that every other tensor keeps its stream
+            specs.append(("fc_b", (s.hidden,), "bias"))
         return specs
 
     def weight(self, idx: int) -> np.ndarray:
@@ -205,7 +208,9 @@ class Workload:
             if self.shape.bf16:
                 return np.full(shp, 0x3F80, dtype=np.uint16)   # 1.0 in bfloat16
             return np.ones(shp, dtype=np.float32)
-        return normal(self.key, S_WEIGHTS + idx, shp, 0.02, self.shape.bf16)
+        # a bias of unit scale moves f by about a third of its own spread (|W_fc x| ~ 0.02 sqrt(feat_dim))
+        scale = 1.0 if kind == "bias" else 0.02
+        return normal(self.key, S_WEIGHTS + idx, shp, scale, self.shape.bf16)
 
     def weights(self) -> Dict[str, np.ndarray]:
         """All weights (bfloat16 as uint16 bit patterns, or float32)."""
@@ -324,11 +329,21 @@ SMALL = [
              None),
     Workload(110, "small-bf16-l10-b3", dataclasses.replace(SMALL_BF16, block_len=10), 3, None, (1, 200), True,
              None, (0.6, 0.95)),
+    # the optional fusion bias ([DF] §3.4.3 "Feature fusion": the projection may carry one)
+    Workload(111, "small-bf16-bias-b2", SMALL_BF16, 2, None, (1, 300), True, None, (0.6, 0.95), fc_bias=True),
+    Workload(112, "small-fp32-bias-b1", SMALL_FP32, 1, 37, None, True, 0.9, None, top_k=3, fc_bias=True),
+]
+
+# Full-size parity cases beyond the five benchmark configurations (expected values in tests/golden/): the
+# Qwen3-8B shape with a fusion bias, and 4096 + 1000 context rows, which one inject call runs as a whole
+# chunk and a short last chunk.
+FULL_EXTRA = [
+    Workload(20, "qwen3-8b-shape-bias-5096", QWEN3_8B, 1, 5096, None, True, 0.85, None, fc_bias=True),
 ]
 
 
 def by_name(name: str) -> Workload:
-    for w in CONFIGS + SMALL:
+    for w in CONFIGS + SMALL + FULL_EXTRA:
         if w.name == name:
             return w
     raise KeyError(name)
