@@ -17,7 +17,8 @@ OUT = os.path.join(PKG, "libdflash.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("DFLASH_ARCH", "gfx950")
 
-HIP_SOURCES = ["gemm.hip", "attention.hip", "head.hip", "elementwise.hip", "ddtree.hip", "spec_verify.hip", "tree_attn.hip"]
+HIP_SOURCES = ["gemm.hip", "attention.hip", "head.hip", "elementwise.hip", "ddtree.hip", "spec_verify.hip", "tree_attn.hip",
+               "scratch.hip"]
 CPP_SOURCES = ["dflash_api.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]

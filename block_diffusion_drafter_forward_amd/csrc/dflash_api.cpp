@@ -447,14 +447,18 @@ static hipError_t project(const dflash_handle* h, const GemmPlan& p, const void*
 
 // The drafter pass; sample != 0 draws each row's token at temperature 1 (Gumbel-max, keyed by seed) instead
 // of taking the argmax, and logits_out (nullable) receives the full logits.
+// static_scratch: the workspace is the library's own static scratch (ws and ws_bytes unused), looked up only
+// after every argument check has passed.
 static int draft_impl(dflash_handle* h, int batch, const int32_t* block_tokens, const int32_t* ctx_len,
                       const int32_t* page_table, int max_pages, const dflash_kv* kv, int max_ctx, int top_k,
                       int sample, uint64_t seed, int32_t* tokens, int32_t* topk_ids, float* topk_logprobs,
-                      float* logits_out, const dflash_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
+                      float* logits_out, const dflash_debug* dbg, void* ws, size_t ws_bytes, bool static_scratch,
+                      void* stream) {
     if (!h) return fail(DFLASH_E_ARG, "handle is NULL");
     const dflash_config& c = h->cfg;
     if (batch < 1) return fail(DFLASH_E_ARG, "batch must be >= 1");
-    if (!block_tokens || !ctx_len || !tokens || !ws) return fail(DFLASH_E_ARG, "a required pointer is NULL");
+    if (!block_tokens || !ctx_len || !tokens || (!ws && !static_scratch))
+        return fail(DFLASH_E_ARG, "a required pointer is NULL");
     if (top_k < 0 || top_k > DF_TOPK) return fail(DFLASH_E_UNSUPPORTED, "top_k must be in [0, 8]");
     if (top_k > c.vocab) return fail(DFLASH_E_ARG, "top_k exceeds the vocabulary");
     if (top_k > 0 && (!topk_ids || !topk_logprobs)) return fail(DFLASH_E_ARG, "top-k outputs are NULL");
@@ -469,9 +473,18 @@ static int draft_impl(dflash_handle* h, int batch, const int32_t* block_tokens, 
         return fail(DFLASH_E_UNSUPPORTED, "float32 drafters support batch * block_len <= 32 (got %d)",
                     batch * c.block_len);
     const DraftPlan p = plan_draft(c, batch, max_ctx);
-    if (ws_bytes < p.total) return fail(DFLASH_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, p.total);
-    if (((uintptr_t)ws) & 255) return fail(DFLASH_E_ARG, "workspace must be 256-byte aligned");
+    if (static_scratch) {
+        if (p.total > DFLASH_NOALLOC_SCRATCH_BYTES)
+            return fail(DFLASH_E_CAPACITY,
+                        "batch %d with max_ctx %d needs %zu bytes of scratch; the allocation-free pass has %u "
+                        "(use dflash_draft_block with a workspace)",
+                        batch, max_ctx, p.total, (unsigned)DFLASH_NOALLOC_SCRATCH_BYTES);
+    } else {
+        if (ws_bytes < p.total) return fail(DFLASH_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, p.total);
+        if (((uintptr_t)ws) & 255) return fail(DFLASH_E_ARG, "workspace must be 256-byte aligned");
+    }
     if (is_bf16(c) && !h->packed) return fail(DFLASH_E_ARG, "bfloat16 weights are not packed (dflash_pack_weights)");
+    if (static_scratch) HIP_TRY(scratch_region(&ws, &ws_bytes));
 
     hipStream_t st = (hipStream_t)stream;
     char* W = (char*)ws;
@@ -585,7 +598,16 @@ extern "C" int dflash_draft_block(dflash_handle* h, int batch, const int32_t* bl
                                   int top_k, int32_t* tokens, int32_t* topk_ids, float* topk_logprobs,
                                   const dflash_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
     return draft_impl(h, batch, block_tokens, ctx_len, page_table, max_pages, kv, max_ctx, top_k, 0, 0, tokens,
-                      topk_ids, topk_logprobs, dbg ? dbg->logits : nullptr, dbg, ws, ws_bytes, stream);
+                      topk_ids, topk_logprobs, dbg ? dbg->logits : nullptr, dbg, ws, ws_bytes, false, stream);
+}
+
+extern "C" int dflash_draft_block_noalloc(dflash_handle* h, int batch, const int32_t* block_tokens,
+                                          const int32_t* ctx_len, const int32_t* page_table, int max_pages,
+                                          const dflash_kv* kv, int max_ctx, int top_k, int32_t* tokens,
+                                          int32_t* topk_ids, float* topk_logprobs, const dflash_debug* dbg,
+                                          void* stream) {
+    return draft_impl(h, batch, block_tokens, ctx_len, page_table, max_pages, kv, max_ctx, top_k, 0, 0, tokens,
+                      topk_ids, topk_logprobs, dbg ? dbg->logits : nullptr, dbg, nullptr, 0, true, stream);
 }
 
 extern "C" int dflash_draft_block_sample(dflash_handle* h, int batch, const int32_t* block_tokens,
@@ -594,7 +616,7 @@ extern "C" int dflash_draft_block_sample(dflash_handle* h, int batch, const int3
                                          int32_t* topk_ids, float* topk_logprobs, float* logits, void* ws,
                                          size_t ws_bytes, void* stream) {
     return draft_impl(h, batch, block_tokens, ctx_len, page_table, max_pages, kv, max_ctx, top_k, 1, seed, tokens,
-                      topk_ids, topk_logprobs, logits, nullptr, ws, ws_bytes, stream);
+                      topk_ids, topk_logprobs, logits, nullptr, ws, ws_bytes, false, stream);
 }
 
 // ---------------------------------------------------------------------------------------------------------

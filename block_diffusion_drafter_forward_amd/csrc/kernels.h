@@ -29,6 +29,11 @@ extern thread_local LaunchTiming* df_launch_timing;
         }                                                                                                  \
     } while (0)
 
+// ---- allocation-free scratch -------------------------------------------------------------------------------
+// The calling device's copy of the library's static scratch (DFLASH_NOALLOC_SCRATCH_BYTES): its device address
+// and size.  The first call on a device looks the address up (no allocation); later calls reuse it.
+hipError_t scratch_region(void** ptr, size_t* bytes);
+
 // ---- GEMM ------------------------------------------------------------------------------------------------
 enum GemmKind { GEMM_SKINNY1 = 0, GEMM_SKINNY2 = 1, GEMM_TILED = 2, GEMM_F32 = 3 };
 struct GemmPlan {

@@ -77,6 +77,10 @@ _SIGS = {
                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.POINTER(dflash_debug), ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.c_void_p]),
+    "dflash_draft_block_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(dflash_kv),
+                                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.POINTER(dflash_debug), ctypes.c_void_p]),
     "dflash_accept_len": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     "dflash_draft_block_sample": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -201,6 +205,15 @@ def dflash_draft_block(h, batch, block_tokens, ctx_len, page_table, max_pages, k
                                     ctypes.byref(kv) if kv is not None else None, max_ctx, top_k, tokens, topk_ids,
                                     topk_logprobs, ctypes.byref(dbg) if dbg is not None else None, ws, ws_bytes,
                                     stream)
+
+
+def dflash_draft_block_noalloc(h, batch, block_tokens, ctx_len, page_table, max_pages, kv: Optional[dflash_kv],
+                               max_ctx, top_k, tokens, topk_ids, topk_logprobs, dbg: Optional[dflash_debug],
+                               stream) -> int:
+    return lib().dflash_draft_block_noalloc(h, batch, block_tokens, ctx_len, page_table, max_pages,
+                                            ctypes.byref(kv) if kv is not None else None, max_ctx, top_k, tokens,
+                                            topk_ids, topk_logprobs, ctypes.byref(dbg) if dbg is not None else None,
+                                            stream)
 
 
 def dflash_accept_len(batch, n_draft, draft, draft_stride, target, target_stride, tau, stream) -> int:

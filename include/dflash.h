@@ -24,7 +24,7 @@
  *
  * Conventions
  *   - Every pointer marked "device" is GPU memory owned by the caller; the library never allocates, frees
- *     or keeps device memory between calls.  Host structs are read during the call only (the handle keeps
+ *     or keeps device memory between calls, except the static scratch of dflash_draft_block_noalloc.  Host structs are read during the call only (the handle keeps
  *     a copy of the config and of the weight pointers).
  *   - Matrices are row-major [out, in] ("W[n][k]"), bfloat16 (DFLASH_BF16) or float32 (DFLASH_F32).
  *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream) and never
@@ -190,6 +190,23 @@ int dflash_draft_block(dflash_handle *h, int batch, const int32_t *block_tokens,
                        const int32_t *page_table, int max_pages, const dflash_kv *kv, int max_ctx, int top_k,
                        int32_t *tokens, int32_t *topk_ids, float *topk_logprobs, const dflash_debug *dbg,
                        void *ws, size_t ws_bytes, void *stream);
+
+/* Allocation-free variant of dflash_draft_block, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same pass, arguments (less the
+ * workspace) and results.  The workspace is a static device array of DFLASH_NOALLOC_SCRATCH_BYTES inside the
+ * library, which each GPU the library runs on holds from the code object's load until the process ends; the
+ * first call on a device looks up its address there (no allocation).  A call whose
+ * dflash_draft_workspace_bytes(h, batch, max_ctx) exceeds the array returns DFLASH_E_CAPACITY before anything
+ * runs (every batch-1 pass of the 4B- and 8B-sized drafters fits, at any context length).  Every call on one
+ * GPU uses that GPU's one array, which keeps the last call's contents (the pass writes every byte it reads):
+ * calls that overlap on one GPU -- on several streams, threads or handles -- race and give undefined results.
+ * The device error word of this variant lives in the array and is not reported; dflash_draft_block reports
+ * it.                                                                                                      */
+#define DFLASH_NOALLOC_SCRATCH_BYTES (32u << 20)
+int dflash_draft_block_noalloc(dflash_handle *h, int batch, const int32_t *block_tokens, const int32_t *ctx_len,
+                               const int32_t *page_table, int max_pages, const dflash_kv *kv, int max_ctx,
+                               int top_k, int32_t *tokens, int32_t *topk_ids, float *topk_logprobs,
+                               const dflash_debug *dbg, void *stream);
 
 /* tau[r] = 1 + the number of leading j < n_draft with draft[r*draft_stride + j] == target[r*target_stride
  * + j]; tau lies in [1, n_draft + 1].  Typical call: draft = tokens + 1 with stride L, n_draft = L - 1.

@@ -409,3 +409,26 @@ def test_inject_short_last_chunk_needs_its_own_split_partials(D):
         assert D.dflash_inject_workspace_bytes(m.handle, 4096 + 1000) >= with_tail
     finally:
         m.close()
+
+
+def test_noalloc_pass_validates_before_touching_the_gpu(D):
+    """dflash_draft_block_noalloc shares the pass's argument checks and refuses, before any HIP call, a pass
+    whose workspace would exceed its static scratch (DFLASH_NOALLOC_SCRATCH_BYTES = 32 MiB)."""
+    import workloads as W
+    m = _create(D, W.QWEN3_8B)
+    kv = D.dflash_kv(0x40, 0x50, 8192)
+    call = lambda **o: D.dflash_draft_block_noalloc(m.handle, o.get("batch", 1), 0x10, 0x20, 0x30,
+                                                    o.get("max_pages", 512), kv, o.get("max_ctx", 4096), 8, 0x60,
+                                                    0x70, 0x80, None, None)
+    try:
+        assert D.dflash_draft_workspace_bytes(m.handle, 16, 8192) > 32 << 20
+        assert call(batch=16, max_ctx=8192) == D.DFLASH_E_CAPACITY
+        assert "allocation-free" in D.dflash_last_error()
+        assert call(batch=0) == D.DFLASH_E_ARG
+        assert call(max_ctx=8193) == D.DFLASH_E_CAPACITY        # beyond max_pages * 16
+        # batch 1 at any context fits: the call gets as far as the missing weight store
+        for ctx in (0, 4096, 8192):
+            assert D.dflash_draft_workspace_bytes(m.handle, 1, ctx) <= 32 << 20
+            assert call(max_ctx=ctx) == D.DFLASH_E_ARG and "packed" in D.dflash_last_error()
+    finally:
+        m.close()
