@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "drafter block fwd µs & blocks/s (Qwen3-8B-shape, B=1, L=16); HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
 N_NEW = 7  # tokens committed per cycle: the pages report mean acceptance of about 6.5-7.8 for Qwen3-8B
+KV_COPIES = 4  # cache copies rotated for the cold-K/V figures
 
 
 def parse():
@@ -131,6 +132,149 @@ def launch_bytes(name, s, batch, ctx_total):
     return 0
 
 
+def pass_bytes(s, batch, ctx_total):
+    """Algorithmic bytes of one drafter pass (the spec byte model): every weight of the pass read once
+    (the drafter layers' projections and the shared LM head) plus every request's context K/V read once per
+    layer.  Activations and the two embedding rows are left out."""
+    E = 2 if s.bf16 else 4
+    H, qd, kvd, F, V = s.hidden, s.q_dim, s.kv_dim, s.ffn, s.vocab
+    weights = s.n_layers * (H * (qd + 2 * kvd) + qd * H + 2 * F * H + F * H) + V * H
+    return weights * E + s.n_layers * ctx_total * 2 * kvd * E
+
+
+def launch_flops(name, s, batch):
+    """(algorithmic, executed) floating-point operations of one launch of a profiled GEMM or LM head: 2 M N K
+    for the product; executed doubles it where the activation enters as a hi/lo pair of bfloat16 planes."""
+    M = batch * s.block_len
+    if name.startswith("gemm_"):
+        parts = dict(kv.split("=") for kv in name.split()[1:])
+        N, K = int(parts["N"]), int(parts["K"])
+        m = N_NEW * batch if (K == s.feat_dim or N == s.n_layers * 2 * s.kv_dim) else M
+        alg = 2.0 * m * N * K
+        return alg, alg * (2 if name.split()[0].endswith("_pair") else 1)
+    if name.startswith("lm_head"):
+        alg = 2.0 * M * s.vocab * s.hidden
+        return alg, alg * (2 if s.bf16 else 1)
+    return 0.0, 0.0
+
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bfloat16 MFMA
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def gpu_clock_state():
+    """Current shader and memory clock levels of the GPU (sysfs DPM tables, else rocm-smi); None if unreadable."""
+    import glob
+    import subprocess
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for key in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                lines = open(os.path.join(dev, key)).read().splitlines()
+            except OSError:
+                continue
+            cur = [l.split(":", 1)[1].strip().rstrip("*").strip() for l in lines if l.strip().endswith("*")]
+            if cur:
+                out[key.replace("pp_dpm_", "")] = cur[0]
+        if out:
+            out["source"] = os.path.join(dev, "pp_dpm_*")
+            return out
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+        lines = [l.strip() for l in r.stdout.splitlines() if "clk" in l.lower() and "(" in l]
+        if lines:
+            return {"rocm_smi": lines[:8]}
+    except Exception:
+        pass
+    return None
+
+
+def _f32(a):
+    import workloads as W
+    return W.bf16_bits_to_f32(a) if a.dtype == np.uint16 else np.asarray(a, dtype=np.float32)
+
+
+def cpu_fp32_cycle(wl, weights, ctx_kv, n_new):
+    """A plain float32 NumPy run of the same steady-state cycle (the oracle's steps, in float32 and without
+    rounding the cache): inject n_new tokens, one drafter pass, acceptance.  ctx_kv[r][l] = (K, V) of the
+    context before the new tokens.  Returns (seconds, logits [B, L, V])."""
+    s = wl.shape
+    import workloads as W
+    t0 = time.perf_counter()
+    d, nq, nkv = s.head_dim, s.n_q_heads, s.n_kv_heads
+    inv = (np.float64(s.rope_theta) ** (-(2.0 * np.arange(d // 2)) / d)).astype(np.float32) if s.rope_theta > 0 else None
+
+    def rope(x, pos):  # x [n, heads, d], rotate-half pairs
+        if inv is None:
+            return x
+        ang = pos.astype(np.float32)[:, None] * inv[None, :]
+        c, sn = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+        a, b = x[..., : d // 2], x[..., d // 2:]
+        return np.concatenate([a * c - b * sn, b * c + a * sn], axis=-1)
+
+    def rms(h, g):
+        return h / np.sqrt((h * h).mean(-1, keepdims=True) + np.float32(s.rms_eps)) * _f32(g)
+
+    kv = []
+    fc = _f32(weights["fc_w"])
+    for r in range(wl.batch):
+        C = int(wl.ctx_lens()[r])
+        f = _f32(wl.features(r, n_new, row0=C - n_new)) @ fc.T
+        if "fc_b" in weights:
+            f = f + _f32(weights["fc_b"])
+        pos = np.arange(C - n_new, C)
+        layers = []
+        for l in range(s.n_layers):
+            k = rope((f @ _f32(weights[f"l{l}.uk"]).T).reshape(n_new, nkv, d), pos)
+            v = (f @ _f32(weights[f"l{l}.uv"]).T).reshape(n_new, nkv, d)
+            k0, v0 = ctx_kv[r][l]
+            layers.append((np.concatenate([k0, k]), np.concatenate([v0, v])))
+        kv.append(layers)
+    bt = wl.block_tokens()
+    B, L = bt.shape
+    h = _f32(weights["embed"][bt.reshape(-1)])
+    for l in range(s.n_layers):
+        p = f"l{l}."
+        u = rms(h, weights[p + "attn_norm"])
+        q = (u @ _f32(weights[p + "wq"]).T).reshape(B, L, nq, d)
+        kb = (u @ _f32(weights[p + "wk"]).T).reshape(B, L, nkv, d)
+        vb = (u @ _f32(weights[p + "wv"]).T).reshape(B, L, nkv, d)
+        o = np.empty((B, L, nq, d), dtype=np.float32)
+        for r in range(B):
+            C = kv[r][l][0].shape[0]
+            pos = np.arange(C, C + L)
+            qr, kr = rope(q[r], pos), rope(kb[r], pos)
+            keys = np.concatenate([kv[r][l][0], kr])
+            vals = np.concatenate([kv[r][l][1], vb[r]])
+            for hh in range(nq):
+                g = hh * nkv // nq
+                sc = qr[:, hh] @ keys[:, g].T / np.float32(np.sqrt(d))
+                sc = np.exp(sc - sc.max(-1, keepdims=True))
+                o[r, :, hh] = (sc / sc.sum(-1, keepdims=True)) @ vals[:, g]
+        h = h + o.reshape(B * L, nq * d) @ _f32(weights[p + "wo"]).T
+        u2 = rms(h, weights[p + "ffn_norm"])
+        gt = u2 @ _f32(weights[p + "w_gate"]).T
+        h = h + ((gt / (1 + np.exp(-gt))) * (u2 @ _f32(weights[p + "w_up"]).T)) @ _f32(weights[p + "w_down"]).T
+    logits = rms(h, weights["final_norm"]) @ _f32(weights["lm_head"]).T
+    tokens = logits.argmax(-1).reshape(B, L)
+    np.argpartition(-logits, wl.top_k, axis=-1)
+    bern, rand = wl.target_draws()
+    target = W.make_target(tokens, bern, rand)
+    eq = tokens[:, 1:] == target[:, : L - 1]
+    _ = 1 + np.where(eq.all(1), L - 1, eq.argmin(1))
+    return time.perf_counter() - t0, logits.reshape(B, L, -1)
+
+
 def _oracle_cores():
     try:
         from threadpoolctl import threadpool_info
@@ -190,21 +334,29 @@ def cpu_baseline(wl, weights, n_new, cap_s):
     kv = []
     for r in range(wl.batch):
         C = int(wl.ctx_lens()[r])
-        kv.append(O.inject(weights, s, wl.features(r, C - n_new), 0))
+        kv.append(O.inject(weights, s, wl.features(r, C - n_new), 0, fc_b=weights.get("fc_b")))
     t0 = time.perf_counter()
     for r in range(wl.batch):
         C = int(wl.ctx_lens()[r])
-        tail = O.inject(weights, s, wl.features(r, n_new, row0=C - n_new), C - n_new)
+        tail = O.inject(weights, s, wl.features(r, n_new, row0=C - n_new), C - n_new, fc_b=weights.get("fc_b"))
         kv[r] = [(np.concatenate([kv[r][l][0], tail[l][0]]), np.concatenate([kv[r][l][1], tail[l][1]]))
                  for l in range(s.n_layers)]
     out = O.draft_block(weights, s, kv, wl.block_tokens(), wl.top_k)
     bern, rand = wl.target_draws()
     O.accept_len(out["tokens"][:, 1:], W.make_target(out["tokens"], bern, rand))
     dt = time.perf_counter() - t0
+    # the same cycle as plain float32 NumPy (the prefilled context K/V reused, cast to float32)
+    ctx_kv = [[(kv[r][l][0][: -n_new].astype(np.float32), kv[r][l][1][: -n_new].astype(np.float32))
+               for l in range(s.n_layers)] for r in range(wl.batch)]
+    dt32, lg32 = cpu_fp32_cycle(wl, weights, ctx_kv, n_new)
     return {"value": wl.batch / dt, "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
             "sample": f"one full cycle of {wl.name} (inject {n_new} tokens x {wl.batch} request(s) + drafter pass "
                       f"+ acceptance), fp64 NumPy, after an untimed oracle prefill of the context; "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s",
+            "cpu_model": cpu_model(),
+            "fp32_numpy": {"value": wl.batch / dt32, "unit": "blocks/s", "kind": "numpy-fp32",
+                           "sample": f"the same cycle in float32 NumPy; {dt32:.2f} s",
+                           "max_logit_diff_vs_oracle": float(np.abs(lg32 - out["logits"]).max())}}
 
 
 def sweep_block(args):
@@ -619,6 +771,68 @@ def main():
     ms_draft = e0.elapsed_time(e1) / args.steps
     assert g.error_word() == 0, "device error word set"
 
+    # Cold K/V: the same pass and cycle rotating over KV_COPIES copies of the cache (whose total exceeds the
+    # 256 MB Infinity Cache at 4 x 84 MB), so that no pass finds its context K/V left in the cache by the
+    # pass before.  The weights (3.2 GB) never fit, so they are cold either way.
+    kv_copies = [g.kv]
+    pools = []
+    for _ in range(KV_COPIES - 1):
+        kp, vp = g.kpool.clone(), g.vpool.clone()
+        pools.append((kp, vp))
+        kv_copies.append(D.make_kv(kp, vp, g.n_pages))
+
+    def draft_on(kv):
+        g.model.draft(g.block_tokens, g.ctx_len, g.page_table, kv, g.max_ctx, wl.top_k, g.tokens, g.topk_ids,
+                      g.topk_lp, g.draft_ws, stream=stream)
+
+    def step_on(kv):
+        g.model.inject(feats_d, offs_d, start_d, g.page_table, kv, inj_ws, stream=stream)
+        draft_on(kv)
+        g.accept(target, stream=stream)
+
+    def timed_rotating(fn):
+        for i in range(KV_COPIES):
+            fn(kv_copies[i])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(kv_copies[i % KV_COPIES])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_draft_cold = timed_rotating(draft_on)
+    ms_step_cold = timed_rotating(step_on)
+    ref_tok = g.tokens.clone()
+    draft_on(kv_copies[0])
+    torch.cuda.synchronize()
+    assert torch.equal(ref_tok, g.tokens), "drafts differ between cache copies"
+    del kv_copies, pools
+
+    # Prefill: dflash_inject_ctx of every request's whole context in one call (fusion GEMM over C rows, then
+    # K/V of every layer), into a scratch copy of the cache; MFMA-bound at C = 4096.
+    kp, vp = g.kpool.clone(), g.vpool.clone()
+    kv_pre = D.make_kv(kp, vp, g.n_pages)
+    pre_rows = int(ctx.sum())
+    pre_feats = S.to_device(np.concatenate([wl.features(r, int(ctx[r])) for r in range(wl.batch)], axis=0))
+    pre_offs = S.to_device(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32))
+    pre_start = S.to_device(np.zeros(wl.batch, dtype=np.int32))
+    pre_ws = g.model.inject_workspace(pre_rows)
+
+    def prefill():
+        g.model.inject(pre_feats, pre_offs, pre_start, g.page_table, kv_pre, pre_ws, stream=stream)
+
+    prefill()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(3):
+        prefill()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_prefill = e0.elapsed_time(e1) / 3
+    pre_flops = 2.0 * pre_rows * s.hidden * (s.feat_dim + s.n_layers * 2 * s.kv_dim)
+    del pre_feats, kv_pre, kp, vp, pre_ws
+
     # per-kernel HIP-event timing over a few steps (separate from the timed region)
     prof_steps = 5
     D.check(D.dflash_profile_enable(g.model.handle, 1), "profile_enable")
@@ -641,13 +855,37 @@ def main():
         gsum["bytes"] += nb * d["launches_per_step"]
         gsum["us"] += d["total_us_per_step"]
         gsum["launches"] += d["launches_per_step"]
+    for n, d in kernels.items():
+        alg, exe = launch_flops(n, s, wl.batch)
+        if alg:
+            gsum = groups[n.split(" ")[0]]
+            gsum["flops"] = gsum.get("flops", 0.0) + alg * d["launches_per_step"]
+            gsum["flops_exec"] = gsum.get("flops_exec", 0.0) + exe * d["launches_per_step"]
     dom = max(groups, key=lambda k: groups[k]["us"])
     gd = groups[dom]
-    achieved = gd["bytes"] / (gd["us"] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(dom, wl.name), "kernel": dom,
-                "bytes_per_launch": int(gd["bytes"] / gd["launches"]),
-                "avg_launch_us": round(gd["us"] / gd["launches"], 2), "launches_per_step": gd["launches"]}
+    # the bound follows the kernel's executed operations per algorithmic byte against the MI355X ridge
+    # (2.5 PFLOP/s bf16 / 8 TB/s = 312.5 FLOP/B)
+    intensity = gd.get("flops_exec", 0.0) / gd["bytes"]
+    if intensity > RIDGE_FLOP_PER_BYTE:
+        achieved = gd["flops"] / (gd["us"] * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(dom, wl.name),
+                    "kernel": dom, "flops_per_launch": gd["flops"] / gd["launches"],
+                    "executed_frac": round(gd["flops_exec"] / (gd["us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = gd["bytes"] / (gd["us"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(dom, wl.name),
+                    "kernel": dom}
+    roofline.update({"bytes_per_launch": int(gd["bytes"] / gd["launches"]),
+                     "avg_launch_us": round(gd["us"] / gd["launches"], 2), "launches_per_step": gd["launches"],
+                     "flop_per_byte_executed": round(intensity, 1)})
+    pbytes = pass_bytes(s, wl.batch, int(ctx.sum()))
+    pass_roofline = {"bound": "hbm", "bytes": int(pbytes), "us": round(ms_draft * 1e3, 1),
+                     "achieved": round(pbytes / (ms_draft * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(pbytes / (ms_draft * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "us_at_70pct": round(pbytes / (0.7 * PEAK_HBM_GBS * 1e9) * 1e6, 1),
+                     "frac_cold_kv": round(pbytes / (ms_draft_cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     per_kernel_roofline = {k: {"gbs": round(v["bytes"] / (v["us"] * 1e-6) / 1e9, 1), "us_per_step": round(v["us"], 1)}
                            for k, v in groups.items()}
 
@@ -671,6 +909,14 @@ def main():
         "us_per_step": round(ms_step * 1e3, 1),
         "us_per_step_graph_replay": round(ms_step_graph * 1e3, 1) if ms_step_graph is not None else None,
         "draft_block_us": round(ms_draft * 1e3, 1),
+        "draft_block_us_cold_kv": round(ms_draft_cold * 1e3, 1),
+        "us_per_step_cold_kv": round(ms_step_cold * 1e3, 1),
+        "kv_copies_rotated": KV_COPIES,
+        "pass_roofline": pass_roofline,
+        "prefill_inject": {"rows": pre_rows, "us": round(ms_prefill * 1e3, 1),
+                           "tflops": round(pre_flops / (ms_prefill * 1e-3) / 1e12, 1),
+                           "frac_of_bf16_peak": round(pre_flops / (ms_prefill * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "gpu_clocks": gpu_clock_state(),
         "step_algorithmic_bytes": int(total_bytes),
         "step_hbm_gbs": round(total_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(total_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
