@@ -470,7 +470,15 @@ def ddtree_bench(args):
                                           tok.data_ptr(), par.data_ptr(), dep.data_ptr(), lq.data_ptr(), n.data_ptr(),
                                           st), "build")
 
+        def select():
+            D.check(D.dflash_ddtree_select(B, L - 1, K, lp.data_ptr() + 4 * K, ids.data_ptr() + 4 * K, L * K,
+                                           budget, tok.data_ptr(), par.data_ptr(), dep.data_ptr(), lq.data_ptr(),
+                                           n.data_ptr(), st), "select")
+
         topk()
+        select()
+        torch.cuda.synchronize()
+        undecided = int((n == -1).sum().item())
         build()
         torch.cuda.synchronize()
         tk, pa, nn = tok.cpu().numpy(), par.cpu().numpy(), n.cpu().numpy()
@@ -489,7 +497,7 @@ def ddtree_bench(args):
                                          tgt_d.data_ptr(), alen.data_ptr(), anodes.data_ptr(), bonus.data_ptr(), st),
                     "walk")
 
-        us_topk, us_build, us_walk = timed(topk), timed(build), timed(walk)
+        us_topk, us_select, us_build, us_walk = timed(topk), timed(select), timed(build), timed(walk)
         walk()
         torch.cuda.synchronize()
         cpu = None
@@ -497,7 +505,9 @@ def ddtree_bench(args):
             cpu = cpu_baseline_ddtree(logits[0, 1:].cpu().double().numpy(), budget, tgt[0])
         print(json.dumps({"ddtree": wl.name, "budget": budget, "K": K, "depth": L - 1, "nodes": int(nn[0]),
                           "draft_block_us": round(us_draft, 1), "draft_block_with_logits_us": round(us_draft_logits, 1),
-                          "topk_us": round(us_topk, 1), "build_us": round(us_build, 1), "walk_us": round(us_walk, 1),
+                          "topk_us": round(us_topk, 1), "build_us": round(us_build, 1),
+                          "select_only_us": round(us_select, 1), "select_undecided": undecided,
+                          "walk_us": round(us_walk, 1),
                           "accepted_nodes": int(alen.cpu()[0]), "cpu_baseline": cpu,
                           "topk_logits_gbs": round(B * L * V * 4 / (us_topk * 1e-6) / 1e9, 1)}), flush=True)
 

@@ -318,15 +318,18 @@ __device__ __forceinline__ uint32_t dt_meta(int parent, int depth, int rank) {
     return ((uint32_t)(parent + 1) << 16) | ((uint32_t)depth << 11) | (uint32_t)rank;
 }
 
+// With `only_undecided`, a request whose n_nodes entry is not -1 was already built by ddtree_select and is
+// left alone.
 __global__ __launch_bounds__(64) void ddtree_build(int D, int K, const float* __restrict__ lp,
                                                    const int32_t* __restrict__ ids, int64_t req_stride, int budget,
                                                    int32_t* __restrict__ node_token, int32_t* __restrict__ node_parent,
                                                    int32_t* __restrict__ node_depth, float* __restrict__ node_logq,
-                                                   int32_t* __restrict__ n_nodes) {
+                                                   int32_t* __restrict__ n_nodes, int only_undecided) {
     __shared__ DtSlot slot[DT_POOL];                 // key 0: popped (or never written)
     __shared__ uint2 nrec[DT_POOL / 2];              // popped nodes: (meta, score bits)
     __shared__ float slq[DT_MAXD * TK_MAX];
     const int r = blockIdx.x, lane = threadIdx.x;
+    if (only_undecided && n_nodes[r] != -1) return;
     const float* l = lp + (size_t)r * req_stride;
     const int32_t* idr = ids + (size_t)r * req_stride;
     // the log-probabilities into LDS, sixteen independent loads in flight per lane
@@ -409,11 +412,462 @@ __global__ __launch_bounds__(64) void ddtree_build(int D, int K, const float* __
     if (lane == 0) n_nodes[r] = n;
 }
 
+// ------------------------------------------------------------------------------------------------------
+// the same tree by parallel selection, one 1024-thread workgroup per request
+// ------------------------------------------------------------------------------------------------------
+// Scores are float32 path sums (parent score + own log-probability), so along every edge of Algorithm 1's
+// generation order (a tuple -> its next sibling, a tuple -> its first child) the score never rises when the
+// log-probabilities are <= 0 and each depth's row is non-increasing.  The pops therefore come out in
+// non-increasing score order, equal scores in creation order, and the first B pops are the B best tuples
+// under that order (Proposition 2 of §3.4.3).  The kernel finds them without the heap:
+//   1. a pool in LDS holds every tuple whose score key is >= a threshold tau, which only rises and always
+//      stays at or below the B-th best score, level by level: the children of depth d's pool entries with
+//      scores >= tau are a rank prefix of each parent (a binary search over the sorted row), appended in
+//      parent order;
+//   2. when the pool would overflow, tau is raised to the lower edge of the histogram bin that holds the B-th
+//      best key in the pool (refined inside that bin up to three times) and everything below is dropped;
+//      a child never scores above its parent, so the pool stays prefix-closed;
+//   3. the pool is sorted by score (bitonic, in LDS), runs of equal scores are put in creation order by
+//      comparing their generators (the previous sibling, or the parent for a first child; one generator's
+//      sibling is created before its child), and the first B entries are the tree.
+// A request it cannot decide -- rows that are not sorted log-probabilities, runs of more than DS_RUN_MAX
+// equal scores, a tie chain longer than DS_WALK_MAX, a pool that no threshold can thin -- gets
+// n_nodes = -1; ddtree_build then runs the heap on it.
+#define DS_THREADS 1024
+#define DS_CAP 4096
+#define DS_NB 2048
+#define DS_RUN_MAX 32
+#define DS_WALK_MAX 256
+#define DS_MAX_RAISES 64
+
+struct DsLds {
+    float lq[DT_MAXD * TK_MAX];  // row d at d * K
+    uint32_t key[DS_CAP];        // order key of the score
+    uint32_t meta[DS_CAP];       // (parent + 1) << 15 | depth << 10 | rank; parent = pool index, -1 at depth 1
+    union {
+        struct {
+            uint32_t rc[DS_CAP];   // per parent of the level being built: next rank << 16 | end rank
+            uint32_t off[DS_CAP];  // exclusive prefix of the ranks still to append
+        } lv;
+        uint64_t sk[DS_CAP];  // sort keys: score key << 32 | 0xFFFF - pool index
+    } u;
+    uint16_t idx[DS_CAP];  // compaction targets, then output positions
+    uint32_t hist[DS_NB];
+    uint32_t red[2 * (DS_THREADS / 64)];
+    int flag, bstar;
+    uint32_t above, inbin;
+};
+
+__device__ __forceinline__ uint32_t ds_meta(int p, int d, int r) {
+    return ((uint32_t)(p + 1) << 15) | ((uint32_t)d << 10) | (uint32_t)r;
+}
+__device__ __forceinline__ int ds_par(uint32_t m) { return (int)(m >> 15) - 1; }
+__device__ __forceinline__ int ds_dep(uint32_t m) { return (int)((m >> 10) & 31u); }
+__device__ __forceinline__ int ds_rank(uint32_t m) { return (int)(m & 1023u); }
+__device__ __forceinline__ int ds_slot(uint64_t k) { return 0xFFFF - (int)(k & 0xFFFFu); }
+
+// Score key of the tuple (pool parent p, depth d, rank r): the parent's score + the log-probability.
+__device__ __forceinline__ uint32_t ds_score(const DsLds& s, int K, int p, int d, int r) {
+    const float sp = p < 0 ? 0.f : key_value(s.key[p]);
+    return order_key(sp + s.lq[(d - 1) * K + r]);
+}
+
+// Block-wide exclusive prefix sum (all threads call it); `total` gets the sum over the block.
+__device__ __forceinline__ uint32_t ds_scan(uint32_t v, uint32_t* red, uint32_t& total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) red[w] = x;
+    __syncthreads();
+    uint32_t base = 0u, tot = 0u;
+#pragma unroll
+    for (int i = 0; i < DS_THREADS / 64; ++i) {
+        const uint32_t q = red[i];
+        base += i < w ? q : 0u;
+        tot += q;
+    }
+    __syncthreads();
+    total = tot;
+    return base + x - v;
+}
+
+__device__ __forceinline__ void ds_minmax(uint32_t& mn, uint32_t& mx, uint32_t* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+    }
+    if (lane == 0) {
+        red[w] = mn;
+        red[DS_THREADS / 64 + w] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < DS_THREADS / 64; ++i) {
+        mn = min(mn, red[i]);
+        mx = max(mx, red[DS_THREADS / 64 + i]);
+    }
+    __syncthreads();
+}
+
+// First rank in [lo, hi) of depth-(d + 1) row whose score under a parent of score sp falls below tau (the
+// scores fall with the rank); hi when none does.
+__device__ __forceinline__ int ds_count(const DsLds& s, int K, float sp, int d, int lo, int hi, uint32_t tau) {
+    const float* row = s.lq + d * K;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (order_key(sp + row[mid]) >= tau)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+// A threshold >= tau that keeps at least `budget` of the N > budget pool entries: the lower edge of the
+// histogram bin holding the budget-th best key, the bin refined by further histograms while it holds many.
+__device__ uint32_t ds_raise(DsLds& s, int N, int budget, uint32_t tau) {
+    const int t = threadIdx.x;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int e = t; e < N; e += DS_THREADS) {
+        const uint32_t k = s.key[e];
+        lo = min(lo, k);
+        hi = max(hi, k);
+    }
+    ds_minmax(lo, hi, s.red);
+    uint32_t need = (uint32_t)budget, v = lo;  // `need` of the keys in [lo, hi] are still to be kept
+    for (int round = 0; round < 3 && hi > lo; ++round) {
+        const uint32_t span = hi - lo;
+        const int sh = max(0, 32 - __clz((int)span) - 11);  // (k - lo) >> sh < DS_NB
+        for (int b = t; b < DS_NB; b += DS_THREADS) s.hist[b] = 0u;
+        __syncthreads();
+        for (int e = t; e < N; e += DS_THREADS) {
+            const uint32_t k = s.key[e];
+            if (k >= lo && k <= hi) atomicAdd(&s.hist[(k - lo) >> sh], 1u);
+        }
+        __syncthreads();
+        const int b0 = DS_NB - 1 - 2 * t;  // two bins per thread, from the top
+        const uint32_t h0 = s.hist[b0], h1 = s.hist[b0 - 1];
+        uint32_t tot;
+        const uint32_t above = ds_scan(h0 + h1, s.red, tot);
+        if (above < need && above + h0 >= need) {
+            s.bstar = b0;
+            s.above = above;
+            s.inbin = h0;
+        } else if (above + h0 < need && above + h0 + h1 >= need) {
+            s.bstar = b0 - 1;
+            s.above = above + h0;
+            s.inbin = h1;
+        }
+        __syncthreads();
+        const uint32_t bs = (uint32_t)s.bstar, ab = s.above, ib = s.inbin;
+        __syncthreads();
+        v = lo + (bs << sh);
+        if (sh == 0 || ab + ib <= need + DS_CAP / 32) break;
+        need -= ab;  // refine inside the bin
+        lo = v;
+        hi = min(hi, v + ((1u << sh) - 1u));
+    }
+    return v > tau ? v : tau;
+}
+
+// Drops the pool entries below tau, keeping the order; the parents [ps, pe) of the level being built carry
+// their rank state along when `parents`.
+__device__ void ds_compact(DsLds& s, int& N, uint32_t tau, int& ps, int& pe, bool parents) {
+    const int t = threadIdx.x, e0 = 4 * t;
+    uint32_t k4[4], m4[4], rc4[4];
+    bool keep[4];
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u;
+        k4[u] = e < N ? s.key[e] : 0u;
+        keep[u] = e < N && k4[u] >= tau;
+        m4[u] = keep[u] ? s.meta[e] : 0u;
+        rc4[u] = (parents && keep[u] && e >= ps && e < pe) ? s.u.lv.rc[e - ps] : 0u;
+        cnt += keep[u] ? 1u : 0u;
+    }
+    uint32_t nn;
+    uint32_t o = ds_scan(cnt, s.red, nn);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (e0 + u < N) s.idx[e0 + u] = (uint16_t)o;
+        o += keep[u] ? 1u : 0u;
+    }
+    __syncthreads();
+    const int nps = ps < N ? (int)s.idx[ps] : (int)nn, npe = pe < N ? (int)s.idx[pe] : (int)nn;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (!keep[u]) continue;
+        const int e = e0 + u, dst = s.idx[e], p = ds_par(m4[u]);
+        s.key[dst] = k4[u];
+        s.meta[dst] = p < 0 ? m4[u] : ds_meta(s.idx[p], ds_dep(m4[u]), ds_rank(m4[u]));
+        if (parents && e >= ps && e < pe) s.u.lv.rc[dst - nps] = rc4[u];
+    }
+    __syncthreads();
+    N = (int)nn;
+    ps = nps;
+    pe = npe;
+}
+
+// Whether the pool entry x was created before the pool entry y, both of equal score: a tuple is created
+// when its generator pops (the previous sibling, or the parent for a first child), so the order is that of
+// the generators -- by score, then recursively -- and one generator's sibling comes before its child.  The
+// first depth-1 tuple is created before everything.
+__device__ bool ds_before(const DsLds& s, int K, int xi, int yi, int* flag) {
+    const uint32_t mx = s.meta[xi], my = s.meta[yi];
+    int xp = ds_par(mx), xd = ds_dep(mx), xr = ds_rank(mx);
+    int yp = ds_par(my), yd = ds_dep(my), yr = ds_rank(my);
+    for (int step = 0; step < DS_WALK_MAX; ++step) {
+        if (xd == 1 && xr == 0) return true;
+        if (yd == 1 && yr == 0) return false;
+        int gxp, gxd = xd, gxr, gyp, gyd = yd, gyr;
+        const int tx = xr > 0 ? 0 : 1, ty = yr > 0 ? 0 : 1;  // 0: sibling, 1: first child
+        if (tx == 0) {
+            gxp = xp;
+            gxr = xr - 1;
+        } else {
+            const uint32_t m = s.meta[xp];
+            gxp = ds_par(m);
+            gxd = xd - 1;
+            gxr = ds_rank(m);
+        }
+        if (ty == 0) {
+            gyp = yp;
+            gyr = yr - 1;
+        } else {
+            const uint32_t m = s.meta[yp];
+            gyp = ds_par(m);
+            gyd = yd - 1;
+            gyr = ds_rank(m);
+        }
+        if (gxp == gyp && gxd == gyd && gxr == gyr) return tx < ty;
+        const uint32_t sx = ds_score(s, K, gxp, gxd, gxr), sy = ds_score(s, K, gyp, gyd, gyr);
+        if (sx != sy) return sx > sy;
+        xp = gxp, xd = gxd, xr = gxr;
+        yp = gyp, yd = gyd, yr = gyr;
+    }
+    *flag = 1;
+    return false;
+}
+
+__global__ __launch_bounds__(DS_THREADS) void ddtree_select(int D, int K, const float* __restrict__ lp,
+                                                             const int32_t* __restrict__ ids, int64_t req_stride,
+                                                             int budget, int32_t* __restrict__ node_token,
+                                                             int32_t* __restrict__ node_parent,
+                                                             int32_t* __restrict__ node_depth,
+                                                             float* __restrict__ node_logq,
+                                                             int32_t* __restrict__ n_nodes) {
+    __shared__ DsLds s;
+    const int r = blockIdx.x, t = threadIdx.x;
+    const float* l = lp + (size_t)r * req_stride;
+    const int DK = D * K;
+    for (int i0 = 0; i0 < DK; i0 += DS_THREADS * 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int i = i0 + u * DS_THREADS + t;
+            v[u] = i < DK ? l[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int i = i0 + u * DS_THREADS + t;
+            if (i < DK) s.lq[i] = v[u];
+        }
+    }
+    if (t == 0) s.flag = 0;
+    __syncthreads();
+    // the method's input: every row sorted, non-increasing log-probabilities (no NaN, nothing above 0)
+    for (int i = t; i < DK; i += DS_THREADS) {
+        const float x = s.lq[i];
+        if (!(x <= 0.f) || ((i % K) + 1 < K && !(s.lq[i + 1] <= x))) s.flag = 1;
+    }
+    __syncthreads();
+    bool fail = s.flag != 0;
+    int N = 0, ps = 0, pe = 0, raises = 0;
+    uint32_t tau = 0u;  // no threshold yet: every key is >= 0
+    for (int d = 0; d < D && !fail; ++d) {
+        // build depth d + 1 from the pool entries [ps, pe) of depth d (the root when d = 0)
+        const int lim = min(K, budget - d);  // a rank-r child has r elder siblings and d ancestors before it
+        if (lim <= 0) break;
+        if (d > 0 && N > budget + DS_CAP / 8) {
+            tau = ds_raise(s, N, budget, tau);
+            ds_compact(s, N, tau, ps, pe, false);
+        }
+        int P = d == 0 ? 1 : pe - ps;
+        if (P == 0) break;
+        for (int i = t; i < P; i += DS_THREADS) {
+            const float sp = d == 0 ? 0.f : key_value(s.key[ps + i]);
+            s.u.lv.rc[i] = (uint32_t)ds_count(s, K, sp, d, 0, lim, tau);
+        }
+        __syncthreads();
+        while (true) {
+            uint32_t n4[4], loc = 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = 4 * t + u;
+                const uint32_t rc = i < P ? s.u.lv.rc[i] : 0u;
+                n4[u] = (rc & 0xFFFFu) - (rc >> 16);
+                loc += n4[u];
+            }
+            uint32_t T;
+            uint32_t o = ds_scan(loc, s.red, T);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (4 * t + u < P) s.u.lv.off[4 * t + u] = o;
+                o += n4[u];
+            }
+            const int room = DS_CAP - N;
+            const int E = min((int)T, room);
+            __syncthreads();
+            for (int j = t; j < E; j += DS_THREADS) {
+                int lo = 0, hi = P;  // the last parent whose offset is <= j
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if ((int)s.u.lv.off[mid] <= j)
+                        lo = mid + 1;
+                    else
+                        hi = mid;
+                }
+                const int i = lo - 1;
+                const int rank = (int)(s.u.lv.rc[i] >> 16) + (j - (int)s.u.lv.off[i]);
+                const int p = d == 0 ? -1 : ps + i;
+                s.key[N + j] = ds_score(s, K, p, d + 1, rank);
+                s.meta[N + j] = ds_meta(p, d + 1, rank);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = 4 * t + u;
+                if (i < P && n4[u] > 0u) {
+                    const uint32_t rc = s.u.lv.rc[i];
+                    const int took = min((int)n4[u], max(0, E - (int)s.u.lv.off[i]));
+                    s.u.lv.rc[i] = rc + ((uint32_t)took << 16);
+                }
+            }
+            N += E;
+            __syncthreads();
+            if ((int)T <= room) break;
+            // the pool is full: raise the threshold, drop what falls below, recount what is left to append
+            if (++raises > DS_MAX_RAISES) {
+                fail = true;
+                break;
+            }
+            tau = ds_raise(s, N, budget, tau);
+            ds_compact(s, N, tau, ps, pe, d > 0);
+            if (DS_CAP - N < DS_CAP / 16) {
+                fail = true;
+                break;
+            }
+            P = d == 0 ? 1 : pe - ps;
+            for (int i = t; i < P; i += DS_THREADS) {
+                const uint32_t rc = s.u.lv.rc[i];
+                const float sp = d == 0 ? 0.f : key_value(s.key[ps + i]);
+                const int c = ds_count(s, K, sp, d, (int)(rc >> 16), (int)(rc & 0xFFFFu), tau);
+                s.u.lv.rc[i] = (rc & 0xFFFF0000u) | (uint32_t)c;
+            }
+            __syncthreads();
+        }
+        ps = pe;
+        pe = N;
+    }
+    if (!fail && N > budget) {
+        tau = ds_raise(s, N, budget, tau);
+        ds_compact(s, N, tau, ps, pe, false);
+    }
+    const int nout = min(N, budget);
+    if (!fail) {
+        // sort by score, best first; the low half only makes the keys distinct
+        int S = 64;
+        while (S < N) S <<= 1;
+        for (int i = t; i < S; i += DS_THREADS)
+            s.u.sk[i] = i < N ? (((uint64_t)s.key[i] << 32) | (uint64_t)(0xFFFFu - (uint32_t)i)) : 0ull;
+        __syncthreads();
+        for (int k = 2; k <= S; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int i = t; i < S / 2; i += DS_THREADS) {
+                    const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1)), b = a + j;
+                    const uint64_t ka = s.u.sk[a], kb = s.u.sk[b];
+                    if (((a & k) == 0) ? ka < kb : ka > kb) {
+                        s.u.sk[a] = kb;
+                        s.u.sk[b] = ka;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // runs of equal scores that reach into the first `budget` positions: creation order
+        for (int j = t; j < nout; j += DS_THREADS) {
+            const uint32_t h = (uint32_t)(s.u.sk[j] >> 32);
+            if (j + 1 >= N || (uint32_t)(s.u.sk[j + 1] >> 32) != h) continue;
+            if (j > 0 && (uint32_t)(s.u.sk[j - 1] >> 32) == h) continue;
+            int e = j + 1;
+            while (e < N && e - j <= DS_RUN_MAX && (uint32_t)(s.u.sk[e] >> 32) == h) ++e;
+            if (e - j > DS_RUN_MAX) {
+                s.flag = 1;
+                continue;
+            }
+            for (int a = j + 1; a < e; ++a) {
+                const uint64_t x = s.u.sk[a];
+                int b = a;
+                while (b > j && ds_before(s, K, ds_slot(x), ds_slot(s.u.sk[b - 1]), &s.flag)) {
+                    s.u.sk[b] = s.u.sk[b - 1];
+                    --b;
+                }
+                s.u.sk[b] = x;
+            }
+        }
+        for (int i = t; i < N; i += DS_THREADS) s.idx[i] = 0xFFFFu;
+        __syncthreads();
+        for (int j = t; j < nout; j += DS_THREADS) s.idx[ds_slot(s.u.sk[j])] = (uint16_t)j;
+        __syncthreads();
+        int32_t* out_tok = node_token + (size_t)r * budget;
+        int32_t* out_par = node_parent + (size_t)r * budget;
+        int32_t* out_dep = node_depth + (size_t)r * budget;
+        float* out_lq = node_logq + (size_t)r * budget;
+        const int32_t* idr = ids + (size_t)r * req_stride;
+        for (int j = t; j < nout; j += DS_THREADS) {
+            const uint64_t k = s.u.sk[j];
+            const uint32_t m = s.meta[ds_slot(k)];
+            const int p = ds_par(m), dd = ds_dep(m), rk = ds_rank(m);
+            int pj = -1;
+            if (p >= 0) {
+                pj = (int)s.idx[p];
+                if (pj >= j) s.flag = 1;  // never: a parent scores and is created before its children
+            }
+            out_tok[j] = idr[(size_t)(dd - 1) * K + rk];
+            out_par[j] = pj;
+            out_dep[j] = dd;
+            out_lq[j] = key_value((uint32_t)(k >> 32));
+        }
+        __syncthreads();
+        fail = s.flag != 0;
+    }
+    if (t == 0) n_nodes[r] = fail ? -1 : nout;
+}
+
+// Below this budget the heap's few pops take less time than the selection's fixed cost of one
+// synchronised round per depth (measured: 12.8 vs 22.5 us at 16 nodes, 42.5 vs 20.6 us at 64).
+#define DS_MIN_BUDGET 28
+
 hipError_t launch_ddtree_build(int batch, int D, int K, const float* lp, const int32_t* ids, int64_t req_stride,
                                int budget, int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
-                               float* node_logq, int32_t* n_nodes, hipStream_t st) {
+                               float* node_logq, int32_t* n_nodes, bool select_only, hipStream_t st) {
+    if (!select_only && budget < DS_MIN_BUDGET) {
+        hipLaunchKernelGGL(ddtree_build, dim3(batch), dim3(64), 0, st, D, K, lp, ids, req_stride, budget, node_token,
+                           node_parent, node_depth, node_logq, n_nodes, 0);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(ddtree_select, dim3(batch), dim3(DS_THREADS), 0, st, D, K, lp, ids, req_stride, budget,
+                       node_token, node_parent, node_depth, node_logq, n_nodes);
+    if (select_only) return hipGetLastError();
     hipLaunchKernelGGL(ddtree_build, dim3(batch), dim3(64), 0, st, D, K, lp, ids, req_stride, budget, node_token,
-                       node_parent, node_depth, node_logq, n_nodes);
+                       node_parent, node_depth, node_logq, n_nodes, 1);
     return hipGetLastError();
 }
 

@@ -835,9 +835,10 @@ extern "C" int dflash_topk_logprobs(int rows, int vocab, int k, const float* log
     return DFLASH_OK;
 }
 
-extern "C" int dflash_ddtree_build(int batch, int depth, int k, const float* logprobs, const int32_t* ids,
-                                   int64_t req_stride, int budget, int32_t* node_token, int32_t* node_parent,
-                                   int32_t* node_depth, float* node_logq, int32_t* n_nodes, void* stream) {
+static int ddtree_build_impl(int batch, int depth, int k, const float* logprobs, const int32_t* ids,
+                             int64_t req_stride, int budget, int32_t* node_token, int32_t* node_parent,
+                             int32_t* node_depth, float* node_logq, int32_t* n_nodes, bool select_only,
+                             void* stream) {
     if (batch < 1) return fail(DFLASH_E_ARG, "batch must be >= 1");
     if (!logprobs || !ids || !node_token || !node_parent || !node_depth || !node_logq || !n_nodes)
         return fail(DFLASH_E_ARG, "a required pointer is NULL");
@@ -847,8 +848,22 @@ extern "C" int dflash_ddtree_build(int batch, int depth, int k, const float* log
                     DDT_MAX_BUDGET);
     if (req_stride < (int64_t)depth * k) return fail(DFLASH_E_ARG, "req_stride < depth * k");
     HIP_TRY(launch_ddtree_build(batch, depth, k, logprobs, ids, req_stride, budget, node_token, node_parent,
-                                node_depth, node_logq, n_nodes, (hipStream_t)stream));
+                                node_depth, node_logq, n_nodes, select_only, (hipStream_t)stream));
     return DFLASH_OK;
+}
+
+extern "C" int dflash_ddtree_build(int batch, int depth, int k, const float* logprobs, const int32_t* ids,
+                                   int64_t req_stride, int budget, int32_t* node_token, int32_t* node_parent,
+                                   int32_t* node_depth, float* node_logq, int32_t* n_nodes, void* stream) {
+    return ddtree_build_impl(batch, depth, k, logprobs, ids, req_stride, budget, node_token, node_parent,
+                             node_depth, node_logq, n_nodes, false, stream);
+}
+
+extern "C" int dflash_ddtree_select(int batch, int depth, int k, const float* logprobs, const int32_t* ids,
+                                    int64_t req_stride, int budget, int32_t* node_token, int32_t* node_parent,
+                                    int32_t* node_depth, float* node_logq, int32_t* n_nodes, void* stream) {
+    return ddtree_build_impl(batch, depth, k, logprobs, ids, req_stride, budget, node_token, node_parent,
+                             node_depth, node_logq, n_nodes, true, stream);
 }
 
 extern "C" int dflash_ddtree_walk(int batch, int budget, int max_accept, const int32_t* node_token,

@@ -122,7 +122,7 @@ hipError_t launch_topk_rows(int rows, const float* logits, int64_t stride, int V
 // Algorithm 1 per request: depth d (0-based) of request r reads lp / ids at r * req_stride + d * K.
 hipError_t launch_ddtree_build(int batch, int D, int K, const float* lp, const int32_t* ids, int64_t req_stride,
                                int budget, int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
-                               float* node_logq, int32_t* n_nodes, hipStream_t st);
+                               float* node_logq, int32_t* n_nodes, bool select_only, hipStream_t st);
 hipError_t launch_ddtree_walk(int batch, int budget, int max_accept, const int32_t* node_token,
                               const int32_t* node_parent, const int32_t* n_nodes, const int32_t* target_next,
                               int32_t* accept_len, int32_t* accept_nodes, int32_t* bonus, hipStream_t st);

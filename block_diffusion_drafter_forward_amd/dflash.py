@@ -99,6 +99,9 @@ _SIGS = {
     "dflash_ddtree_build": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "dflash_ddtree_select": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "dflash_ddtree_walk": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p]),
@@ -168,6 +171,12 @@ def dflash_ddtree_build(batch, depth, k, logprobs, ids, req_stride, budget, node
                         node_logq, n_nodes, stream) -> int:
     return lib().dflash_ddtree_build(batch, depth, k, logprobs, ids, req_stride, budget, node_token, node_parent,
                                      node_depth, node_logq, n_nodes, stream)
+
+
+def dflash_ddtree_select(batch, depth, k, logprobs, ids, req_stride, budget, node_token, node_parent, node_depth,
+                         node_logq, n_nodes, stream) -> int:
+    return lib().dflash_ddtree_select(batch, depth, k, logprobs, ids, req_stride, budget, node_token, node_parent,
+                                      node_depth, node_logq, n_nodes, stream)
 
 
 def dflash_ddtree_walk(batch, budget, max_accept, node_token, node_parent, n_nodes, target_next, accept_len,

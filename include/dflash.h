@@ -262,16 +262,27 @@ int dflash_verify_sample(int batch, int n_draft, int vocab, const int32_t *draft
 int dflash_topk_logprobs(int rows, int vocab, int k, const float *logits, int64_t row_stride, int32_t *ids,
                          float *logprobs, void *stream);
 
-/* Algorithm 1 per request: the `budget` most probable prefixes under the factorised distribution, popped
- * best-first from a heap of rank tuples (next sibling and first child pushed per pop; equal scores pop in
- * creation order).  Input: depth d (0-based, d < depth) of request r has its k sorted log-probs and ids at
- * logprobs / ids + r * req_stride + d * k (device).  Output, device [batch][budget], node i = the i-th pop:
- * node_token (token id), node_parent (node index of its prefix, -1 = the root / bonus token), node_depth
- * (1-based), node_logq (log-probability score, float32 sums: parent's score + own log-prob); n_nodes[b] =
- * nodes written (min(budget, prefixes available)).  depth <= 16, k <= 1024, budget <= 2047.              */
+/* Algorithm 1 per request: the `budget` most probable prefixes under the factorised distribution, in the
+ * order a best-first heap of rank tuples pops them (next sibling and first child pushed per pop; equal
+ * scores pop in creation order).  Input: depth d (0-based, d < depth) of request r has its k sorted
+ * log-probs and ids at logprobs / ids + r * req_stride + d * k (device).  Output, device [batch][budget],
+ * node i = the i-th pop: node_token (token id), node_parent (node index of its prefix, -1 = the root / bonus
+ * token), node_depth (1-based), node_logq (log-probability score, float32 sums: parent's score + own
+ * log-prob); n_nodes[b] = nodes written (min(budget, prefixes available)).  depth <= 16, k <= 1024,
+ * budget <= 2047.  The tree is found by a parallel selection of the top-`budget` prefixes (Proposition 2 of
+ * §3.4.3) followed by a sort into pop order; a request the selection cannot decide (rows that are not
+ * non-increasing log-probabilities <= 0, long runs of exactly equal scores) is built by the heap itself.
+ * Both give the heap's result.  No workspace.                                                              */
 int dflash_ddtree_build(int batch, int depth, int k, const float *logprobs, const int32_t *ids, int64_t req_stride,
                         int budget, int32_t *node_token, int32_t *node_parent, int32_t *node_depth,
                         float *node_logq, int32_t *n_nodes, void *stream);
+
+/* The parallel selection of dflash_ddtree_build alone, for callers that want to see which requests it
+ * decides: same arguments and outputs, except that n_nodes[b] = -1 marks a request it left undecided (its
+ * other outputs are then unspecified).                                                                    */
+int dflash_ddtree_select(int batch, int depth, int k, const float *logprobs, const int32_t *ids, int64_t req_stride,
+                         int budget, int32_t *node_token, int32_t *node_parent, int32_t *node_depth,
+                         float *node_logq, int32_t *n_nodes, void *stream);
 
 /* Greedy verifier walk per request over a tree from dflash_ddtree_build: target_next[b][0] is the target's
  * choice after the root and target_next[b][i + 1] its choice after node i (device [batch][budget + 1]).

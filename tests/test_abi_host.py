@@ -247,12 +247,13 @@ def test_topk_logprobs_validation(D, args, code):
     (dict(batch=0), -1), (dict(depth=0), -1), (dict(depth=17), -4), (dict(k=1025), -4),
     (dict(budget=2048), -4), (dict(budget=0), -1), (dict(req_stride=7), -1), (dict(n_nodes=None), -1),
 ])
-def test_ddtree_build_validation(D, args, code):
+@pytest.mark.parametrize("entry", ["dflash_ddtree_build", "dflash_ddtree_select"])
+def test_ddtree_build_validation(D, args, code, entry):
     a = dict(batch=1, depth=15, k=64, lp=0x1000, ids=0x2000, req_stride=15 * 64, budget=256, tok=0x3000,
              par=0x4000, dep=0x5000, lq=0x6000, n_nodes=0x7000)
     a.update(args)
-    assert D.dflash_ddtree_build(a["batch"], a["depth"], a["k"], a["lp"], a["ids"], a["req_stride"], a["budget"],
-                                 a["tok"], a["par"], a["dep"], a["lq"], a["n_nodes"], None) == code
+    assert getattr(D, entry)(a["batch"], a["depth"], a["k"], a["lp"], a["ids"], a["req_stride"], a["budget"],
+                             a["tok"], a["par"], a["dep"], a["lq"], a["n_nodes"], None) == code
     assert D.dflash_last_error()
 
 

@@ -135,6 +135,99 @@ def test_ddtree_build_matches_oracle(depth, K, budget):
         assert np.all(par[b, :n[b]] < np.arange(n[b]))
 
 
+def _tie_logprobs(rng, kind, batch, depth, K):
+    """Sorted per-depth log-probabilities with exact float32 score ties: rounded to 2^-10 (short runs of equal
+    scores), to 2^-3 (long runs), all equal, or one dominant token per depth."""
+    if kind == "peaked":
+        lg = rng.normal(0.0, 1.0, size=(batch * depth, 3000))
+        lg[:, 0] += 9.0
+        ids, lp = T.topk_logprobs(lg, K)
+        return ids.reshape(batch, depth, K).astype(np.int32), lp.reshape(batch, depth, K).astype(np.float32)
+    ids, lp = _sorted_logprobs(rng, batch, depth, K)
+    if kind == "q10":
+        lp = (np.round(lp.astype(np.float64) * 1024) / 1024).astype(np.float32)
+    elif kind == "q3":
+        lp = (np.round(lp.astype(np.float64) * 8) / 8).astype(np.float32)
+    elif kind == "const":
+        lp = np.full_like(lp, -np.log(K))
+    return ids, lp
+
+
+def _check_f32(tok, par, dep, lq, n, ids, lp, budget):
+    nodes = T.build_tree(lp, budget, dtype=np.float32, score="path_sum")
+    assert n == len(nodes)
+    np.testing.assert_array_equal(tok[:n], T.tree_tokens(nodes, ids))
+    np.testing.assert_array_equal(par[:n], [p for _, _, p in nodes])
+    np.testing.assert_array_equal(dep[:n], [len(r) for r, _, _ in nodes])
+    np.testing.assert_array_equal(lq[:n].view(np.uint32), np.array([s for _, s, _ in nodes], np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["q10", "q3", "const", "peaked"])
+@pytest.mark.parametrize("depth,K,budget", [(15, 1024, 1024), (6, 512, 2047), (16, 8, 512), (3, 3, 100)])
+def test_ddtree_build_with_score_ties(kind, depth, K, budget):
+    """Exact float32 score ties: equal scores pop in creation order ([DDT] §3.4.4), whichever way the tree is
+    built (the parallel selection orders short runs itself and hands long ones to the heap)."""
+    torch, D, S = _mods()
+    rng = np.random.default_rng(900 + depth + K + budget + len(kind))
+    ids, lp = _tie_logprobs(rng, kind, 2, depth, K)
+    tok, par, dep, lq, n = _build_gpu(torch, D, ids, lp, budget)
+    for b in range(2):
+        _check_f32(tok[b], par[b], dep[b], lq[b], int(n[b]), ids[b], lp[b], budget)
+
+
+def _select_gpu(torch, D, ids, lp, budget):
+    batch, depth, K = lp.shape
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    lpd, idd = dev(lp), dev(ids)
+    tok = torch.empty((batch, budget), dtype=torch.int32, device="cuda")
+    par, dep = torch.empty_like(tok), torch.empty_like(tok)
+    lq = torch.empty((batch, budget), dtype=torch.float32, device="cuda")
+    n = torch.empty(batch, dtype=torch.int32, device="cuda")
+    D.check(D.dflash_ddtree_select(batch, depth, K, lpd.data_ptr(), idd.data_ptr(), depth * K, budget,
+                                   tok.data_ptr(), par.data_ptr(), dep.data_ptr(), lq.data_ptr(), n.data_ptr(),
+                                   D._stream()), "select")
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), par.cpu().numpy(), dep.cpu().numpy(), lq.cpu().numpy(), n.cpu().numpy()
+
+
+@pytest.mark.parametrize("kind", ["normal", "q10", "peaked", "q3", "const"])
+@pytest.mark.parametrize("depth,K,budget", [(15, 1024, 1024), (15, 64, 16), (6, 512, 2047), (16, 8, 512),
+                                            (1, 50, 64), (2, 1, 5), (15, 32, 2047)])
+def test_ddtree_select_decides_and_matches(kind, depth, K, budget):
+    """The parallel selection alone: it must decide every request with continuous scores or short runs of
+    equal scores, and whatever it decides is Algorithm 1's pop order, score bit for score bit."""
+    torch, D, S = _mods()
+    rng = np.random.default_rng(1000 + depth * 3 + K + budget + len(kind))
+    if kind == "normal":
+        ids, lp = _sorted_logprobs(rng, 3, depth, K)
+    else:
+        ids, lp = _tie_logprobs(rng, kind, 3, depth, K)
+    tok, par, dep, lq, n = _select_gpu(torch, D, ids, lp, budget)
+    for b in range(3):
+        if kind in ("normal", "q10", "peaked"):
+            assert n[b] != -1
+        if n[b] != -1:
+            _check_f32(tok[b], par[b], dep[b], lq[b], int(n[b]), ids[b], lp[b], budget)
+
+
+def test_ddtree_select_declines_unsorted_rows():
+    """Rows that are not non-increasing log-probabilities are left to the heap (n_nodes = -1), and the full
+    build still returns the heap's pops."""
+    torch, D, S = _mods()
+    rng = np.random.default_rng(77)
+    ids, lp = _sorted_logprobs(rng, 2, 5, 64)
+    lp[0, 2, 10], lp[0, 2, 11] = lp[0, 2, 11], lp[0, 2, 10] - 0.5   # request 0: one row out of order
+    lp[1, 0, 0] = 0.25                                              # request 1: a log-probability above 0
+    tok, par, dep, lq, n = _select_gpu(torch, D, ids, lp, 200)
+    assert list(n) == [-1, -1]
+    tok, par, dep, lq, n = _build_gpu(torch, D, ids, lp, 200)
+    for b in range(2):
+        nodes = T.build_tree(lp[b], 200, dtype=np.float32, score="path_sum")
+        assert n[b] == len(nodes)
+        np.testing.assert_array_equal(par[b, :n[b]], [p for _, _, p in nodes])
+        np.testing.assert_array_equal(tok[b, :n[b]], T.tree_tokens(nodes, ids[b]))
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_ddtree_walk_matches_oracle(seed):
     torch, D, S = _mods()
