@@ -462,8 +462,12 @@ def ddtree_bench(args):
         anodes = torch.empty((B, L - 1), dtype=torch.int32, device="cuda")
         bonus = torch.empty(B, dtype=torch.int32, device="cuda")
 
+        nws = D.dflash_topk_logprobs_workspace_bytes(B * L, V, K)
+        tk_ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+
         def topk():
-            D.check(D.dflash_topk_logprobs(B * L, V, K, logits.data_ptr(), V, ids.data_ptr(), lp.data_ptr(), st), "topk")
+            D.check(D.dflash_topk_logprobs(B * L, V, K, logits.data_ptr(), V, ids.data_ptr(), lp.data_ptr(),
+                                           tk_ws.data_ptr(), nws, st), "topk")
 
         def build():
             D.check(D.dflash_ddtree_build(B, L - 1, K, lp.data_ptr() + 4 * K, ids.data_ptr() + 4 * K, L * K, budget,

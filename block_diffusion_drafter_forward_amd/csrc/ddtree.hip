@@ -10,7 +10,7 @@ namespace df {
 // wide top-K of one logits row: radix select of the K-th largest key, gather, bitonic sort
 // ------------------------------------------------------------------------------------------------------
 // One workgroup of 1024 threads per row.  Floats map to unsigned keys that order like the floats
-// (negative: all bits flipped; non-negative: sign bit set).  Three radix passes (11, 11 and 10 bits, the
+// (negative: all bits flipped; non-negative: sign bit set; -0 taken as +0).  Three radix passes (11, 11 and 10 bits, the
 // first one over the row also accumulating an online max / sum of exponentials) find the key T of the K-th
 // largest value and how many entries equal to T belong to the top K; a gather takes every key above T and
 // the entries equal to T (all of them in the common case where they all fit, else the ones with the
@@ -25,7 +25,8 @@ namespace df {
 #define TK_UNROLL 8
 
 __device__ __forceinline__ uint32_t order_key(float f) {
-    const uint32_t u = __float_as_uint(f);
+    uint32_t u = __float_as_uint(f);
+    u = u == 0x80000000u ? 0u : u;  // -0 and +0 are one value: equal logits tie by id
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 __device__ __forceinline__ float key_value(uint32_t k) {
@@ -73,35 +74,34 @@ __device__ __forceinline__ float tk_block_max(float v, float* red) {
 }
 
 // Radix step over the histogram: the bin (from the top) that holds the krem-th largest, and the rank left
-// inside it.  Wave 0 scans TK_BINS bins from the top, 32 per lane, with a wave prefix sum.
+// inside it.  Every thread takes two adjacent bins from the top (nbins <= 2 * TK_THREADS), so neighbouring
+// lanes read neighbouring words; a block-wide prefix sum over the pairs finds the bin.  All threads call it.
 __device__ __forceinline__ void tk_pick_bin(const uint32_t* hist, int nbins, int krem, int* s_bin, int* s_krem) {
-    const int t = threadIdx.x;
-    if (t < 64) {
-        const int per = nbins / 64;
-        // lane 0 takes the top bins: lane l covers bins [nbins - (l + 1) per, nbins - l per)
-        int cnt = 0;
-        for (int q = 0; q < per; ++q) cnt += (int)hist[nbins - 1 - (t * per + q)];
-        int incl = cnt;
+    __shared__ int wsum[TK_THREADS / 64];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int b0 = nbins - 1 - 2 * t;
+    const int h0 = b0 >= 0 ? (int)hist[b0] : 0, h1 = b0 >= 1 ? (int)hist[b0 - 1] : 0;
+    const int pair = h0 + h1;
+    int incl = pair;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o, 64);
-            if (t >= o) incl += y;
-        }
-        const int excl = incl - cnt;
-        if (excl < krem && incl >= krem) {
-            int cum = excl;
-            for (int q = 0; q < per; ++q) {
-                const int b = nbins - 1 - (t * per + q);
-                const int c = (int)hist[b];
-                if (cum + c >= krem) {
-                    *s_bin = b;
-                    *s_krem = krem - cum;
-                    break;
-                }
-                cum += c;
-            }
-        }
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
     }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < TK_THREADS / 64; ++i) base += i < w ? wsum[i] : 0;
+    const int excl = base + incl - pair;
+    if (excl < krem && excl + h0 >= krem) {
+        *s_bin = b0;
+        *s_krem = krem - excl;
+    } else if (excl + h0 < krem && excl + pair >= krem) {
+        *s_bin = b0 - 1;
+        *s_krem = krem - excl - h0;
+    }
+    __syncthreads();  // wsum is free again
 }
 
 // The selection after the first radix pass: radix passes 2 and 3 (11 and 10 bits) among the keys with
@@ -175,18 +175,180 @@ __device__ void tk_select(Each&& each, uint32_t prefix, uint32_t mask, int krem,
 
 #define TK_CAND 6144  // candidates kept in LDS after the first radix pass
 
-__global__ __launch_bounds__(TK_THREADS) void topk_rows(const float* __restrict__ logits, int64_t stride, int V,
-                                                         int K, int32_t* __restrict__ ids, float* __restrict__ lp) {
+// Sort entries are packed as key << 32 | ~id: a larger packed value is a larger key, then a smaller id.
+__device__ __forceinline__ uint64_t tk_pack(uint32_t key, int id) {
+    return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)id);
+}
+__device__ __forceinline__ uint32_t tk_pkey(uint64_t p) { return (uint32_t)(p >> 32); }
+__device__ __forceinline__ int tk_pid(uint64_t p) { return (int)~(uint32_t)p; }
+// The value of lane (lane ^ lx), lx in {1, 2, 4, 8, 16, 32}, with VALU lane moves only: DPP quad
+// permutations (1, 2), row shifts (4), a row rotation (8), and the row-swap permutes (16, 32).
+__device__ __forceinline__ uint32_t tk_xor_lane(uint32_t v, int lx) {
+    const int x = (int)v;
+    const int lane = threadIdx.x & 63;
+    switch (lx) {
+        case 1:
+            return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+        case 2:
+            return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+        case 4: {
+            const int up = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0xF, false);  // row_shl:4, lane + 4
+            const int dn = __builtin_amdgcn_update_dpp(x, x, 0x114, 0xF, 0xF, false);  // row_shr:4, lane - 4
+            return (uint32_t)((lane & 4) ? dn : up);
+        }
+        case 8:
+            return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false);  // row_ror:8
+        case 16: {
+            const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+            return (lane & 16) ? p[0] : p[1];
+        }
+        default: {
+            const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+            return (lane & 32) ? p[0] : p[1];
+        }
+    }
+}
+__device__ __forceinline__ uint64_t tk_shfl_xor64(uint64_t v, int lx) {
+    const uint32_t lo = tk_xor_lane((uint32_t)v, lx);
+    const uint32_t hi = tk_xor_lane((uint32_t)(v >> 32), lx);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One bitonic stage between a lane's own elements s and s ^ J (J < E), in runs of size kk.
+template <int E, int J>
+__device__ __forceinline__ void tk_lane_stage(uint64_t (&v)[E], int base, int kk) {
+#pragma unroll
+    for (int s = 0; s < E; ++s) {
+        if ((s & J) == 0 && (s ^ J) < E) {
+            const int q = s ^ J;
+            const bool desc = ((base + s) & kk) == 0;  // this run is sorted largest first
+            const uint64_t a = v[s], b = v[q];
+            const bool sw = desc ? b > a : a > b;
+            v[s] = sw ? b : a;
+            v[q] = sw ? a : b;
+        }
+    }
+}
+
+// Bitonic sort, largest first, of the 64E packed entries a wave holds (lane l: run positions E l + s), in
+// registers: swaps inside a lane, shuffles across lanes.  No barrier.
+template <int E>
+__device__ __forceinline__ void tk_wave_sort(uint64_t (&v)[E]) {
+    const int lane = threadIdx.x & 63, base = E * lane;
+#pragma unroll
+    for (int kk = 2; kk <= 64 * E; kk <<= 1) {
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            if (j < E) {
+                if (j == 1)
+                    tk_lane_stage<E, 1>(v, base, kk);
+                else
+                    tk_lane_stage<E, 2>(v, base, kk);
+            } else {
+                const int lx = j / E;
+                const bool lower = (lane & lx) == 0;
+#pragma unroll
+                for (int s = 0; s < E; ++s) {
+                    const uint64_t o = tk_shfl_xor64(v[s], lx);
+                    const bool desc = ((base + s) & kk) == 0;
+                    const bool take_max = lower == desc;
+                    v[s] = take_max ? (o > v[s] ? o : v[s]) : (o < v[s] ? o : v[s]);
+                }
+            }
+        }
+    }
+}
+
+// Number of entries of the descending run a[0, len) larger than x, len <= RUN (a power of two): a
+// fixed-length binary search, so that several of them interleave.
+template <int RUN>
+__device__ __forceinline__ int tk_count_larger(const uint64_t* a, int len, uint64_t x) {
+    int pos = 0;
+#pragma unroll
+    for (int step = RUN; step > 0; step >>= 1)
+        if (pos + step <= len && a[pos + step - 1] > x) pos += step;
+    return pos;
+}
+
+// One four-way merge round over the first n entries: runs of RUN entries in groups of four, the last run
+// holding fewer than RUN real entries being cut at n.  An entry's place in its merged group is its index
+// in its own run plus the number of larger entries in each of the three other runs (three independent
+// searches); entries are distinct, so the places are a permutation of [0, n).
+template <int E, int RUN>
+__device__ __forceinline__ void tk_merge4(const uint64_t* src, uint64_t* dst, int n) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int s = 0; s < E; ++s) {
+        const int i = t + TK_THREADS * s;
+        if (i < n) {
+            const uint64_t x = src[i];
+            const int g0 = i & ~(4 * RUN - 1), a = (i - g0) / RUN;
+            int pos = g0 + (i & (RUN - 1));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int len = min(RUN, n - (g0 + b * RUN));
+                if (b != a && len > 0) pos += tk_count_larger<RUN>(src + g0 + b * RUN, len, x);
+            }
+            dst[pos] = x;
+        }
+    }
+}
+
+// Sorts the packed entries [0, n) of buf, largest first, n <= 1024 E; buf holds 2048 E entries (the second
+// half is the merge target).  Each wave sorts a run of 64E in registers (a run past n is skipped, one cut
+// by n is padded with entries smaller than every real one); two four-way merge rounds over the real
+// entries then join the runs, one barrier each.  All threads call it; the result is in buf[0, n).
+template <int E>
+__device__ __forceinline__ void tk_sort_lds(int n, uint64_t* buf) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    constexpr int R = 64 * E, P = TK_THREADS * E;
+    const bool live = w * R < n;
+    uint64_t v[E];
+    if (live) {
+#pragma unroll
+        for (int s = 0; s < E; ++s) {
+            const int i = w * R + E * lane + s;
+            v[s] = i < n ? buf[i] : tk_pack(0u, 0x7FFFFFFF - (i - n));
+        }
+        tk_wave_sort<E>(v);
+    }
+    __syncthreads();  // every entry read before the runs are written back
+    if (live) {
+#pragma unroll
+        for (int s = 0; s < E; ++s) {
+            const int i = w * R + E * lane + s;
+            if (i < n) buf[i] = v[s];  // the padding sorts last
+        }
+    }
+    __syncthreads();
+    tk_merge4<E, R>(buf, buf + P, n);
+    __syncthreads();
+    tk_merge4<E, 4 * R>(buf + P, buf, n);
+    __syncthreads();
+}
+
+// n <= 2 * TK_THREADS
+__device__ __forceinline__ void tk_sort_any(int n, uint64_t* buf) {
+    if (n <= TK_THREADS)
+        tk_sort_lds<1>(n, buf);
+    else
+        tk_sort_lds<2>(n, buf);
+}
+
+// The whole selection for one row in one workgroup: ids / lp of the row's K best (value descending, id
+// ascending) and log-probabilities value - logsumexp.
+__device__ __forceinline__ void tk_row(const float* __restrict__ x, int V, int K, int32_t* __restrict__ ids,
+                       float* __restrict__ lp) {
     __shared__ uint32_t hist[TK_BINS];
     __shared__ float red[TK_THREADS / 64];
     __shared__ float red2[TK_THREADS / 64];
     __shared__ uint32_t skey[TK_MAX];
     __shared__ int sid[TK_MAX];
+    __shared__ uint64_t sbuf[2 * TK_MAX];
     __shared__ uint32_t ckey[TK_CAND];
     __shared__ int cid[TK_CAND];
     __shared__ int s_bin, s_krem, s_slot, s_cnt;
     const int t = threadIdx.x;
-    const float* x = logits + (size_t)blockIdx.x * stride;
 
     // pass 1: online max / sum of exponentials, and the histogram of the top 11 key bits
     for (int i = t; i < TK_BINS; i += TK_THREADS) hist[i] = 0u;
@@ -208,7 +370,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(const float* __restrict_
     se = block_sum(se, red2);
     const float lse = mx + logf(se);
     tk_pick_bin(hist, TK_BINS, K, &s_bin, &s_krem);
-    __syncthreads();
     const uint32_t b1 = (uint32_t)s_bin;
     const int krem = s_krem;
     const int n_cand = (K - krem) + (int)hist[b1];  // keys in bin b1 or above
@@ -231,43 +392,309 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(const float* __restrict_
         auto each = [&](auto&& f) { tk_for_row(x, V, f); };
         tk_select(each, b1 << 21, 0xFFE00000u, krem, K, hist, red, skey, sid, &s_bin, &s_krem, &s_slot);
     }
-    // pad to a power of two and sort: better = larger key, then smaller id
-    int P = 1;
-    while (P < K) P <<= 1;
-    for (int i = K + t; i < P; i += TK_THREADS) {
-        skey[i] = 0u;
-        sid[i] = 0x7FFFFFFF;
-    }
+    for (int i = t; i < K; i += TK_THREADS) sbuf[i] = tk_pack(skey[i], sid[i]);
     __syncthreads();
-    for (int k = 2; k <= P; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = t; i < P; i += TK_THREADS) {
-                const int o = i ^ j;
-                if (o > i) {
-                    const uint32_t ki = skey[i], ko = skey[o];
-                    const int ii = sid[i], io = sid[o];
-                    const bool o_better = ko > ki || (ko == ki && io < ii);
-                    const bool first = (i & k) == 0;  // this pair's half runs best-first
-                    if (first == o_better) {
-                        skey[i] = ko;
-                        skey[o] = ki;
-                        sid[i] = io;
-                        sid[o] = ii;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
+    tk_sort_lds<1>(K, sbuf);
     for (int i = t; i < K; i += TK_THREADS) {
-        ids[(size_t)blockIdx.x * K + i] = sid[i];
-        lp[(size_t)blockIdx.x * K + i] = key_value(skey[i]) - lse;
+        ids[i] = tk_pid(sbuf[i]);
+        lp[i] = key_value(tk_pkey(sbuf[i])) - lse;
     }
 }
 
+__global__ __launch_bounds__(TK_THREADS) void topk_rows(const float* __restrict__ logits, int64_t stride, int V,
+                                                         int K, int32_t* __restrict__ ids, float* __restrict__ lp) {
+    tk_row(logits + (size_t)blockIdx.x * stride, V, K, ids + (size_t)blockIdx.x * K, lp + (size_t)blockIdx.x * K);
+}
+
+// ------------------------------------------------------------------------------------------------------
+// the same top-K with each row split over C workgroups
+// ------------------------------------------------------------------------------------------------------
+// With few rows, one workgroup per row leaves most of the chip idle.  topk_chunk takes one chunk of CL
+// entries of a row into registers, computes its max and sum of exponentials, and finds a threshold key t_c
+// at or below its kt-th largest key (kt about 1.5 K / C: the chunk's expected share of the row's top K, with
+// room to spare) by histograms over the chunk's key range, refined once inside the bin that holds it.  It
+// writes every entry with key >= t_c (at most capc; more marks the chunk as overflowed) and its partial
+// (max, sum, t_c, count).  topk_merge sorts the union of the candidates (a few thousand) and takes the first
+// K.  That is the row's top K whenever the K-th key T is >= every t_c: an entry left out scores below its
+// chunk's t_c <= T and so has K entries ahead of it.  Chunks with t_c > T are read again for their entries
+// in [T, t_c), and the union is sorted once more; an overflow falls back to the one-workgroup selection.
+#define TK_PER 12            // chunk entries per thread, held in registers
+#define TK_SORT_MAX 2048     // candidates a merge sorts
+
+__global__ __launch_bounds__(TK_THREADS) void topk_chunk(const float* __restrict__ logits, int64_t stride, int V,
+                                                          int C, int CL, int kt, int capc, uint2* __restrict__ cand,
+                                                          float4* __restrict__ part) {
+    __shared__ uint32_t hist[TK_BINS];
+    __shared__ float fred[TK_THREADS / 64];
+    __shared__ uint32_t ured[2 * (TK_THREADS / 64)];
+    __shared__ int s_bin, s_krem;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, row = blockIdx.x / C, c = blockIdx.x % C;
+    const int j0 = c * CL, n = min(V - j0, CL);
+    const float* x = logits + (size_t)row * stride + j0;
+    for (int i = t; i < TK_BINS; i += TK_THREADS) hist[i] = 0u;
+    float v[TK_PER];
+#pragma unroll
+    for (int q = 0; q < TK_PER; ++q) {
+        const int e = q * TK_THREADS + t;
+        v[q] = e < n ? x[e] : -INFINITY;
+    }
+    uint32_t k[TK_PER];
+    float m = -INFINITY;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int q = 0; q < TK_PER; ++q) {
+        k[q] = order_key(v[q]);
+        if (q * TK_THREADS + t < n) {
+            m = fmaxf(m, v[q]);
+            lo = min(lo, k[q]);
+            hi = max(hi, k[q]);
+        }
+    }
+    // one block reduction: the chunk's max value and its smallest and largest keys
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        m = fmaxf(m, __shfl_xor(m, o, 64));
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+    }
+    if (lane == 0) {
+        fred[w] = m;
+        ured[w] = lo;
+        ured[TK_THREADS / 64 + w] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TK_THREADS / 64; ++i) {
+        m = fmaxf(m, fred[i]);
+        lo = min(lo, ured[i]);
+        hi = max(hi, ured[TK_THREADS / 64 + i]);
+    }
+    float se = 0.f;  // sum of exp(v - max) over the chunk, finished with the count below
+    if (m != -INFINITY) {
+#pragma unroll
+        for (int q = 0; q < TK_PER; ++q) se += __expf(v[q] - m);  // exp(-inf) = 0 for the padding
+    }
+    uint32_t tc = 0u;  // every entry is a candidate
+    if (n > kt) {
+        tc = lo;
+        int need = kt;
+        uint32_t L = lo, H = hi;
+        for (int round = 0; round < 2 && H > L; ++round) {
+            const uint32_t span = H - L;
+            const int sh = max(0, 32 - __clz((int)span) - 11);  // (key - L) >> sh < TK_BINS
+            if (round > 0) {
+                for (int i = t; i < TK_BINS; i += TK_THREADS) hist[i] = 0u;
+                __syncthreads();
+            }
+#pragma unroll
+            for (int q = 0; q < TK_PER; ++q)
+                if (q * TK_THREADS + t < n && k[q] >= L && k[q] <= H) atomicAdd(&hist[(k[q] - L) >> sh], 1u);
+            __syncthreads();
+            tk_pick_bin(hist, TK_BINS, need, &s_bin, &s_krem);
+            const int b = s_bin, rem = s_krem;
+            const int inbin = (int)hist[b];
+            __syncthreads();
+            tc = L + ((uint32_t)b << sh);
+            if (sh == 0 || (need - rem) + inbin <= need + 32) break;
+            need = rem;  // refine inside the bin
+            L = tc;
+            H = min(H, tc + ((1u << sh) - 1u));
+        }
+    }
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int q = 0; q < TK_PER; ++q) cnt += (q * TK_THREADS + t < n && k[q] >= tc) ? 1u : 0u;
+    // block prefix sum of the counts, with the block sum of se alongside
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
+        if (lane >= o) incl += y;
+        se += __shfl_xor(se, o, 64);
+    }
+    __syncthreads();  // fred / ured are reused
+    if (lane == 63) ured[w] = incl;
+    if (lane == 0) fred[w] = se;
+    __syncthreads();
+    uint32_t off = 0u, total = 0u;
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < TK_THREADS / 64; ++i) {
+        const uint32_t q = ured[i];
+        off += i < w ? q : 0u;
+        total += q;
+        sum += fred[i];
+    }
+    off += incl - cnt;
+    const bool ovf = total > (uint32_t)capc;
+    if (!ovf) {
+        uint2* out = cand + (size_t)blockIdx.x * capc;
+#pragma unroll
+        for (int q = 0; q < TK_PER; ++q) {
+            const int e = q * TK_THREADS + t;
+            if (e < n && k[q] >= tc) out[off++] = make_uint2(k[q], (uint32_t)(j0 + e));
+        }
+    }
+    if (t == 0) part[blockIdx.x] = make_float4(m, sum, __uint_as_float(tc), __int_as_float(ovf ? -1 : (int)total));
+}
+
+#define TK_SLOTS_PT 8  // candidate slots each merge thread loads at once
+
+__global__ __launch_bounds__(TK_THREADS) void topk_merge(const float* __restrict__ logits, int64_t stride, int V,
+                                                          int K, int C, int CL, int capc,
+                                                          const uint2* __restrict__ cand,
+                                                          const float4* __restrict__ part, int32_t* __restrict__ ids,
+                                                          float* __restrict__ lp) {
+    __shared__ uint64_t cb[2 * TK_SORT_MAX];
+    __shared__ uint32_t ptc[64];
+    __shared__ int pcnt[64], poff[65];
+    __shared__ int s_n, s_ovf;
+    __shared__ float s_lse;
+    const int t = threadIdx.x, row = blockIdx.x;
+    const float* x = logits + (size_t)row * stride;
+    const uint2* cr = cand + (size_t)row * C * capc;
+    const int slots = C * capc;
+    // the partials and the first candidate slots in one round trip (slots past a chunk's count are ignored)
+    float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < C) q4 = part[(size_t)row * C + t];
+    uint2 e[TK_SLOTS_PT];
+#pragma unroll
+    for (int u = 0; u < TK_SLOTS_PT; ++u) {
+        const int i = u * TK_THREADS + t;
+        e[u] = i < slots ? cr[i] : make_uint2(0u, 0u);
+    }
+    if (t < 64) {  // wave 0, lane c = chunk c: offsets, overflow and logsumexp by lane reductions
+        const bool on = t < C;
+        const int cnt = on ? __float_as_int(q4.w) : 0;
+        const bool bad = on && cnt < 0;
+        int incl = bad ? 0 : cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (t >= o) incl += y;
+        }
+        const int total = __shfl(incl, 63, 64);
+        float M = on ? q4.x : -INFINITY;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        float S = (on && q4.x != -INFINITY) ? q4.y * __expf(q4.x - M) : 0.f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) S += __shfl_xor(S, o, 64);
+        const bool any_bad = __ballot(bad) != 0ull;
+        if (on) {
+            pcnt[t] = cnt;
+            ptc[t] = __float_as_uint(q4.z);
+            poff[t] = incl - (bad ? 0 : cnt);
+        }
+        if (t == 0) {
+            poff[C] = total;
+            s_n = (any_bad || total > TK_SORT_MAX || total < K) ? -1 : total;
+            s_ovf = 0;
+            s_lse = M + __logf(S);
+        }
+    }
+    __syncthreads();
+    const float lse = s_lse;
+    int n = s_n;
+    bool fallback = n < 0;  // a chunk overflowed, or too many candidates: the one-workgroup selection
+    if (!fallback) {
+    for (int i0 = 0; i0 < slots; i0 += TK_SLOTS_PT * TK_THREADS) {
+#pragma unroll
+        for (int u = 0; u < TK_SLOTS_PT; ++u) {
+            const int i = i0 + u * TK_THREADS + t;
+            if (i0 > 0) e[u] = i < slots ? cr[i] : make_uint2(0u, 0u);
+            if (i < slots) {
+                const int c = i / capc, r = i - c * capc;
+                if (r < pcnt[c]) cb[poff[c] + r] = tk_pack(e[u].x, (int)e[u].y);
+            }
+        }
+    }
+    __syncthreads();
+    for (int pass = 0; pass < 2; ++pass) {
+        tk_sort_any(n, cb);
+        const uint32_t T = tk_pkey(cb[K - 1]);
+        bool again = false;
+        for (int c = 0; c < C; ++c) again |= ptc[c] > T;
+        if (!again) break;
+        // chunks cut above T: their entries in [T, t_c) join the candidates, and the union is sorted again
+        // (once: the K-th key can only rise, and every chunk then holds all of its entries >= T)
+        if (t == 0) s_n = n;
+        __syncthreads();
+        for (int c = 0; c < C; ++c) {
+            if (ptc[c] <= T) continue;
+            const int j0 = c * CL, nc = min(V - j0, CL);
+            for (int j = t; j < nc; j += TK_THREADS) {
+                const uint32_t kk = order_key(x[j0 + j]);
+                if (kk >= T && kk < ptc[c]) {
+                    const int sl = atomicAdd(&s_n, 1);
+                    if (sl < TK_SORT_MAX)
+                        cb[sl] = tk_pack(kk, j0 + j);
+                    else
+                        s_ovf = 1;
+                }
+            }
+        }
+        __syncthreads();
+        if (s_ovf) {
+            fallback = true;
+            break;
+        }
+        n = s_n;
+    }
+    }
+    if (fallback) {
+        tk_row(x, V, K, ids + (size_t)row * K, lp + (size_t)row * K);
+        return;
+    }
+    for (int i = t; i < K; i += TK_THREADS) {
+        const uint64_t p = cb[i];
+        ids[(size_t)row * K + i] = tk_pid(p);
+        lp[(size_t)row * K + i] = key_value(tk_pkey(p)) - lse;
+    }
+}
+
+// Split of each row: C chunks of CL entries (a multiple of 4), kt the share each chunk keeps, capc the
+// candidate slots per chunk.  C = 1: one workgroup per row.
+struct TkSplit {
+    int C, CL, kt, capc;
+};
+static TkSplit topk_split(int rows, int V, int K) {
+    TkSplit sp{1, V, K, 0};
+    int C = (256 + rows - 1) / rows;  // about one workgroup per compute unit
+    if (C < 2) return sp;              // enough rows to fill the chip one workgroup each
+    C = std::max(C, (V + TK_PER * TK_THREADS - 1) / (TK_PER * TK_THREADS));  // chunks fit in registers
+    C = std::min(C, 32);
+    const int CL = (((V + C - 1) / C) + 3) & ~3;
+    if (CL > TK_PER * TK_THREADS) return sp;
+    C = (V + CL - 1) / CL;  // no empty chunk
+    if (C < 2) return sp;
+    const int kt = std::min(CL, (3 * K + 2 * C - 1) / (2 * C) + 8);
+    sp.C = C;
+    sp.CL = CL;
+    sp.kt = kt;
+    sp.capc = std::min(CL, 2 * kt + 32);
+    return sp;
+}
+
+size_t topk_workspace_bytes(int rows, int V, int K) {
+    const TkSplit sp = topk_split(rows, V, K);
+    if (sp.C < 2) return 0;
+    return (size_t)rows * sp.C * (sizeof(float4) + (size_t)sp.capc * sizeof(uint2));
+}
+
 hipError_t launch_topk_rows(int rows, const float* logits, int64_t stride, int V, int K, int32_t* ids, float* lp,
-                            hipStream_t st) {
-    hipLaunchKernelGGL(topk_rows, dim3(rows), dim3(TK_THREADS), 0, st, logits, stride, V, K, ids, lp);
+                            void* ws, hipStream_t st) {
+    const TkSplit sp = topk_split(rows, V, K);
+    if (sp.C < 2) {
+        hipLaunchKernelGGL(topk_rows, dim3(rows), dim3(TK_THREADS), 0, st, logits, stride, V, K, ids, lp);
+        return hipGetLastError();
+    }
+    float4* part = (float4*)ws;
+    uint2* cand = (uint2*)(part + (size_t)rows * sp.C);
+    hipLaunchKernelGGL(topk_chunk, dim3(rows * sp.C), dim3(TK_THREADS), 0, st, logits, stride, V, sp.C, sp.CL, sp.kt,
+                       sp.capc, cand, part);
+    hipLaunchKernelGGL(topk_merge, dim3(rows), dim3(TK_THREADS), 0, st, logits, stride, V, K, sp.C, sp.CL, sp.capc,
+                       cand, part, ids, lp);
     return hipGetLastError();
 }
 

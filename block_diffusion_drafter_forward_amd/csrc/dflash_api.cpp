@@ -824,14 +824,24 @@ extern "C" int dflash_linear(int dtype, int M, int N, int K, const void* x, int6
 #define DDT_MAX_DEPTH 16
 #define DDT_MAX_BUDGET 2047
 
+extern "C" size_t dflash_topk_logprobs_workspace_bytes(int rows, int vocab, int k) {
+    if (rows < 1 || vocab < 1 || k < 1 || k > vocab || k > DDT_MAX_K) return 0;
+    return topk_workspace_bytes(rows, vocab, k);
+}
+
 extern "C" int dflash_topk_logprobs(int rows, int vocab, int k, const float* logits, int64_t row_stride,
-                                    int32_t* ids, float* logprobs, void* stream) {
+                                    int32_t* ids, float* logprobs, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
     if (rows < 1 || vocab < 1) return fail(DFLASH_E_ARG, "rows and vocab must be >= 1");
     if (!logits || !ids || !logprobs) return fail(DFLASH_E_ARG, "a required pointer is NULL");
     if (k < 1 || k > vocab) return fail(DFLASH_E_ARG, "k must be in [1, vocab]");
     if (k > DDT_MAX_K) return fail(DFLASH_E_UNSUPPORTED, "k must be <= %d", DDT_MAX_K);
     if (row_stride < vocab) return fail(DFLASH_E_ARG, "row_stride < vocab");
-    HIP_TRY(launch_topk_rows(rows, logits, row_stride, vocab, k, ids, logprobs, (hipStream_t)stream));
+    const size_t need = topk_workspace_bytes(rows, vocab, k);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(DFLASH_E_ARG, "workspace of %zu bytes needed", need);
+    if (need && ((uintptr_t)workspace & 15)) return fail(DFLASH_E_ARG, "workspace must be 16-byte aligned");
+    HIP_TRY(launch_topk_rows(rows, logits, row_stride, vocab, k, ids, logprobs, workspace, (hipStream_t)stream));
     return DFLASH_OK;
 }
 

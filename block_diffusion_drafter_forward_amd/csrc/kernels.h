@@ -118,7 +118,9 @@ hipError_t launch_head_merge(int bf16, int M, int V, int top_k, int sample, cons
 // ---- DDTree ----------------------------------------------------------------------------------------------
 // Per row of logits[rows][stride]: the K best (value desc, id asc) and their log-probabilities.
 hipError_t launch_topk_rows(int rows, const float* logits, int64_t stride, int V, int K, int32_t* ids, float* lp,
-                            hipStream_t st);
+                            void* ws, hipStream_t st);
+// Workspace of launch_topk_rows (0 when each row gets one workgroup).
+size_t topk_workspace_bytes(int rows, int V, int K);
 // Algorithm 1 per request: depth d (0-based) of request r reads lp / ids at r * req_stride + d * K.
 hipError_t launch_ddtree_build(int batch, int D, int K, const float* lp, const int32_t* ids, int64_t req_stride,
                                int budget, int32_t* node_token, int32_t* node_parent, int32_t* node_depth,

@@ -94,8 +94,10 @@ _SIGS = {
                                             ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "dflash_last_error": (ctypes.c_char_p, []),
+    "dflash_topk_logprobs_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "dflash_topk_logprobs": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
-                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p]),
     "dflash_ddtree_build": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -163,8 +165,14 @@ def dflash_destroy(h: int) -> None:
     lib().dflash_destroy(h)
 
 
-def dflash_topk_logprobs(rows, vocab, k, logits, row_stride, ids, logprobs, stream) -> int:
-    return lib().dflash_topk_logprobs(rows, vocab, k, logits, row_stride, ids, logprobs, stream)
+def dflash_topk_logprobs_workspace_bytes(rows, vocab, k) -> int:
+    return lib().dflash_topk_logprobs_workspace_bytes(rows, vocab, k)
+
+
+def dflash_topk_logprobs(rows, vocab, k, logits, row_stride, ids, logprobs, workspace, workspace_bytes,
+                         stream) -> int:
+    return lib().dflash_topk_logprobs(rows, vocab, k, logits, row_stride, ids, logprobs, workspace, workspace_bytes,
+                                      stream)
 
 
 def dflash_ddtree_build(batch, depth, k, logprobs, ids, req_stride, budget, node_token, node_parent, node_depth,

@@ -257,10 +257,14 @@ int dflash_verify_sample(int batch, int n_draft, int vocab, const int32_t *draft
  * (1 .. L-1) is the distribution of draft depth d.                                                        */
 
 /* The k best tokens of each of `rows` logit rows (device float, row stride row_stride >= vocab), ordered by
- * (logit descending, id ascending), and their log-probabilities logit - logsumexp(row).  Outputs are device
- * [rows][k] int32 ids and float log-probs.  1 <= k <= min(vocab, 1024).  No workspace.                    */
+ * (logit descending, id ascending), and their log-probabilities logit - logsumexp(row) ([DDT] §3.4.4
+ * Lemma 1: only each depth's top K can enter the tree).  Outputs are device [rows][k] int32 ids and float
+ * log-probs.  1 <= k <= min(vocab, 1024).  With few rows each row is split over several workgroups whose
+ * partial results go through `workspace` (device, 16-byte aligned, at least
+ * dflash_topk_logprobs_workspace_bytes(rows, vocab, k) bytes; NULL allowed when that is 0).                */
+size_t dflash_topk_logprobs_workspace_bytes(int rows, int vocab, int k);
 int dflash_topk_logprobs(int rows, int vocab, int k, const float *logits, int64_t row_stride, int32_t *ids,
-                         float *logprobs, void *stream);
+                         float *logprobs, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Algorithm 1 per request: the `budget` most probable prefixes under the factorised distribution, in the
  * order a best-first heap of rank tuples pops them (next sibling and first child pushed per pop; equal

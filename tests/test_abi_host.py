@@ -234,13 +234,29 @@ def test_unpacked_bf16_handle_refuses_to_run(D):
 @pytest.mark.parametrize("args,code", [
     (dict(rows=0), -1), (dict(k=0), -1), (dict(k=6000), -1), (dict(k=1025, vocab=4096), -4),
     (dict(row_stride=10), -1), (dict(logits=None), -1),
+    (dict(ws=None), -1), (dict(ws_bytes=100), -1), (dict(ws=0x8008), -1),
 ])
 def test_topk_logprobs_validation(D, args, code):
-    a = dict(rows=2, vocab=5003, k=8, logits=0x1000, row_stride=5003, ids=0x2000, lp=0x3000)
+    a = dict(rows=2, vocab=5003, k=8, logits=0x1000, row_stride=5003, ids=0x2000, lp=0x3000, ws=0x8000,
+             ws_bytes=1 << 30)
     a.update(args)
     assert D.dflash_topk_logprobs(a["rows"], a["vocab"], a["k"], a["logits"], a["row_stride"], a["ids"], a["lp"],
-                                  None) == code
+                                  a["ws"], a["ws_bytes"], None) == code
     assert D.dflash_last_error()
+
+
+def test_topk_logprobs_workspace_size(D):
+    """Few rows split over chunks: a 16-byte partial per chunk plus (key, id) slots for its candidates (twice its
+    share kt = ceil(1.5 K / C) + 8, plus 32); a batch that fills the chip with one workgroup per row needs
+    none."""
+    # 16 rows of 151936: 16 chunks of 9496
+    assert D.dflash_topk_logprobs_workspace_bytes(16, 151936, 1024) == 16 * 16 * (16 + (2 * (96 + 8) + 32) * 8)
+    assert D.dflash_topk_logprobs_workspace_bytes(16, 151936, 16) == 16 * 16 * (16 + (2 * (2 + 8) + 32) * 8)
+    assert D.dflash_topk_logprobs_workspace_bytes(256, 151936, 1024) == 0
+    assert D.dflash_topk_logprobs_workspace_bytes(16, 151936, 1025) == 0   # refused by the call itself
+    # a short row: chunks shorter than k keep every entry
+    n = D.dflash_topk_logprobs_workspace_bytes(1, 5003, 1000)
+    assert n > 0 and n % 16 == 0
 
 
 @pytest.mark.parametrize("args,code", [

@@ -30,7 +30,10 @@ def _topk_gpu(torch, D, lg, k):
     x = torch.from_numpy(np.ascontiguousarray(lg.astype(np.float32))).cuda()
     ids = torch.empty((rows, k), dtype=torch.int32, device="cuda")
     lp = torch.empty((rows, k), dtype=torch.float32, device="cuda")
-    D.check(D.dflash_topk_logprobs(rows, V, k, x.data_ptr(), V, ids.data_ptr(), lp.data_ptr(), D._stream()), "topk")
+    nws = D.dflash_topk_logprobs_workspace_bytes(rows, V, k)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+    D.check(D.dflash_topk_logprobs(rows, V, k, x.data_ptr(), V, ids.data_ptr(), lp.data_ptr(), ws.data_ptr(), nws,
+                                   D._stream()), "topk")
     torch.cuda.synchronize()
     return ids.cpu().numpy(), lp.cpu().numpy()
 
@@ -45,6 +48,25 @@ def test_topk_logprobs_matches_oracle(k):
     lg[2] = 0.5                              # every logit equal
     lg[3, rng.choice(V, 40, replace=False)] = lg[3].max() + 1.0  # a 40-way tie at the top
     lg[4] = -lg[4]                           # negative keys dominate the order
+    ids, lp = _topk_gpu(torch, D, lg, k)
+    want_ids, want_lp = T.topk_logprobs(lg.astype(np.float64), k)
+    np.testing.assert_array_equal(ids, want_ids)
+    assert np.all(np.abs(lp - want_lp) <= 2e-5 + 2e-6 * np.abs(want_lp))
+
+
+@pytest.mark.parametrize("rows,V,k", [(16, 151936, 1024), (16, 151936, 16), (1, 151936, 1000), (3, 65537, 257),
+                                      (256, 5003, 64), (40, 2000, 1024)])
+def test_topk_logprobs_split_rows_match_oracle(rows, V, k):
+    """Row counts that split each row over many workgroups (few rows, the drafter's 16 block rows at the full
+    vocabulary) and ones that do not (256 rows), with ties inside and across chunks."""
+    torch, D, S = _mods()
+    rng = np.random.default_rng(rows * 7 + V + k)
+    lg = rng.normal(0.0, 2.5, size=(rows, V)).astype(np.float32)
+    lg[0] = np.round(lg[0] * 4) / 4                                  # ties everywhere, across chunk borders
+    if rows > 1:
+        lg[1] = -3.0                                                # one value: the smallest ids win
+    if rows > 2:
+        lg[2, rng.choice(V, min(V, 3 * k), replace=False)] = 30.0   # 3k-way tie at the top
     ids, lp = _topk_gpu(torch, D, lg, k)
     want_ids, want_lp = T.topk_logprobs(lg.astype(np.float64), k)
     np.testing.assert_array_equal(ids, want_ids)
@@ -274,8 +296,10 @@ def test_ddtree_chain_on_a_drafter_pass():
     K = min(budget, V)
     ids = torch.empty((B, L, K), dtype=torch.int32, device="cuda")
     lp = torch.empty((B, L, K), dtype=torch.float32, device="cuda")
-    D.check(D.dflash_topk_logprobs(B * L, V, K, logits.data_ptr(), V, ids.data_ptr(), lp.data_ptr(), D._stream()),
-            "topk")
+    nws = D.dflash_topk_logprobs_workspace_bytes(B * L, V, K)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+    D.check(D.dflash_topk_logprobs(B * L, V, K, logits.data_ptr(), V, ids.data_ptr(), lp.data_ptr(), ws.data_ptr(),
+                                   nws, D._stream()), "topk")
     tok = torch.empty((B, budget), dtype=torch.int32, device="cuda")
     par, dep = torch.empty_like(tok), torch.empty_like(tok)
     lq = torch.empty((B, budget), dtype=torch.float32, device="cuda")
