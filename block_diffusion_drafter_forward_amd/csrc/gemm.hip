@@ -146,33 +146,32 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_bf16(const bf16_t* __restr
 }
 
 // ------------------------------------------------------------------------------------------------------
-// LDS-tiled MFMA GEMM (bfloat16) for large M; the main loop lives in gemm_core.h (shared with the LM head)
+// wide-tile MFMA GEMM (bfloat16) for large M: the main loop of gemm_core.h, split-K partials out
 // ------------------------------------------------------------------------------------------------------
-template <bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict__ x, int ldx, size_t xplane, int M,
-                                                       const bf16_t* __restrict__ wp, int N, int K, int kps,
-                                                       float* __restrict__ part) {
-    __shared__ __attribute__((aligned(16))) bf16_t sw[TL_SW];
-    __shared__ __attribute__((aligned(16))) bf16_t sx[(SPLIT ? 2 : 1) * TL_BM * TL_LD];
+template <bool SPLIT, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_wide_bf16(
+    const bf16_t* __restrict__ x, int ldx, size_t xplane, int M, const bf16_t* __restrict__ wp, int N, int K,
+    int kps, float* __restrict__ part) {
+    __shared__ __attribute__((aligned(16))) bf16_t lds[wd_lds_elems(NT, SPLIT)];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int wn = wave >> 1, wm = wave & 1;
     int tx, ty;
-    if (!xcd_tile(blockIdx.x, (N + TL_BN - 1) / TL_BN, (M + TL_BM - 1) / TL_BM, tx, ty)) return;
-    const int n0 = tx * TL_BN, m0 = ty * TL_BM, s = blockIdx.y;
-    const int kb = s * kps, ke = min(K, kb + kps);
-    f32x4 acc[4][4];
-    tiled_mainloop<SPLIT>(x, ldx, xplane, M, wp, N, K, n0, m0, kb, ke, sw, sx, acc);
+    if (!xcd_tile(blockIdx.x, (N + wd_bn(NT) - 1) / wd_bn(NT), (M + WD_BM - 1) / WD_BM, tx, ty)) return;
+    const int n0 = tx * wd_bn(NT), m0 = ty * WD_BM, sp = blockIdx.y;
+    const int kb = sp * kps, ke = min(K, kb + kps);
+    f32x4 acc[NT][4];
+    wide_mainloop<SPLIT, NT>(x, ldx, xplane, M, wp, N, n0, m0, kb, ke, lds, acc);
     // D lane l: n = 4 (l / 16) + i, m = l % 16 within each 16 x 16 tile
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < NT; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int n = n0 + wn * 64 + a * 16 + 4 * g;
+            const int n = n0 + wn * 16 * NT + a * 16 + 4 * g;
             const int m = m0 + wm * 64 + b * 16 + r;
             if (m >= M || n >= N) continue;
-            float* dst = part + ((size_t)s * M + m) * N + n;
-            f32x4 v = acc[a][b];
+            float* dst = part + ((size_t)sp * M + m) * N + n;
+            const f32x4 v = acc[a][b];
             if ((N & 3) == 0 && n + 3 < N) {
                 *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
             } else {
@@ -263,19 +262,31 @@ GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K, bool few_splits) {
         return p;
     }
     p.kind = GEMM_TILED;
-    const int tiles = ((N + TL_BN - 1) / TL_BN) * ((M + TL_BM - 1) / TL_BM);
-    const int kt = (K + TL_BK - 1) / TL_BK;
-    // The tiled kernel is MFMA-bound at serving sizes, so what counts is an even share per CU: below 512
-    // tiles, split K (powers of two) until every split has at most 32 k-tiles and there are 256 or more
-    // workgroups.  Measured on MI355X at M = 256 (Qwen3-8B shapes): gate/up 2 splits, QKV 4, O 4, down 8,
-    // 200 us per drafter pass less than aiming at ~384 workgroups; more splits cost more in partial traffic
-    // than they gain in balance.
-    int splits = 1;
-    if (tiles < 512)
-        while (splits < 16 && (kt > 32 * splits || tiles * splits < 256)) splits *= 2;
-    if (splits > kt / 4) splits = kt / 4 > 0 ? kt / 4 : 1;
-    int kps_tiles = (kt + splits - 1) / splits;
-    p.kps = kps_tiles * TL_BK;
+    // Wide tiles, one workgroup per CU: pick the tile width (256 or 192 columns) and the split of K by an
+    // estimate of time = generations of workgroups over the 256 CUs x k-tiles per split x the k-tile time
+    // (measured on MI355X with both activation planes: 2.2 us for a 256 x 128 x 64 k-tile, 1.8 us for a
+    // 192-wide one) + the float32 partials written and read back by the consumer at ~5 TB/s.  At M = 256
+    // (Qwen3-8B shapes) this picks gate/up 192 wide x 1 split (256 workgroups), QKV 192 x 4, O 256 x 8,
+    // down 256 x 8.
+    double best_us = 1e30;
+    p.nt = 8;
+    p.kps = K;
+    for (int nt : {8, 6}) {
+        const int tiles = ((N + 32 * nt - 1) / (32 * nt)) * ((M + WD_BM - 1) / WD_BM);
+        const int kt = (K + WD_BK - 1) / WD_BK;
+        const double ktile_us = nt == 8 ? 2.2 : 1.8;
+        for (int sp = 1; sp <= 16 && sp <= kt; ++sp) {
+            const int per = (kt + sp - 1) / sp;
+            const int used = (kt + per - 1) / per;  // splits actually launched
+            const double gens = (double)((tiles * used + 255) / 256);
+            const double us = gens * per * ktile_us + (double)used * M * N * 4.0 * 2.0 / 5.0e6;
+            if (us < best_us - 1e-9) {
+                best_us = us;
+                p.nt = nt;
+                p.kps = per * WD_BK;
+            }
+        }
+    }
     p.splits = (K + p.kps - 1) / p.kps;
     return p;
 }
@@ -284,7 +295,6 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, const void* x, int ldx, size_t xp
                             int N, int K, float* part, hipStream_t st) {
     const bool split = xplane != 0;
     const dim3 gs((N + 63) / 64, p.splits);
-    const dim3 gt(xcd_tile_count((N + TL_BN - 1) / TL_BN, (M + TL_BM - 1) / TL_BM), p.splits);
     const bf16_t* xb = (const bf16_t*)x;
     const bf16_t* wp = (const bf16_t*)wpacked;
     switch (p.kind) {
@@ -303,12 +313,18 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, const void* x, int ldx, size_t xp
 #undef DF_SKINNY
             break;
         }
-        case GEMM_TILED:
-            if (split)
-                DF_LAUNCH((gemm_tiled_bf16<true>), gt, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kps, part);
-            else
-                DF_LAUNCH((gemm_tiled_bf16<false>), gt, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kps, part);
+        case GEMM_TILED: {
+            if (p.nt != 6 && p.nt != 8) return hipErrorInvalidValue;
+            const dim3 gt(xcd_tile_count((N + 32 * p.nt - 1) / (32 * p.nt), (M + WD_BM - 1) / WD_BM), p.splits);
+#define DF_WIDE(SP, NT) DF_LAUNCH((gemm_wide_bf16<SP, NT>), gt, dim3(256), 0, st, xb, ldx, xplane, M, wp, N, K, p.kps, part)
+            if (p.nt == 6) {
+                if (split) DF_WIDE(true, 6); else DF_WIDE(false, 6);
+            } else {
+                if (split) DF_WIDE(true, 8); else DF_WIDE(false, 8);
+            }
+#undef DF_WIDE
             break;
+        }
         default:
             return hipErrorInvalidValue;
     }
@@ -324,7 +340,7 @@ const char* gemm_kernel_name(const GemmPlan& p, bool pair) {
     switch (p.kind) {
         case GEMM_SKINNY1: return pair ? "gemm_skinny_bf16_m16_pair" : "gemm_skinny_bf16_m16";
         case GEMM_SKINNY2: return pair ? "gemm_skinny_bf16_m32_pair" : "gemm_skinny_bf16_m32";
-        case GEMM_TILED: return pair ? "gemm_tiled_bf16_pair" : "gemm_tiled_bf16";
+        case GEMM_TILED: return pair ? "gemm_wide_bf16_pair" : "gemm_wide_bf16";
         default: return "gemm_f32";
     }
 }

@@ -42,6 +42,7 @@ struct GemmPlan {
     int kpw;     // skinny: k-range per wave (multiple of 256)
     int waves;   // skinny: waves per workgroup (4 or 8)
     int kps;     // tiled: k-range per split (multiple of 64)
+    int nt;      // tiled: n-tiles of 16 per wave (8: 256-wide workgroup tiles, 6: 192-wide)
 };
 // few_splits: prefer fewer, longer k-ranges per wave (set for the drafter layer's GEMMs, where it was measured
 // to pay off through cheaper split-K consumers).
