@@ -410,20 +410,23 @@ def _min_inject_ws(D, m, n, kv):
 
 
 def test_inject_short_last_chunk_needs_its_own_split_partials(D):
-    """4096 + 1000 rows: the 1000-row chunk has fewer output tiles, so its fusion GEMM splits K further and
-    writes more float32 partials than a whole 4096-row chunk.  A workspace sized for one whole chunk must be
-    refused for that call instead of being overrun."""
+    """4096 + t rows: the t-row tail chunk has its own GEMM plans, and a tail whose fusion or KV GEMM splits K
+    further than a whole chunk's writes more float32 partials than a whole 4096-row chunk.  Some of the tried
+    tails must do so (the plan weighs generations of workgroups against partial traffic, so which ones
+    depends on it), and for each of them a workspace sized for one whole chunk must be refused instead of
+    being overrun."""
     import workloads as W
     kv = D.dflash_kv(0x40, 0x50, 8)
     m = _create(D, W.QWEN3_8B)
     try:
         one_chunk = _min_inject_ws(D, m, 4096, kv)
-        with_tail = _min_inject_ws(D, m, 4096 + 1000, kv)
-        assert with_tail > one_chunk
-        rc = D.dflash_inject_ctx(m.handle, 1, 4096 + 1000, 0x10, m.shape.feat_dim, 0x20, 0x30, 0x40, 8, kv, 0x100000,
-                                 one_chunk, None)
-        assert rc == D.DFLASH_E_CAPACITY
-        assert D.dflash_inject_workspace_bytes(m.handle, 4096 + 1000) >= with_tail
+        larger = [t for t in (1000, 2500, 3500) if _min_inject_ws(D, m, 4096 + t, kv) > one_chunk]
+        assert larger
+        for t in larger:
+            rc = D.dflash_inject_ctx(m.handle, 1, 4096 + t, 0x10, m.shape.feat_dim, 0x20, 0x30, 0x40, 8, kv,
+                                     0x100000, one_chunk, None)
+            assert rc == D.DFLASH_E_CAPACITY
+            assert D.dflash_inject_workspace_bytes(m.handle, 4096 + t) >= _min_inject_ws(D, m, 4096 + t, kv)
     finally:
         m.close()
 
