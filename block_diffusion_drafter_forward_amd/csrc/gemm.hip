@@ -47,7 +47,7 @@ hipError_t launch_pack(const Segs& src, int N, int K, void* dst, hipStream_t st)
 // ------------------------------------------------------------------------------------------------------
 // skinny MFMA GEMM (bfloat16), M <= 16 * MT, packed weights
 // ------------------------------------------------------------------------------------------------------
-// Workgroup = W waves (4, or 8: see plan_gemm) on the same 64 output columns (4 n-tiles of 16); wave w takes
+// Workgroup = W waves (4, 8 or 2: see plan_gemm) on the same 64 output columns (4 n-tiles of 16); wave w takes
 // the k-range [k0 + w * kpw, k0 + (w + 1) * kpw) of the workgroup's split.  Per 256-wide k-chunk a wave loads, for each
 // n-tile, eight packed weight fragments (one coalesced 1 KB load each: the A operand, row = lane % 16,
 // k = 32 j + 8 (lane / 16)) and the matching eight 16-byte pieces of its activation row (B operand), then
@@ -259,6 +259,24 @@ GemmPlan plan_gemm(int dtype_bf16, int M, int N, int K, bool few_splits) {
                 p.splits = K / 2048;
             }
         }
+        // K a whole number of 512-wide pairs of chunks but not of 1024-wide four-wave splits (whose last split
+        // leaves waves idle), and one generation of waves (eight per CU) covering every chunk: two-wave
+        // workgroups, one chunk per wave, keep every wave busy and spread the workgroups over all CUs.  Where
+        // that would give more than eight splits (more than one batch of the consumer's split loads), eight-wave
+        // workgroups halve the splits instead.  Measured on MI355X with cold weights: QKV 6144 x 2560 8.2 us
+        // with two waves instead of 9.7; down 2560 x 9728 10.9 with two waves (19 splits, its row norm +1.1)
+        // or 11.7 with eight (5 splits) instead of 12.3 (10 splits); gate/up 19456 x 2560 (3040 chunks, more
+        // than one generation) stays faster with four waves.
+        if (few_splits && M <= 16 && p.kpw == 256 && p.waves == 4 && K % 1024 != 0 && K % 512 == 0 &&
+            groups * (K / 256) <= 2048) {
+            if (K / 512 <= 8) {
+                p.waves = 2;
+                p.splits = K / 512;
+            } else {
+                p.waves = 8;
+                p.splits = (K + 2047) / 2048;
+            }
+        }
         return p;
     }
     p.kind = GEMM_TILED;
@@ -303,9 +321,10 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, const void* x, int ldx, size_t xp
             const dim3 block(64 * p.waves);
 #define DF_SKINNY(MT, SP, W) DF_LAUNCH((gemm_skinny_bf16<MT, SP, W>), gs, block, 0, st, xb, ldx, xplane, M, wp, N, K, p.kpw, part)
             const int mt = p.kind == GEMM_SKINNY1 ? 1 : 2;
-            if (p.waves == 8) {
+            if (p.waves == 8 || p.waves == 2) {
                 if (mt != 1) return hipErrorInvalidValue;
-                if (split) DF_SKINNY(1, true, 8); else DF_SKINNY(1, false, 8);
+                if (p.waves == 8) { if (split) DF_SKINNY(1, true, 8); else DF_SKINNY(1, false, 8); }
+                else { if (split) DF_SKINNY(1, true, 2); else DF_SKINNY(1, false, 2); }
             } else {
                 if (mt == 1) { if (split) DF_SKINNY(1, true, 4); else DF_SKINNY(1, false, 4); }
                 else { if (split) DF_SKINNY(2, true, 4); else DF_SKINNY(2, false, 4); }
