@@ -15,6 +15,8 @@
 //                   for every tile.  Writes (m, l, O) partials.
 //   tree_merge      one wave per (token, KV head): the token's ancestor keys (at most depth + 1, a short list)
 //                   by vector dot products, merged with the context partials by log-sum-exp; bfloat16 out.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -23,8 +25,12 @@ namespace df {
 #define TA_D 128
 #define TA_SUB 64         // keys per LDS round
 #define TA_MAX_PAGES 256  // pages of one context chunk
-#define TA_KLD (128 + 8)
-#define TA_VLD (16 + 8)
+#define TA_KLD (128 + 16)
+// Values in LDS: one row per (32-key slice hk, d) holding the slice's two pages interleaved by groups of four
+// slots, [g][page 2 hk + pp][4 slots] (g = slot / 4), so that a lane's V^T operand (slots 4g..4g+3 of both
+// pages) is one aligned 16-byte read; rows padded to 80 bytes.
+#define TA_SVLD (32 + 8)
+#define TA_RESCALE 8.0f  // log2 growth of a row maximum before the running reference is raised
 
 static size_t ta_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
     constexpr int PPT = PIECES / NT;
     constexpr int PPP = 512 / NT;
     __shared__ __attribute__((aligned(16))) bf16_t sk[TA_SUB * TA_KLD];
-    __shared__ __attribute__((aligned(16))) bf16_t sv[NPG * D * TA_VLD];
+    __shared__ __attribute__((aligned(16))) bf16_t sv[(NPG / 2) * D * TA_SVLD];
     __shared__ int spg[TA_MAX_PAGES];
     // grid: KV head fastest, then super tile, chunk, request
     const int stiles = (tiles + TW * QT - 1) / (TW * QT);
@@ -260,8 +266,27 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
             }
         }
     };
+    // piece qq of page slot e into LDS: K row-major, V^T (piece q2 = slots 8 h .. 8 h + 7 of row d, groups 2 h
+    // and 2 h + 1) into the interleaved value rows
+    auto put = [&](int e, int qq, u32x4 v) {
+        if (qq < 256) {
+            *(u32x4*)(sk + (e * 16 + (qq >> 4)) * TA_KLD + (qq & 15) * 8) = v;
+        } else {
+            const int q2 = qq - 256, half = q2 & 1;
+            bf16_t* row = sv + ((e >> 1) * D + (q2 >> 1)) * TA_SVLD + (e & 1) * 4;
+            *(u32x2*)(row + (2 * half) * 8) = u32x2{v[0], v[1]};
+            *(u32x2*)(row + (2 * half + 1) * 8) = u32x2{v[2], v[3]};
+        }
+    };
     auto stash = [&](int ts) {
         okmask = __builtin_amdgcn_readfirstlane(okmask);
+        if (okmask == (1u << NPG) - 1 && ts + TA_SUB <= t1) {  // every page mapped and full (scalar branch)
+#pragma unroll
+            for (int e = 0; e < NPG; ++e)
+#pragma unroll
+                for (int u = 0; u < PPP; ++u) put(e, tid + u * NT, pf[e * PPP + u]);
+            return;
+        }
 #pragma unroll
         for (int e = 0; e < NPG; ++e) {
             const bool ok = (okmask >> e) & 1u;
@@ -271,21 +296,16 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
                 const int qq = tid + u * NT;
                 u32x4 v = pf[e * PPP + u];
                 if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-                if (qq < 256) {
-                    *(u32x4*)(sk + (e * 16 + (qq >> 4)) * TA_KLD + (qq & 15) * 8) = v;
-                } else {
-                    const int q2 = qq - 256;
-                    if (nvalid < 16) {  // values of slots past the last key may hold anything: zero them
-                        const int half = q2 & 1;
+                if (qq >= 256 && nvalid < 16) {  // values of slots past the last key may hold anything: zero them
+                    const int half = (qq - 256) & 1;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int s0 = half * 8 + 2 * j;
-                            const uint32_t m = (s0 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
-                            v[j] &= m;
-                        }
+                    for (int j = 0; j < 4; ++j) {
+                        const int s0 = half * 8 + 2 * j;
+                        const uint32_t m = (s0 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
+                        v[j] &= m;
                     }
-                    *(u32x4*)(sv + (e * D + (q2 >> 1)) * TA_VLD + (q2 & 1) * 8) = v;
                 }
+                put(e, qq, v);
             }
         }
     };
@@ -299,23 +319,32 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
 #pragma unroll
         for (int s = 0; s < 4; ++s) qf[qi][s] = ok ? ld16(qp + s * 32) : u32x4{0u, 0u, 0u, 0u};
     }
-    f32x4 o[QT][8];
-    float m_run[QT], l_run[QT];
+    // o[qi][0..7]: O^T for the eight 16-row d-tiles; o[qi][8]: the same product against an all-ones V^T,
+    // i.e. the row sums l of the bfloat16 P that weighted O (every lane ends with its token's sum).
+    f32x4 o[QT][9];
+    float m_run[QT];
 #pragma unroll
     for (int qi = 0; qi < QT; ++qi) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[qi][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < 9; ++dt) o[qi][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         m_run[qi] = -INFINITY;
-        l_run[qi] = 0.f;
     }
+    const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bfloat16 1.0 x 8
 
     __syncthreads();  // page ids in LDS
     for (int j = tid; j < chunk_tokens / 16 && t0 + 16 * j < t1; j += NT) {
         if ((t0 >> 4) + j >= max_pages) set_err(err, DFLASH_DEVERR_POS);
         else if (spg[j] < 0 || spg[j] >= n_pages) set_err(err, DFLASH_DEVERR_PAGE);
     }
-    if (t0 < t1) prefetch(t0);
-    for (int ts = t0; ts < t1; ts += TA_SUB) {
+    // One 64-key round starting at ts.  TAIL: the round runs past the chunk's last key (masked scores, slices
+    // past the end skipped); the full rounds carry no masking code.
+    //
+    // Softmax in the log2 domain against a running reference m: p = 2^(s * scale - m).  The reference is raised
+    // (and O, l rescaled by 2^(m_old - m_new)) only when some row's maximum exceeds it by more than
+    // TA_RESCALE; otherwise p may reach 2^TA_RESCALE, which float32 sums and the bfloat16 P hold at the same
+    // relative precision.  The (m, l, O) partials are exact for any reference, so the merge is unchanged.
+    auto round = [&](int ts, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
         __syncthreads();
         stash(ts);
         __syncthreads();
@@ -336,70 +365,65 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
         u32x4 pb[QT][NPG / 2];
 #pragma unroll
         for (int qi = 0; qi < QT; ++qi) {
-            float x[NPG][4];
-#pragma unroll
-            for (int e = 0; e < NPG; ++e)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x[e][i] = sa[qi][e][i] * scale_log2;
-            if (ts + TA_SUB > t1) {
+            if (TAIL) {
                 const int nk = t1 - ts;
 #pragma unroll
                 for (int e = 0; e < NPG; ++e)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) x[e][i] = 16 * e + 4 * g + i < nk ? x[e][i] : -INFINITY;
+                    for (int i = 0; i < 4; ++i) sa[qi][e][i] = 16 * e + 4 * g + i < nk ? sa[qi][e][i] : -INFINITY;
             }
+            // row maximum of the raw scores (scale_log2 > 0 keeps the order)
             float mx = -INFINITY;
 #pragma unroll
             for (int e = 0; e < NPG; ++e)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[e][i]);
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sa[qi][e][i]);
             mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run[qi], mx);
-            const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run[qi] - m_ref);
-            m_run[qi] = m_new;
+            const float mxs = mx * scale_log2;
+            if (__any(mxs > m_run[qi] + TA_RESCALE)) {
+                const float m_new = fmaxf(m_run[qi], mxs);
+                const float alpha = __builtin_amdgcn_exp2f(m_run[qi] - (m_new == -INFINITY ? 0.f : m_new));
+                m_run[qi] = m_new;
+#pragma unroll
+                for (int dt = 0; dt < 9; ++dt) {
+                    o[qi][dt][0] *= alpha; o[qi][dt][1] *= alpha; o[qi][dt][2] *= alpha; o[qi][dt][3] *= alpha;
+                }
+            }
+            const float neg_m = m_run[qi] == -INFINITY ? 0.f : -m_run[qi];
             float p[NPG][4];
-            float psum = 0.f;
 #pragma unroll
             for (int e = 0; e < NPG; ++e)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[e][i] = __builtin_amdgcn_exp2f(x[e][i] - m_ref);
-                    psum += p[e][i];
-                }
-            l_run[qi] = l_run[qi] * alpha + psum;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                o[qi][dt][0] *= alpha; o[qi][dt][1] *= alpha; o[qi][dt][2] *= alpha; o[qi][dt][3] *= alpha;
-            }
+                for (int i = 0; i < 4; ++i) p[e][i] = __builtin_amdgcn_exp2f(fmaf(sa[qi][e][i], scale_log2, neg_m));
 #pragma unroll
             for (int hk = 0; hk < NPG / 2; ++hk)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     pb[qi][hk][j] = f2bf2(p[2 * hk + (j >> 1)][2 * (j & 1)], p[2 * hk + (j >> 1)][2 * (j & 1) + 1]);
         }
-        // O^T += V^T P^T over 32-key slices, P as bfloat16; each V^T fragment feeds every tile
+        // O^T += V^T P^T over 32-key slices, P as bfloat16; each V^T fragment feeds every tile, and the
+        // all-ones operand accumulates the row sums from the same P
 #pragma unroll
         for (int hk = 0; hk < NPG / 2; ++hk) {
-            if (ts + 32 * hk >= t1) break;
+            if (TAIL && ts + 32 * hk >= t1) break;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
-                const int d = dt * 16 + r;
-                const u32x2 va = *(const u32x2*)(sv + ((2 * hk) * D + d) * TA_VLD + 4 * g);
-                const u32x2 vb = *(const u32x2*)(sv + ((2 * hk + 1) * D + d) * TA_VLD + 4 * g);
-                const u32x4 vf = u32x4{va[0], va[1], vb[0], vb[1]};
+                const u32x4 vf = ld16(sv + (hk * D + dt * 16 + r) * TA_SVLD + g * 8);
 #pragma unroll
                 for (int qi = 0; qi < QT; ++qi) o[qi][dt] = mfma16(vf, pb[qi][hk], o[qi][dt]);
             }
+#pragma unroll
+            for (int qi = 0; qi < QT; ++qi) o[qi][8] = mfma16(ones, pb[qi][hk], o[qi][8]);
         }
-    }
+    };
+    if (t0 < t1) prefetch(t0);
+    int ts = t0;
+    for (; ts + TA_SUB <= t1; ts += TA_SUB) round(ts, std::false_type{});
+    if (ts < t1) round(ts, std::true_type{});
 #pragma unroll
     for (int qi = 0; qi < QT; ++qi) {
         const int tile = tile0 + qi;
-        float l_tot = l_run[qi];
-        l_tot += __shfl_xor(l_tot, 16, 64);
-        l_tot += __shfl_xor(l_tot, 32, 64);
         if (tile >= tiles) continue;
         const size_t base = ((((size_t)b * tiles + tile) * nq + h) * n_chunks + c) * 16 + r;
         float* op = opart + base * D;
@@ -408,7 +432,7 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
             *(float4*)(op + dt * 16 + 4 * g) = make_float4(o[qi][dt][0], o[qi][dt][1], o[qi][dt][2], o[qi][dt][3]);
         if (g == 0) {
             mlpart[base * 2 + 0] = m_run[qi];
-            mlpart[base * 2 + 1] = l_tot;
+            mlpart[base * 2 + 1] = o[qi][8][0];
         }
     }
 }
