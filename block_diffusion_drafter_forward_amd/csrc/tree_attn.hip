@@ -48,15 +48,25 @@ TreePlan plan_tree(int batch, int max_tokens, int nq, int nkv, int max_ctx) {
     p.chunks = 0;
     p.chunk_tokens = 0;
     if (max_ctx > 0) {
+        // One eight-wave workgroup per CU (the kernel's registers allow no second), so a grid runs in
+        // generations of 256 workgroups.  Pick the chunk count that minimises generations x (rounds per
+        // chunk + about one round of per-workgroup start-up), plus a small charge per chunk for the merge.
         const int units = batch * p.stiles * nkv;
-        int want = (512 + units - 1) / units;
         const int max_chunks = (max_ctx + TA_SUB - 1) / TA_SUB;
-        want = want < 1 ? 1 : (want > max_chunks ? max_chunks : want);
-        int ct = (max_ctx + want - 1) / want;
-        ct = (ct + TA_SUB - 1) / TA_SUB * TA_SUB;
-        if (ct > 16 * TA_MAX_PAGES) ct = 16 * TA_MAX_PAGES;
-        p.chunk_tokens = ct;
-        p.chunks = (max_ctx + ct - 1) / ct;
+        double best = 1e30;
+        for (int want = 1; want <= max_chunks; ++want) {
+            int ct = (max_ctx + want - 1) / want;
+            ct = (ct + TA_SUB - 1) / TA_SUB * TA_SUB;
+            if (ct > 16 * TA_MAX_PAGES) continue;
+            const int chunks = (max_ctx + ct - 1) / ct;
+            const long wgs = (long)units * chunks;
+            const double cost = (double)((wgs + 255) / 256) * (ct / TA_SUB + 1.2) + 0.1 * chunks;
+            if (cost < best - 1e-9) {
+                best = cost;
+                p.chunk_tokens = ct;
+                p.chunks = chunks;
+            }
+        }
     }
     const size_t T = (size_t)p.tiles * 16;
     size_t off = 256;  // error word
