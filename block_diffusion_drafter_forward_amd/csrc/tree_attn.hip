@@ -5,9 +5,9 @@
 // is its depth, i.e. absolute position ctx_len + depth.
 //
 // Three launches:
-//   tree_prep       per 16 tokens: depth and root-to-token ancestor list from the parent links (walked in
-//                   LDS), and RoPE of q and the tree k at ctx_len + depth (cos / sin per depth from an LDS
-//                   table), rounded to bfloat16
+//   tree_prep       per 16 tokens and group of eight heads: depth and (first group) root-to-token ancestor
+//                   list from the parent links (walked in LDS), and RoPE of the group's q / k rows at
+//                   ctx_len + depth (cos / sin per depth from an LDS table), rounded to bfloat16
 //   tree_ctx_bf16   the context part, MFMA: one workgroup per (16-token tile, KV head, context chunk,
 //                   request), one wave per query head of the KV group; 64-key rounds staged in LDS as in the
 //                   drafter's attention.  The KV head is the fastest grid index, so with 8 KV heads (or a
@@ -30,13 +30,15 @@ namespace df {
 // slots, [g][page 2 hk + pp][4 slots] (g = slot / 4), so that a lane's V^T operand (slots 4g..4g+3 of both
 // pages) is one aligned 16-byte read; rows padded to 80 bytes.
 #define TA_SVLD (32 + 8)
-#define TA_RESCALE 8.0f  // log2 growth of a row maximum before the running reference is raised
+#define TA_RESCALE 8.0f
+#define TP_HEADS 8  // heads whose rows one tree_prep workgroup rotates (16 tokens x 8 heads: one round trip)
+#define TM_BATCH 8  // context chunks (and ancestor keys) whose loads tree_merge keeps in flight together  // log2 growth of a row maximum before the running reference is raised
 
 static size_t ta_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Waves per context workgroup: the G query heads of a KV head times TA_WAVES / G wave slots, each slot
 // TA_QT token tiles, all served by the same staged K/V.  Two tiles per wave make every K (V) fragment read
-// from LDS feed two MFMAs: the kernel is bound by LDS reads, not by the matrix cores.
+// from LDS feed two MFMAs (with one tile per wave, LDS reads bounded the kernel).
 #define TA_WAVES 8
 #define TA_QT 2
 
@@ -132,17 +134,19 @@ __global__ __launch_bounds__(256) void tree_prep(int T, const int32_t* __restric
             }
             if (bad) set_err(err, DFLASH_DEVERR_TREE);
             depth = len;
-            // second walk: the path from the token up, stored root first
-            a[1] = 0;
-            cur = i;
-            for (int j = len; j >= 1; --j) {
-                a[1 + j] = cur;
-                int p = spar[cur];
-                cur = (p < 0 || p >= cur) ? 0 : p;
+            // second walk (head group 0 only): the path from the token up, stored root first
+            if (blockIdx.z == 0) {
+                a[1] = 0;
+                cur = i;
+                for (int j = len; j >= 1; --j) {
+                    a[1 + j] = cur;
+                    int p = spar[cur];
+                    cur = (p < 0 || p >= cur) ? 0 : p;
+                }
             }
             atomicMax(&smaxdep, depth);
         }
-        a[0] = depth;
+        if (blockIdx.z == 0) a[0] = depth;
         sdep[t] = depth;
     }
     __syncthreads();
@@ -156,9 +160,10 @@ __global__ __launch_bounds__(256) void tree_prep(int T, const int32_t* __restric
         scs[dep][pr][1] = s;
     }
     __syncthreads();
-    // RoPE of the tile's rows (16 tokens x (nq + nkv) heads): eight lanes per row, lane j rotating the pairs
-    // (8j + e, 64 + 8j + e), e < 8, from two 16-byte loads; four rows in flight per lane
-    const int hh = nq + nkv, rows = 16 * hh;
+    // RoPE of the tile's rows for this workgroup's group of TP_HEADS heads (16 tokens x up to TP_HEADS heads):
+    // eight lanes per row, lane j rotating the pairs (8j + e, 64 + 8j + e), e < 8, from two 16-byte loads;
+    // four rows in flight per lane, i.e. every row of the group in one round trip
+    const int hh = nq + nkv, h0 = blockIdx.z * TP_HEADS, nh = min(TP_HEADS, hh - h0), rows = 16 * nh;
     const int sub = t & 7, slot = t >> 3;  // 32 row slots per pass
     for (int r0 = 0; r0 < rows; r0 += 32 * 4) {
         u32x4 x1[4], x2[4];
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(256) void tree_prep(int T, const int32_t* __restric
         for (int u = 0; u < 4; ++u) {
             const int row = r0 + u * 32 + slot;
             rr[u] = row;
-            const int tok = row / hh, h = row - tok * hh;
+            const int tok = row / nh, h = h0 + row - tok * nh;
             const bool ok = row < rows && sdep[min(tok, 15)] >= 0;
             const bool isq = h < nq;
             const bf16_t* src = isq ? q + (((size_t)b * T + i0 + tok) * nq + h) * TA_D
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(256) void tree_prep(int T, const int32_t* __restric
         for (int u = 0; u < 4; ++u) {
             const int row = rr[u];
             if (row >= rows) break;
-            const int tok = row / hh, h = row - tok * hh;
+            const int tok = row / nh, h = h0 + row - tok * nh;
             const int dep = sdep[tok];
             const bool isq = h < nq;
             bf16_t* dst = isq ? qr + (((size_t)b * Tpad + i0 + tok) * nq + h) * TA_D
@@ -465,8 +470,11 @@ __global__ __launch_bounds__(256) void tree_merge(int T, int Tpad, int tiles, in
     const int G = nq / nkv;
     const int hs = lane >> 4, dl = lane & 15;
     const int32_t* a = anc + ((size_t)b * Tpad + i) * TREE_MAX_ANC;
+    // the depth and the ancestor list in one round trip (lane e: the e-th entry, read whatever the depth)
     const int depth = a[0];
+    const int anc_e = a[1 + min(lane, TREE_MAX_ANC - 2)];
     if (depth < 0) return;
+    const int my_anc = lane <= depth ? anc_e : 0;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)TA_D);
     const int tile = i >> 4, row = i & 15;
     for (int hg = 0; hg < G; hg += 4) {
@@ -488,18 +496,18 @@ __global__ __launch_bounds__(256) void tree_merge(int T, int Tpad, int tiles, in
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.f;
         const size_t cbase = (((size_t)b * tiles + tile) * nq + h) * n_chunks;
-        for (int c0 = 0; c0 < n_chunks; c0 += 4) {  // four chunks' loads in flight at a time
-            float2 mlc[4];
-            float4 oc0[4], oc1[4];
+        for (int c0 = 0; c0 < n_chunks; c0 += TM_BATCH) {  // TM_BATCH chunks' loads in flight at a time
+            float2 mlc[TM_BATCH];
+            float4 oc0[TM_BATCH], oc1[TM_BATCH];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < TM_BATCH; ++u) {
                 const size_t base = (cbase + min(c0 + u, n_chunks - 1)) * 16 + row;
                 mlc[u] = *(const float2*)(mlpart + base * 2);
                 oc0[u] = *(const float4*)(opart + base * TA_D + 8 * dl);
                 oc1[u] = *(const float4*)(opart + base * TA_D + 8 * dl + 4);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < TM_BATCH; ++u) {
                 const float mc = mlc[u].x, lc = mlc[u].y;
                 if (c0 + u >= n_chunks || mc == -INFINITY) continue;
                 const float mn = fmaxf(m, mc);
@@ -511,18 +519,17 @@ __global__ __launch_bounds__(256) void tree_merge(int T, int Tpad, int tiles, in
                 m = mn;
             }
         }
-        // the token's ancestors and itself, root first: lane e holds the e-th, four keys in flight at a time
-        const int my_anc = lane <= depth ? a[1 + lane] : 0;
-        for (int e0 = 0; e0 <= depth; e0 += 4) {
-            u32x4 ku[4], vu[4];
+        // the token's ancestors and itself, root first: lane e holds the e-th, TM_BATCH keys in flight at a time
+        for (int e0 = 0; e0 <= depth; e0 += TM_BATCH) {
+            u32x4 ku[TM_BATCH], vu[TM_BATCH];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < TM_BATCH; ++u) {
                 const int tok = __shfl(my_anc, min(e0 + u, depth), 64);
                 ku[u] = ld16(kr + (((size_t)b * Tpad + tok) * nkv + kvh) * TA_D + 8 * dl);
                 vu[u] = ld16(v + (((size_t)b * T + tok) * nkv + kvh) * TA_D + 8 * dl);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < TM_BATCH; ++u) {
                 if (e0 + u > depth) break;  // uniform
                 float s = 0.f;
 #pragma unroll
@@ -569,7 +576,8 @@ hipError_t launch_tree_attention(const TreePlan& p, int batch, int T, const int3
     const int Tpad = p.tiles * 16;
     hipError_t e = launch_clear_err(err, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(tree_prep, dim3(p.tiles, batch), dim3(256), 0, st, T, n_tokens, parent, nq, nkv,
+    hipLaunchKernelGGL(tree_prep, dim3(p.tiles, batch, (nq + nkv + TP_HEADS - 1) / TP_HEADS), dim3(256), 0, st, T,
+                       n_tokens, parent, nq, nkv,
                        (const bf16_t*)q, (const bf16_t*)k, ctx_len, max_ctx, rf, qr, kr, anc, Tpad, err);
     if (p.chunks > 0) {
         const dim3 grid(nkv * p.stiles * p.chunks * batch);
