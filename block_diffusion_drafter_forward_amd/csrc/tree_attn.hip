@@ -30,9 +30,9 @@ namespace df {
 // slots, [g][page 2 hk + pp][4 slots] (g = slot / 4), so that a lane's V^T operand (slots 4g..4g+3 of both
 // pages) is one aligned 16-byte read; rows padded to 80 bytes.
 #define TA_SVLD (32 + 8)
-#define TA_RESCALE 8.0f
-#define TP_HEADS 8  // heads whose rows one tree_prep workgroup rotates (16 tokens x 8 heads: one round trip)
-#define TM_BATCH 8  // context chunks (and ancestor keys) whose loads tree_merge keeps in flight together  // log2 growth of a row maximum before the running reference is raised
+#define TA_RESCALE 8.0f  // log2 growth of a row maximum before the running reference is raised
+#define TP_HEADS 8        // heads whose rows one tree_prep workgroup rotates (16 tokens x 8 heads: one round trip)
+#define TM_BATCH 8        // context chunks (and ancestor keys) whose loads tree_merge keeps in flight together
 
 static size_t ta_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -51,10 +51,13 @@ TreePlan plan_tree(int batch, int max_tokens, int nq, int nkv, int max_ctx) {
     p.chunk_tokens = 0;
     if (max_ctx > 0) {
         // One eight-wave workgroup per CU (the kernel's registers allow no second), so a grid runs in
-        // generations of 256 workgroups.  Pick the chunk count that minimises generations x (rounds per
-        // chunk + about one round of per-workgroup start-up), plus a small charge per chunk for the merge.
+        // generations of 256 workgroups.  Pick the chunk count that minimises the estimated time (measured on
+        // MI355X): generations x (rounds per chunk + about one round of start-up) x 2.8 us, plus each chunk's
+        // float32 (m, l, O) partials written and read back by the merge at ~5 TB/s, plus one merge round trip
+        // (~1.5 us) per TM_BATCH chunks.
         const int units = batch * p.stiles * nkv;
         const int max_chunks = (max_ctx + TA_SUB - 1) / TA_SUB;
+        const double part_us = (double)batch * p.tiles * nq * 16 * (TA_D + 2) * 4 * 2 / 5.0e6;  // per chunk
         double best = 1e30;
         for (int want = 1; want <= max_chunks; ++want) {
             int ct = (max_ctx + want - 1) / want;
@@ -62,7 +65,8 @@ TreePlan plan_tree(int batch, int max_tokens, int nq, int nkv, int max_ctx) {
             if (ct > 16 * TA_MAX_PAGES) continue;
             const int chunks = (max_ctx + ct - 1) / ct;
             const long wgs = (long)units * chunks;
-            const double cost = (double)((wgs + 255) / 256) * (ct / TA_SUB + 1.2) + 0.1 * chunks;
+            const double cost = 2.8 * (double)((wgs + 255) / 256) * (ct / TA_SUB + 1.2) + chunks * part_us +
+                                1.5 * ((chunks + TM_BATCH - 1) / TM_BATCH);
             if (cost < best - 1e-9) {
                 best = cost;
                 p.chunk_tokens = ct;
