@@ -64,14 +64,14 @@ AttnPlan plan_attention(int batch, int n_q, int n_kv, int max_ctx, int n_layers)
 // bfloat16.  The block's keys are attended first (every pair of hi / lo terms), from operands each lane
 // loads itself at the start, so they add no staging round: chunk 0 then takes as many rounds as the
 // other chunks, and its block step overlaps the wait for its first context round.
-#define AT_KLD (128 + 8)  // padded LDS row of a key (elements): 16 consecutive keys hit distinct banks
+#define AT_KPAD 8  // padding of an LDS key row (elements), so that 16 consecutive keys spread over the banks
 // Values in LDS: one row per (32-key slice hk, d) holding the slice's two pages interleaved by groups of four
 // slots, [g][page 2 hk + pp][4 slots] (g = slot / 4), so that the 16 bytes a lane needs for the V^T operand
 // (slots 4g..4g+3 of both pages) are one aligned LDS read; rows padded to 80 bytes spread a wave's reads over
 // the banks.
 #define AT_SVLD (32 + 8)
 
-template <int G, int SUB, bool NTKV>
+template <int G, int SUB, bool NTKV, int D>
 __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kb,
                                                     const bf16_t* __restrict__ vbt, const bf16_t* __restrict__ kpool,
                                                     const bf16_t* __restrict__ vpool, int layer, int n_pages,
@@ -80,12 +80,18 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
                                                     int chunk_tokens, int L, int nq, int nkv,
                                                     float* __restrict__ opart, float* __restrict__ mlpart,
                                                     uint32_t* err) {
-    constexpr int D = 128;
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
     constexpr int NT = 64 * G;
     constexpr int NPG = SUB / 16;        // pages per sub-chunk
-    constexpr int PIECES = NPG * 512;    // 16-byte pieces per sub-chunk: per page 256 of K and 256 of V^T
-    constexpr int PPT = PIECES / NT;
-    __shared__ __attribute__((aligned(16))) bf16_t sk[SUB * AT_KLD];
+    constexpr int KS = D / 32;           // 32-wide k-steps of q . k
+    constexpr int DT = D / 16;           // 16-row d-tiles of the output
+    constexpr int KLD = D + AT_KPAD;     // LDS key row (elements)
+    constexpr int PG_PIECES = 4 * D;     // 16-byte pieces per page: 2 D of K, then 2 D of V^T
+    // pieces per page per thread; with more threads than pieces (eight heads per KV head at d = 64) the first
+    // PG_PIECES threads move every page and the rest stage nothing
+    constexpr int PPP = PG_PIECES >= NT ? PG_PIECES / NT : 1;
+    constexpr int PPT = NPG * PPP;
+    __shared__ __attribute__((aligned(16))) bf16_t sk[SUB * KLD];
     __shared__ __attribute__((aligned(16))) bf16_t sv[(NPG / 2) * D * AT_SVLD];
     __shared__ int spg[AT_MAX_PAGES];
     const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -112,17 +118,17 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the page-id loads ahead of the q loads
     // Q^T operand: lane supplies query row r (zero beyond L), eight d-values per 32-wide k-step
-    u32x4 qf[4], ql[4];
+    u32x4 qf[KS], ql[KS];
     {
         const bool ok = r < L;
         const bf16_t* qp = q + ((size_t)(b * L + (ok ? r : 0)) * nq + h) * D + g * 8;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < KS; ++s) {
             qf[s] = ld16(qp + s * 32);  // unconditional loads (row 0 for rows past L), zeroed below
             ql[s] = ld16(qp + qplane + s * 32);
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int w4 = 0; w4 < 4; ++w4) {
                 qf[s][w4] = ok ? qf[s][w4] : 0u;
@@ -137,17 +143,17 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
     }
     // chunk 0: the block's K operand (lane: key slot r, d = 32 s + 8 g ..) and V^T operand (lane: d = 16 dt + r,
     // slots 4 g .. 4 g + 3), hi and lo planes
-    u32x4 bk[2][4];
-    u32x2 bv[2][8];
+    u32x4 bk[2][KS];
+    u32x2 bv[2][DT];
     if (c == 0) {
         const bf16_t* kr = kb + (((size_t)b * nkv + kvh) * 16 + r) * D + g * 8;
         const bf16_t* vr = vbt + ((size_t)b * nkv + kvh) * page_elems + (size_t)r * 16 + 4 * g;
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) bk[pl][s] = ld16(kr + pl * bplane + s * 32);
+            for (int s = 0; s < KS; ++s) bk[pl][s] = ld16(kr + pl * bplane + s * 32);
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) bv[pl][dt] = *(const u32x2*)(vr + pl * bplane + (size_t)dt * 16 * 16);
+            for (int dt = 0; dt < DT; ++dt) bv[pl][dt] = *(const u32x2*)(vr + pl * bplane + (size_t)dt * 16 * 16);
         }
     }
 
@@ -165,10 +171,9 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
     const int R = t0 < t1 ? (t1 - t0 + SUB - 1) / SUB : 0;  // context rounds of this workgroup
     auto ts_of = [&](int rr) { return t0 + rr * SUB; };
 
-    // Staging: a page is 512 16-byte pieces (256 of K, then 256 of V^T), and piece j of either half sits at
+    // Staging: a page is 4 D 16-byte pieces (2 D of K, then 2 D of V^T), and piece j of either half sits at
     // element 8 j of its page, so thread tid moves pieces tid, tid + NT, ... of every page of the sub-chunk:
     // the per-thread offsets are compile-time constants and only the page bases change per sub-chunk.
-    constexpr int PPP = 512 / NT;  // pieces per page per thread
     u32x4 pf[PPT];
     uint32_t okm = 0u;
     // Page slot e of the sub-chunk starting at key ts: its K and V^T bases always name readable memory (an
@@ -190,7 +195,8 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
 #pragma unroll
             for (int u = 0; u < PPP; ++u) {
                 const int qq = tid + u * NT;
-                const bf16_t* src = (qq < 256 ? kbase : vbase) + (qq & 255) * 8;
+                if (PG_PIECES < NT && qq >= PG_PIECES) continue;  // (eight heads at d = 64: an idle thread)
+                const bf16_t* src = (qq < 2 * D ? kbase : vbase) + (qq & (2 * D - 1)) * 8;
                 pf[e * PPP + u] = NTKV ? ld16_nt(src) : ld16(src);
             }
         }
@@ -206,12 +212,13 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
 #pragma unroll
             for (int u = 0; u < PPP; ++u) {
                 const int qq = tid + u * NT;
+                if (PG_PIECES < NT && qq >= PG_PIECES) continue;
                 u32x4 v = pf[e * PPP + u];
                 if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-                if (qq < 256) {
-                    *(u32x4*)(sk + (e * 16 + (qq >> 4)) * AT_KLD + (qq & 15) * 8) = v;
+                if (qq < 2 * D) {  // key row qq / (D / 8), pieces of 8 elements
+                    *(u32x4*)(sk + (e * 16 + qq / (D / 8)) * KLD + (qq % (D / 8)) * 8) = v;
                 } else {
-                    const int q2 = qq - 256;
+                    const int q2 = qq - 2 * D;
                     if (nvalid < 16) {
                         // zero the values of slots past the last key (they may hold anything)
                         const int half = q2 & 1;
@@ -233,9 +240,9 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
     };
 
 
-    f32x4 o[8];
+    f32x4 o[DT];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
     __syncthreads();  // page ids in LDS
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < KS; ++s) {
                 sa = mfma16(bk[pl][s], qf[s], sa);
                 sa = mfma16(bk[pl][s], ql[s], sa);
             }
@@ -292,7 +299,7 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
+            for (int dt = 0; dt < DT; ++dt) {
                 const u32x2 v = bv[t >> 1][dt];
                 o[dt] = mfma16(u32x4{v[0] & vm[0], v[1] & vm[1], 0u, 0u}, (t & 1) ? plo : phi, o[dt]);
             }
@@ -316,10 +323,10 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
             sl[e] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int e = 0; e < NPG; ++e) {
-                const u32x4 kf = ld16(sk + (e * 16 + r) * AT_KLD + g * 8 + s * 32);
+                const u32x4 kf = ld16(sk + (e * 16 + r) * KLD + g * 8 + s * 32);
                 sh[e] = mfma16(kf, qf[s], sh[e]);
                 sl[e] = mfma16(kf, ql[s], sl[e]);
             }
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
             }
         l_run = l_run * alpha + psum;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
+        for (int dt = 0; dt < DT; ++dt) {
             o[dt][0] *= alpha; o[dt][1] *= alpha; o[dt][2] *= alpha; o[dt][3] *= alpha;
         }
         // O^T += V^T P^T over the sub-chunk's 32-key slices; P enters as two bfloat16 terms (hi + lo)
@@ -375,7 +382,7 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
             // four d-tiles' operands at a time, then their MFMAs term by term (independent accumulators back to
             // back; each tile still adds its terms in the same order)
 #pragma unroll
-            for (int d0 = 0; d0 < 8; d0 += 4) {
+            for (int d0 = 0; d0 < DT; d0 += 4) {
                 u32x4 vf[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) vf[u] = ld16(sv + (hk * D + (d0 + u) * 16 + r) * AT_SVLD + g * 8);
@@ -393,7 +400,7 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
     const size_t base = (((size_t)b * nq + h) * C1 + c) * 16 + r;
     float* op = opart + base * D;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
         *(float4*)(op + dt * 16 + 4 * g) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
     if (g == 0) {
         mlpart[base * 2 + 0] = m_run;
@@ -406,7 +413,8 @@ __global__ __launch_bounds__(64 * G, 2) void attn_bf16(const bf16_t* __restrict_
 // ------------------------------------------------------------------------------------------------------
 // One wave per (request, query head, block row): lanes first combine the chunks' (m, l) in the log2 domain,
 // then each lane accumulates two of the 128 output columns over the chunks in a fixed order.
-template <typename T>
+// TWO: two output columns per lane (d = 128: lane and lane + 64), else one (d = 64).
+template <typename T, bool TWO>
 __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ opart, const float* __restrict__ mlpart,
                                                   int B, int L, int nq, int d, int C1, T* __restrict__ o) {
     __shared__ float wsh[4][64];
@@ -438,13 +446,13 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ opar
         for (int i = 0; i < cn; ++i) {
             const float wi = wsh[w][i];
             acc0 += wi * op[(size_t)i * 16 * d + lane];
-            acc1 += wi * op[(size_t)i * 16 * d + lane + 64];
+            if (TWO) acc1 += wi * op[(size_t)i * 16 * d + lane + 64];
         }
         __builtin_amdgcn_wave_barrier();
     }
     lsum = wave_sum(lsum);
     put_act(o, plane, base_o + lane, acc0 / lsum);
-    put_act(o, plane, base_o + lane + 64, acc1 / lsum);
+    if (TWO) put_act(o, plane, base_o + lane + 64, acc1 / lsum);
 }
 
 // Float32 drafters: one wave per (block row, query head, request); lanes take keys round-robin with their
@@ -525,16 +533,20 @@ hipError_t launch_attention(int bf16, const AttnPlan& p, int B, int L, int nq, i
     if (bf16) {
         const int G = nq / nkv;
         const dim3 grid(attn_slots(p), nkv, B);
-        if (p.chunk_tokens % attn_sub(G) || p.chunk_tokens > 16 * AT_MAX_PAGES) return hipErrorInvalidValue;
-#define DF_ATTN_NT(GG, NT)                                                                                         \
-    DF_LAUNCH((attn_bf16<GG, 64, NT>), grid, dim3(64 * GG), 0, st, (const bf16_t*)q, (const bf16_t*)kb,        \
+        if (p.chunk_tokens % attn_sub(G) || p.chunk_tokens > 16 * AT_MAX_PAGES || (d != 64 && d != 128))
+            return hipErrorInvalidValue;
+#define DF_ATTN_NT(GG, NT, DD)                                                                                     \
+    DF_LAUNCH((attn_bf16<GG, 64, NT, DD>), grid, dim3(64 * GG), 0, st, (const bf16_t*)q, (const bf16_t*)kb,    \
               (const bf16_t*)vbt, (const bf16_t*)kpool, (const bf16_t*)vpool, layer, n_pages, page_table,       \
               max_pages, ctx_len, max_ctx, p.chunk_tokens, L, nq, nkv, opart, mlpart, err)
-#define DF_ATTN(GG)                 \
-    if (p.stream_kv)                \
-        DF_ATTN_NT(GG, true);       \
-    else                            \
-        DF_ATTN_NT(GG, false)
+#define DF_ATTN(GG)                                       \
+    if (d == 64) {                                        \
+        if (p.stream_kv) DF_ATTN_NT(GG, true, 64);        \
+        else DF_ATTN_NT(GG, false, 64);                   \
+    } else {                                              \
+        if (p.stream_kv) DF_ATTN_NT(GG, true, 128);       \
+        else DF_ATTN_NT(GG, false, 128);                  \
+    }
         switch (G) {
             case 1: DF_ATTN(1); break;
             case 2: DF_ATTN(2); break;
@@ -555,14 +567,24 @@ hipError_t launch_attention(int bf16, const AttnPlan& p, int B, int L, int nq, i
 
 hipError_t launch_attn_merge(int bf16, const AttnPlan& p, int B, int L, int nq, int d, const float* opart,
                              const float* mlpart, void* o, hipStream_t st) {
-    const long n = (long)B * L * nq;  // one wave each (d == 128)
+    const long n = (long)B * L * nq;  // one wave each (d = 64 or 128)
     const dim3 grid((unsigned)((n + 3) / 4));
-    if (bf16)
-        hipLaunchKernelGGL(attn_merge<bf16_t>, grid, dim3(256), 0, st, opart, mlpart, B, L, nq, d, attn_slots(p),
-                           (bf16_t*)o);
-    else
-        hipLaunchKernelGGL(attn_merge<float>, grid, dim3(256), 0, st, opart, mlpart, B, L, nq, d, attn_slots(p),
-                           (float*)o);
+    if (d != 64 && d != 128) return hipErrorInvalidValue;
+    if (bf16) {
+        if (d == 128)
+            hipLaunchKernelGGL((attn_merge<bf16_t, true>), grid, dim3(256), 0, st, opart, mlpart, B, L, nq, d,
+                               attn_slots(p), (bf16_t*)o);
+        else
+            hipLaunchKernelGGL((attn_merge<bf16_t, false>), grid, dim3(256), 0, st, opart, mlpart, B, L, nq, d,
+                               attn_slots(p), (bf16_t*)o);
+    } else {
+        if (d == 128)
+            hipLaunchKernelGGL((attn_merge<float, true>), grid, dim3(256), 0, st, opart, mlpart, B, L, nq, d,
+                               attn_slots(p), (float*)o);
+        else
+            hipLaunchKernelGGL((attn_merge<float, false>), grid, dim3(256), 0, st, opart, mlpart, B, L, nq, d,
+                               attn_slots(p), (float*)o);
+    }
     return hipGetLastError();
 }
 

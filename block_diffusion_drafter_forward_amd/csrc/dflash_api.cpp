@@ -127,7 +127,7 @@ static int validate_config(const dflash_config* c) {
     if (!(c->rms_eps >= 0.f) || !(c->rope_theta >= 0.f)) return fail(DFLASH_E_ARG, "rms_eps and rope_theta must be >= 0");
     const int qd = c->n_q_heads * c->head_dim;
     if (is_bf16(*c)) {
-        if (c->head_dim != 128) return fail(DFLASH_E_UNSUPPORTED, "bf16 kernels need head_dim 128");
+        if (c->head_dim != 64 && c->head_dim != 128) return fail(DFLASH_E_UNSUPPORTED, "bf16 kernels need head_dim 64 or 128");
         if (c->hidden % 256 || c->ffn % 256 || c->feat_dim % 256 || qd % 256)
             return fail(DFLASH_E_UNSUPPORTED, "bf16 kernels need hidden, ffn, feat_dim, n_q*d multiples of 256");
     } else {

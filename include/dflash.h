@@ -79,7 +79,7 @@ typedef struct {
     int hidden;         /* drafter hidden size H = width of the fused feature                              */
     int n_q_heads;      /* query heads                                                                      */
     int n_kv_heads;     /* key/value heads; n_q_heads % n_kv_heads == 0 (grouped-query attention)           */
-    int head_dim;       /* d: bf16 needs 128; f32 allows even d <= 128                                      */
+    int head_dim;       /* d: bf16 needs 64 or 128; f32 allows even d <= 128                                */
     int ffn;            /* SwiGLU width                                                                     */
     int vocab;          /* V of the shared embedding and LM head                                            */
     int feat_dim;       /* width of the concatenated target hidden states (n_feature_layers * H_target)     */
@@ -133,7 +133,7 @@ typedef struct {
 typedef struct dflash_handle dflash_handle;
 
 /* Create a handle for a drafter.  Validates the config (no HIP call is made).  Supported: dtype BF16 with
- * head_dim 128, hidden/ffn/feat_dim/n_q*d multiples of 256; dtype F32 with even head_dim <= 128 and
+ * head_dim 64 or 128, hidden/ffn/feat_dim/n_q*d multiples of 256; dtype F32 with even head_dim <= 128 and
  * hidden/ffn/feat_dim/n_q*d multiples of 4; 2 <= L <= 16; page_size 16; n_q/n_kv <= 8.
  * Returns DFLASH_OK and *out, or an error status (and *out = NULL).                                       */
 int dflash_create(const dflash_config *cfg, const dflash_weights *w, dflash_handle **out);

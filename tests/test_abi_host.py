@@ -66,14 +66,16 @@ def _create(D, shape, bad=None):
 
 def test_create_accepts_supported_shapes(D):
     import workloads as W
-    for s in (W.TINY, W.QWEN3_8B, W.LLAMA31_8B, W.SMALL_FP32, W.SMALL_GQA8):
+    for s in (W.TINY, W.QWEN3_8B, W.LLAMA31_8B, W.SMALL_FP32, W.SMALL_GQA8, W.SMALL_BF16_D64, W.SMALL_GQA8_D64,
+              W.SMALL_MHA_D64):
         m = _create(D, s)
         assert m.handle
         m.close()
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(head_dim=64), -4),
+    (dict(head_dim=96), -4),  # bfloat16 kernels: head_dim 64 or 128
+    (dict(head_dim=32), -4),
     (dict(n_q_heads=7), -2),
     (dict(n_q_heads=32, n_kv_heads=2), -4),
     (dict(block_len=17), -4),

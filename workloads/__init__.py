@@ -311,6 +311,12 @@ SMALL_GQA8 = DrafterShape(n_layers=1, hidden=256, n_q_heads=8, n_kv_heads=1, hea
                           vocab=1000, feat_layers=2, target_hidden=256, block_len=12, rope_theta=1e4)
 SMALL_FP32 = DrafterShape(n_layers=2, hidden=128, n_q_heads=4, n_kv_heads=1, head_dim=32, ffn=200,
                           vocab=777, feat_layers=2, target_hidden=96, block_len=5, rope_theta=1e4, bf16=False)
+# head_dim 64 in bfloat16: four, eight and one query heads per KV head
+SMALL_BF16_D64 = dataclasses.replace(SMALL_BF16, head_dim=64)
+SMALL_GQA8_D64 = DrafterShape(n_layers=1, hidden=256, n_q_heads=8, n_kv_heads=1, head_dim=64, ffn=512,
+                              vocab=1000, feat_layers=2, target_hidden=256, block_len=12, rope_theta=1e4)
+SMALL_MHA_D64 = DrafterShape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=4, head_dim=64, ffn=768,
+                             vocab=2053, feat_layers=2, target_hidden=256, block_len=16, rope_theta=1e6)
 
 SMALL = [
     Workload(100, "small-bf16-b1", SMALL_BF16, 1, 100, None, False, 0.8, None),
@@ -332,6 +338,10 @@ SMALL = [
     # the optional fusion bias ([DF] §3.4.3 "Feature fusion": the projection may carry one)
     Workload(111, "small-bf16-bias-b2", SMALL_BF16, 2, None, (1, 300), True, None, (0.6, 0.95), fc_bias=True),
     Workload(112, "small-fp32-bias-b1", SMALL_FP32, 1, 37, None, True, 0.9, None, top_k=3, fc_bias=True),
+    # head_dim 64 (bfloat16): paged ragged contexts; eight query heads per KV head; plain multi-head attention
+    Workload(113, "small-bf16-d64-b2", SMALL_BF16_D64, 2, None, (1, 300), True, None, (0.6, 0.95)),
+    Workload(114, "small-gqa8-d64-b2", SMALL_GQA8_D64, 2, None, (1, 150), True, 0.7, None, top_k=5),
+    Workload(115, "small-mha-d64-b1", SMALL_MHA_D64, 1, 200, None, True, 0.8, None),
 ]
 
 # Full-size parity cases beyond the five benchmark configurations (expected values in tests/golden/): the
