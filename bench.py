@@ -686,7 +686,7 @@ def main():
         sweep_block(args)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the drafter pass has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -1,7 +1,7 @@
 """Write the oracle's expected outputs for the full-size workloads (tests/golden/expected_<name>.npz).
 
 Only the CPU oracle and the seeded input generator are used: the files hold what the fp64 oracle computes
-for each workload, so the GPU parity tests at full size need no heavy CPU work on the GPU machine.
+for each workload, so the GPU parity tests at full size need no heavy CPU work where they run.
 
 Stored per workload:
   tokens [B, L], topk_ids [B, L, 8], topk_logprobs [B, L, 8], lse [B, L], margin1 / margin8 [B, L]
