@@ -230,21 +230,25 @@ hipError_t launch_qkv_epilogue(int bf16, const float* part, int S, int B, int L,
 // ------------------------------------------------------------------------------------------------------
 // SwiGLU and plain reduce + cast
 // ------------------------------------------------------------------------------------------------------
+// Four consecutive columns per thread (F % 4 == 0 for every drafter the API accepts): 16-byte split loads
+// of gate and up, 8-byte stores per activation plane.
 template <typename T>
 __global__ __launch_bounds__(256) void swiglu(const float* __restrict__ part, int S, int M, int F,
                                               T* __restrict__ a) {
-    const int j = blockIdx.x * 256 + threadIdx.x, m = blockIdx.y;  // column, row (grid y)
+    const int j = (blockIdx.x * 256 + threadIdx.x) * 4, m = blockIdx.y;  // first column, row (grid y)
     if (j >= F) return;
-    const size_t idx = (size_t)m * F + j;
     const size_t N = 2 * (size_t)F;
-    const int col[2] = {j, F + j};
-    float sum[2];
-    split_sums<2>(part + (size_t)m * N, col, (size_t)M * N, S, sum);
-    put_act(a, (size_t)M * F, idx, swiglu_value(sum[0], sum[1]));
+    const float* pr = part + (size_t)m * N;
+    const float4 g = split_sum4(pr + j, (size_t)M * N, S);
+    const float4 u = split_sum4(pr + F + j, (size_t)M * N, S);
+    st4_act(a + (size_t)m * F + j, (size_t)M * F,
+            make_float4(swiglu_value(g.x, u.x), swiglu_value(g.y, u.y), swiglu_value(g.z, u.z),
+                        swiglu_value(g.w, u.w)));
 }
 
 hipError_t launch_swiglu(int bf16, const float* part, int S, int M, int F, void* a, hipStream_t st) {
-    const dim3 grid((unsigned)((F + 255) / 256), (unsigned)M);
+    if (F % 4) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((F / 4 + 255) / 256), (unsigned)M);
     if (bf16) hipLaunchKernelGGL(swiglu<bf16_t>, grid, dim3(256), 0, st, part, S, M, F, (bf16_t*)a);
     else hipLaunchKernelGGL(swiglu<float>, grid, dim3(256), 0, st, part, S, M, F, (float*)a);
     return hipGetLastError();
