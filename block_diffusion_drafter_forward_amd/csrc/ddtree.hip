@@ -539,6 +539,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk(const float* __restrict
 }
 
 #define TK_SLOTS_PT 8  // candidate slots each merge thread loads at once
+#define TK_BIN_MAX 64  // fullest bin the merge's counting sort takes (more: heavy ties, left to the sort)
+
+// Bin of key kk (>= tmax) in the merge's counting sort: descending keys, width 2^sh, bin 0 from kmax down.
+__device__ __forceinline__ int tk_cbin(uint32_t kk, uint32_t kmax, int sh, int nb) {
+    return kk >= kmax ? 0 : min(nb - 1, (int)((kmax - kk) >> sh));
+}
 
 __global__ __launch_bounds__(TK_THREADS) void topk_merge(const float* __restrict__ logits, int64_t stride, int V,
                                                           int K, int C, int CL, int capc,
@@ -550,6 +556,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge(const float* __restrict
     __shared__ int pcnt[64], poff[65];
     __shared__ int s_n, s_ovf;
     __shared__ float s_lse;
+    __shared__ uint32_t bcnt[TK_BINS], bcur[TK_BINS], wsum[TK_THREADS / 64], wocc[TK_THREADS / 64];
+    __shared__ uint32_t s_tmax, s_kmax;
     const int t = threadIdx.x, row = blockIdx.x;
     const float* x = logits + (size_t)row * stride;
     const uint2* cr = cand + (size_t)row * C * capc;
@@ -581,6 +589,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge(const float* __restrict
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) S += __shfl_xor(S, o, 64);
         const bool any_bad = __ballot(bad) != 0ull;
+        uint32_t tm = on ? __float_as_uint(q4.z) : 0u;  // the largest chunk threshold
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) tm = max(tm, (uint32_t)__shfl_xor((int)tm, o, 64));
         if (on) {
             pcnt[t] = cnt;
             ptc[t] = __float_as_uint(q4.z);
@@ -591,6 +602,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge(const float* __restrict
             s_n = (any_bad || total > TK_SORT_MAX || total < K) ? -1 : total;
             s_ovf = 0;
             s_lse = M + __logf(S);
+            s_tmax = tm;
+            s_kmax = max(order_key(M), tm);
         }
     }
     __syncthreads();
@@ -610,6 +623,70 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge(const float* __restrict
         }
     }
     __syncthreads();
+    {
+        // Counting sort of the candidates at or above tmax = the largest t_c, taken when at least K of them
+        // are: the K-th key T is then >= every t_c, so no chunk is read again, and every candidate below tmax
+        // ranks K or later.  Keys bin by (kmax - key) >> sh, so that bins run in descending key order; an
+        // entry's place is its bin's start plus the number of larger (key, ~id) pairs in its bin.  A bin of
+        // more than TK_BIN_MAX entries (heavy ties) or fewer than K such candidates leave the row to the sort.
+        const uint32_t tmax = s_tmax, kmax = s_kmax, span = kmax - tmax;
+        const int sh = span >> 11 ? 32 - __clz((int)(span >> 11)) : 0;  // span >> sh < TK_BINS
+        const int nb = (int)(span >> sh) + 1;
+        for (int b = t; b < nb; b += TK_THREADS) bcnt[b] = 0u;
+        __syncthreads();
+        for (int i = t; i < n; i += TK_THREADS) {
+            const uint32_t kk = tk_pkey(cb[i]);
+            if (kk >= tmax) atomicAdd(&bcnt[tk_cbin(kk, kmax, sh, nb)], 1u);
+        }
+        __syncthreads();
+        // exclusive scan of the bin counts (two bins per thread) with the fullest bin alongside
+        const int lane = t & 63, w = t >> 6, b0 = 2 * t;
+        const uint32_t c0 = b0 < nb ? bcnt[b0] : 0u, c1 = b0 + 1 < nb ? bcnt[b0 + 1] : 0u;
+        uint32_t incl = c0 + c1, occ = max(c0, c1);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
+            if (lane >= o) incl += y;
+            occ = max(occ, (uint32_t)__shfl_xor((int)occ, o, 64));
+        }
+        if (lane == 63) wsum[w] = incl;
+        if (lane == 0) wocc[w] = occ;
+        __syncthreads();
+        uint32_t before = 0u, total = 0u;
+#pragma unroll
+        for (int i = 0; i < TK_THREADS / 64; ++i) {
+            before += i < w ? wsum[i] : 0u;
+            total += wsum[i];
+            occ = max(occ, wocc[i]);
+        }
+        if ((int)total >= K && occ <= TK_BIN_MAX) {  // the same decision in every thread
+            const uint32_t st0 = before + incl - c0 - c1;
+            if (b0 < nb) bcur[b0] = st0;
+            if (b0 + 1 < nb) bcur[b0 + 1] = st0 + c0;
+            __syncthreads();
+            uint64_t* binned = cb + TK_SORT_MAX;
+            for (int i = t; i < n; i += TK_THREADS) {
+                const uint64_t e = cb[i];
+                const uint32_t kk = tk_pkey(e);
+                if (kk >= tmax) binned[atomicAdd(&bcur[tk_cbin(kk, kmax, sh, nb)], 1u)] = e;
+            }
+            __syncthreads();
+            // bcur[b] is now the end of bin b
+            for (int i = t; i < (int)total; i += TK_THREADS) {
+                const uint64_t e = binned[i];
+                const int b = tk_cbin(tk_pkey(e), kmax, sh, nb);
+                const int end = (int)bcur[b], beg = end - (int)bcnt[b];
+                if (beg >= K) continue;
+                int r = beg;
+                for (int j = beg; j < end; ++j) r += binned[j] > e ? 1 : 0;
+                if (r < K) {
+                    ids[(size_t)row * K + r] = tk_pid(e);
+                    lp[(size_t)row * K + r] = key_value(tk_pkey(e)) - lse;
+                }
+            }
+            return;
+        }
+    }
     for (int pass = 0; pass < 2; ++pass) {
         tk_sort_any(n, cb);
         const uint32_t T = tk_pkey(cb[K - 1]);

@@ -58,7 +58,8 @@ def test_topk_logprobs_matches_oracle(k):
                                       (256, 5003, 64), (40, 2000, 1024)])
 def test_topk_logprobs_split_rows_match_oracle(rows, V, k):
     """Row counts that split each row over many workgroups (few rows, the drafter's 16 block rows at the full
-    vocabulary) and ones that do not (256 rows), with ties inside and across chunks."""
+    vocabulary) and ones that do not (256 rows), with ties inside and across chunks: heavy ties (left to the
+    merge's sort) and few-way ties (ordered by id in its counting sort)."""
     torch, D, S = _mods()
     rng = np.random.default_rng(rows * 7 + V + k)
     lg = rng.normal(0.0, 2.5, size=(rows, V)).astype(np.float32)
@@ -67,6 +68,8 @@ def test_topk_logprobs_split_rows_match_oracle(rows, V, k):
         lg[1] = -3.0                                                # one value: the smallest ids win
     if rows > 2:
         lg[2, rng.choice(V, min(V, 3 * k), replace=False)] = 30.0   # 3k-way tie at the top
+    if rows > 3:
+        lg[3] = np.round(lg[3] * 64) / 64                           # few-way ties (1/64 steps)
     ids, lp = _topk_gpu(torch, D, lg, k)
     want_ids, want_lp = T.topk_logprobs(lg.astype(np.float64), k)
     np.testing.assert_array_equal(ids, want_ids)
