@@ -69,7 +69,7 @@ def stored_traffic(kernel, workload):
             fields[k.strip()] = v.strip()
     csrc = os.path.join(ROOT, "block_diffusion_drafter_forward_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h"):
+    for f in ("gemm.hip", "gemm_core.h", "common.h"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     if fields.get("source_sha256_16") != h.hexdigest()[:16]:
         return None

@@ -66,7 +66,8 @@ def build(force: bool = False, verbose: bool = False) -> str:
         o = os.path.join(BUILD_DIR, src + ".o")
         objs.append(o)
         if force or _needs_rebuild(o, [s] + headers):
-            jobs.append([hipcc, "-c", s, "-o", o, "-D__HIP_PLATFORM_AMD__"] + COMMON)
+            # (the same target as the kernels: headers they share hold gfx950-only device code)
+            jobs.append([hipcc, "-c", s, "-o", o, "-D__HIP_PLATFORM_AMD__"] + COMMON + DEVICE)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, max(1, len(jobs)))) as ex:
         for out in ex.map(_run, jobs):
             if verbose and out.strip():
