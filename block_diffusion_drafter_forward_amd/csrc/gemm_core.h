@@ -48,8 +48,10 @@ __host__ __device__ inline int xcd_tile_count(int gx, int gy) { return (gx + 7) 
 // next k-tile is fetched into registers while the current one is consumed from LDS (one barrier pair per
 // k-tile).  The weight tile is 16 packed fragments, copied to LDS as they are (conflict-free 1 KB reads per
 // MFMA operand); activation rows are padded to 72 elements in LDS to spread the 16-byte reads over the banks.
-// Three workgroups share a CU, so one workgroup's row reductions overlap the others' MFMAs (the head's
-// epilogue is too long to leave exposed, as it would be with one wide workgroup per CU).
+// Two workgroups share a CU (the head's 66 KB logits tile sets the LDS per workgroup), so one workgroup's
+// row reductions overlap the other's MFMAs (the head's epilogue is too long to leave exposed, as it would be
+// with one wide workgroup per CU).  With two workgroups per CU the register staging stays: the wide loop's
+// direct-to-LDS stages, with the one or two tiles in flight that fit in this LDS, measured slower here.
 #define TL_BN 128
 #define TL_BM 128
 #define TL_BK 64
