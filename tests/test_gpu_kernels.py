@@ -26,6 +26,9 @@ def _mods():
     (256, 640, 512, True),       # tiled kernel
     (130, 200, 256, True),       # tiled, ragged M and N
     (4096, 256, 2048, True),     # tiled, prefill-like
+    (300, 2048, 768, True),      # tiled 192 wide, ragged M and last column tile; four splits of six 32-deep
+                                 # k-tiles (the four-stage loop ends two tiles into its second pass)
+    (200, 1536, 1792, True),     # tiled: ten splits, nine of six k-tiles and a last one of two
     (8, 4096, 256, False),       # float32
     (10, 777, 128, False),
 ])
