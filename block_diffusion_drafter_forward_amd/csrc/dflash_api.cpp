@@ -738,6 +738,9 @@ static int tree_shape_check(int batch, int max_tokens, int nq, int nkv, int d, i
     const int G = nq / nkv;
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return *msg = "n_q_heads / n_kv_heads must be 1, 2, 4 or 8", DFLASH_E_UNSUPPORTED;
+    // the kernels index the context's 64-key rounds of every (request, token tile) in 32-bit arithmetic
+    if ((long long)batch * ((max_tokens + 15) / 16) * ((max_ctx + 63) / 64 + 64) >= (1LL << 31))
+        return *msg = "batch x tree tiles x context rounds is too large", DFLASH_E_UNSUPPORTED;
     return DFLASH_OK;
 }
 

@@ -141,8 +141,14 @@ hipError_t launch_verify_sample(int batch, int n_draft, int V, const int32_t* dr
 // ---- tree attention -----------------------------------------------------------------------------------
 #define TREE_MAX_TOKENS 2048  // tree tokens per request, root included
 #define TREE_MAX_ANC 64       // per token: its depth, then the root-to-token path (depth <= 62)
+// The context part is split stream-K: per KV head, the (request, super tile) units' 64-key rounds form one
+// sequence, and workgroup j of that head takes rounds [j rpw, (j + 1) rpw).  Each unit segment a workgroup
+// covers leaves one (m, l, O) partial in slot (workgroup - first workgroup of the unit), slots < `slots`.
+// A unit's rounds past its context (padding to whole workgroups) are empty.
 struct TreePlan {
-    int tiles, stiles, chunks, chunk_tokens;  // 16-token tiles, workgroup super tiles, context chunks
+    int tiles, stiles;  // 16-token tiles, workgroup super tiles
+    int rpu, rpw;       // 64-key rounds per unit in the sequence (the context, maybe padded), per workgroup
+    int wgs, slots;     // workgroups per KV head, partial slots per unit (0: no context)
     size_t q_off, k_off, anc_off, o_off, ml_off, total;
 };
 TreePlan plan_tree(int batch, int max_tokens, int nq, int nkv, int max_ctx);

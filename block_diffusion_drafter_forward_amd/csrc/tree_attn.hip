@@ -36,6 +36,20 @@ namespace df {
 
 static size_t ta_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// x / d for 0 <= x < 2^31 and a divisor d fixed for the call, as a multiply-high and a shift (Granlund and
+// Montgomery, "Division by Invariant Integers using Multiplication", PLDI 1994, Theorem 4.2 with N = 31):
+// l = ceil(log2 d), m = floor(2^(31 + l) / d) + 1 < 2^32.  The kernels' segment and slot indices use it in
+// place of a run-time division (a long reciprocal-and-correct sequence) ahead of their first loads.
+struct FastDiv {
+    uint32_t m, s;
+};
+static FastDiv fast_div(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    return FastDiv{(uint32_t)((1ull << (31 + l)) / d + 1), 31 + l};
+}
+__device__ __forceinline__ int fdiv(int x, FastDiv f) { return (int)(((uint64_t)(uint32_t)x * f.m) >> f.s); }
+
 // Waves per context workgroup: the G query heads of a KV head times TA_WAVES / G wave slots, each slot
 // TA_QT token tiles, all served by the same staged K/V.  Two tiles per wave make every K (V) fragment read
 // from LDS feed two MFMAs (with one tile per wave, LDS reads bounded the kernel).
@@ -47,31 +61,49 @@ TreePlan plan_tree(int batch, int max_tokens, int nq, int nkv, int max_ctx) {
     p.tiles = (max_tokens + 15) / 16;
     const int tw = TA_WAVES / (nq / nkv) * TA_QT;  // tiles per workgroup
     p.stiles = (p.tiles + tw - 1) / tw;
-    p.chunks = 0;
-    p.chunk_tokens = 0;
+    p.rpu = p.rpw = p.wgs = p.slots = 0;
     if (max_ctx > 0) {
         // One eight-wave workgroup per CU (the kernel's registers allow no second), so a grid runs in
-        // generations of 256 workgroups.  Pick the chunk count that minimises the estimated time (measured on
-        // MI355X): generations x (rounds per chunk + about one round of start-up) x 2.8 us, plus each chunk's
-        // float32 (m, l, O) partials written and read back by the merge at ~5 TB/s, plus one merge round trip
-        // (~1.5 us) per TM_BATCH chunks.
-        const int units = batch * p.stiles * nkv;
-        const int max_chunks = (max_ctx + TA_SUB - 1) / TA_SUB;
-        const double part_us = (double)batch * p.tiles * nq * 16 * (TA_D + 2) * 4 * 2 / 5.0e6;  // per chunk
+        // generations of 256 workgroups.  Pick the rounds per workgroup (and the mode) that minimise the
+        // estimated time (measured on MI355X): generations x (rounds + about one round of start-up per unit
+        // segment) x 2.8 us, plus the float32 (m, l, O) partials written and read back by the merge at ~5 TB/s,
+        // plus one merge round trip (~1.5 us) per TM_BATCH slots.  Two modes:
+        //  - padded: each unit's sequence is padded to whole workgroups (the padding rounds are empty), so every
+        //    workgroup serves one unit: equal chunks of each unit's context;
+        //  - streamed: no padding, so that the workgroups share the rounds evenly, at the price of a second
+        //    start-up where a workgroup's rounds run into the next unit.  Equal chunks leave the last generation
+        //    part-empty when the unit count does not divide into 256s (at 1025 tree tokens of one request: 136
+        //    units).
+        const int units = batch * p.stiles;  // per KV head
+        const int rounds = (max_ctx + TA_SUB - 1) / TA_SUB;
+        const double part_us = (double)batch * p.tiles * nq * 16 * (TA_D + 2) * 4 * 2 / 5.0e6;  // per slot
+        const int max_rpw = std::min(TA_MAX_PAGES / 4, rounds);  // a segment's page ids fit in LDS
         double best = 1e30;
-        for (int want = 1; want <= max_chunks; ++want) {
-            int ct = (max_ctx + want - 1) / want;
-            ct = (ct + TA_SUB - 1) / TA_SUB * TA_SUB;
-            if (ct > 16 * TA_MAX_PAGES) continue;
-            const int chunks = (max_ctx + ct - 1) / ct;
-            const long wgs = (long)units * chunks;
-            const double cost = 2.8 * (double)((wgs + 255) / 256) * (ct / TA_SUB + 1.2) + chunks * part_us +
-                                1.5 * ((chunks + TM_BATCH - 1) / TM_BATCH);
-            if (cost < best - 1e-9) {
-                best = cost;
-                p.chunk_tokens = ct;
-                p.chunks = chunks;
+        for (int rpw = 1; rpw <= max_rpw; ++rpw) {
+            for (int streamed = 0; streamed < 2; ++streamed) {
+                const int chunks = (rounds + rpw - 1) / rpw;
+                const int seq = streamed ? rounds : chunks * rpw;  // the unit's rounds in the sequence
+                if (streamed && seq % rpw == 0) continue;          // same as padded
+                const long wgs = ((long)units * seq + rpw - 1) / rpw;
+                const long gens = (wgs * nkv + 255) / 256;
+                const int segs = streamed ? (rpw + seq - 1) / seq + 1 : 1;
+                const int slots = streamed ? (seq - 1) / rpw + 2 : chunks;
+                const double per_unit = streamed ? (double)seq / rpw + 1.0 : chunks;
+                const double cost = 2.8 * (double)gens * (rpw + 1.2 * segs) + per_unit * part_us +
+                                    1.5 * ((slots + TM_BATCH - 1) / TM_BATCH);
+                if (cost < best - 1e-9) {
+                    best = cost;
+                    p.rpu = seq;
+                    p.rpw = rpw;
+                    p.wgs = (int)wgs;
+                }
             }
+        }
+        // slots: the most workgroups any unit's rounds [u rpu, (u + 1) rpu) meet (a function of u rpu mod rpw,
+        // whose values repeat within rpw units)
+        for (int u = 0; u < std::min(units, p.rpw); ++u) {
+            const long f = (long)u * p.rpu / p.rpw, l = ((long)u * p.rpu + p.rpu - 1) / p.rpw;
+            p.slots = std::max(p.slots, (int)(l - f + 1));
         }
     }
     const size_t T = (size_t)p.tiles * 16;
@@ -83,9 +115,9 @@ TreePlan plan_tree(int batch, int max_tokens, int nq, int nkv, int max_ctx) {
     p.anc_off = off;
     off += ta_align((size_t)batch * T * TREE_MAX_ANC * 4);
     p.o_off = off;
-    off += ta_align((size_t)batch * p.tiles * nq * p.chunks * 16 * TA_D * 4);
+    off += ta_align((size_t)batch * p.tiles * nq * p.slots * 16 * TA_D * 4);
     p.ml_off = off;
-    off += ta_align((size_t)batch * p.tiles * nq * p.chunks * 16 * 2 * 4);
+    off += ta_align((size_t)batch * p.tiles * nq * p.slots * 16 * 2 * 4);
     p.total = off;
     return p;
 }
@@ -230,8 +262,10 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
                                                         const bf16_t* __restrict__ vpool, int n_pages,
                                                         const int32_t* __restrict__ pt, int max_pages,
                                                         const int32_t* __restrict__ ctx_len, int max_ctx,
-                                                        int chunk_tokens, int n_chunks, float* __restrict__ opart,
-                                                        float* __restrict__ mlpart, uint32_t* err) {
+                                                        int units, int rpu, int rpw, FastDiv div_rpu,
+                                                        FastDiv div_rpw, FastDiv div_stiles, int n_slots,
+                                                        float* __restrict__ opart, float* __restrict__ mlpart,
+                                                        uint32_t* err) {
     constexpr int D = TA_D;
     constexpr int TW = TA_WAVES / G;
     constexpr int QT = TA_QT;
@@ -243,217 +277,226 @@ __global__ __launch_bounds__(64 * TA_WAVES) void tree_ctx_bf16(const bf16_t* __r
     __shared__ __attribute__((aligned(16))) bf16_t sk[TA_SUB * TA_KLD];
     __shared__ __attribute__((aligned(16))) bf16_t sv[(NPG / 2) * D * TA_SVLD];
     __shared__ int spg[TA_MAX_PAGES];
-    // grid: KV head fastest, then super tile, chunk, request
+    // grid: KV head fastest (one head per XCD's L2 when there are eight), then the head's workgroups in order;
+    // workgroup wl of a head takes rounds [wl rpw, (wl + 1) rpw) of the sequence unit u = request * stiles +
+    // super tile, rounds 0 .. rpu - 1 of each
     const int stiles = (tiles + TW * QT - 1) / (TW * QT);
-    int bid = blockIdx.x;
-    const int kvh = bid % nkv;
-    bid /= nkv;
-    const int stile = bid % stiles;
-    bid /= stiles;
-    const int c = bid % n_chunks;
-    const int b = bid / n_chunks;
+    const int kvh = blockIdx.x % nkv;
+    const int wl = blockIdx.x / nkv;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int h = kvh * G + w % G;
-    const int tile0 = (stile * TW + w / G) * QT;  // this wave's first tile; the last super tile may reach past the tree
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     const size_t page_elems = (size_t)16 * D;
+    // (units * rpu < 2^31: the API bounds batch x tiles x rounds)
+    const int gend = min(units * rpu, wl * rpw + rpw);
+    for (int gpos = wl * rpw; gpos < gend;) {  // one unit segment per pass
+        const int u = fdiv(gpos, div_rpu);
+        const int r0 = gpos - u * rpu;
+        const int r1 = min(rpu, r0 + (gend - gpos));
+        const int slot = wl - fdiv(u * rpu, div_rpw);  // < n_slots
+        const bool first = gpos == wl * rpw;
+        gpos += r1 - r0;
+        const int b = fdiv(u, div_stiles), stile = u - b * stiles;
+        // this wave's first tile; the last super tile may reach past the tree
+        const int tile0 = (stile * TW + w / G) * QT;
 
-    const int pg0 = c * (chunk_tokens / 16);
-    for (int j = tid; j < chunk_tokens / 16; j += NT)
-        spg[j] = pg0 + j < max_pages ? pt[(size_t)b * max_pages + pg0 + j] : -1;
-    int ctx = ctx_len[b];
-    if (ctx > max_ctx || ctx < 0) ctx = ctx < 0 ? 0 : max_ctx;  // flagged by tree_prep
-    const int t0 = c * chunk_tokens;
-    const int t1 = min(ctx, t0 + chunk_tokens);
+        if (!first) __syncthreads();  // the previous segment's waves are past their page-id reads
+        const int pg0 = r0 * (TA_SUB / 16), npg = (r1 - r0) * (TA_SUB / 16);  // npg <= TA_MAX_PAGES (rpw <= 64)
+        for (int j = tid; j < npg; j += NT) spg[j] = pg0 + j < max_pages ? pt[(size_t)b * max_pages + pg0 + j] : -1;
+        int ctx = ctx_len[b];
+        if (ctx > max_ctx || ctx < 0) ctx = ctx < 0 ? 0 : max_ctx;  // flagged by tree_prep
+        const int t0 = r0 * TA_SUB;
+        const int t1 = min(ctx, r1 * TA_SUB);
 
-    u32x4 pf[PPT];
-    uint32_t okmask = 0;
-    auto prefetch = [&](int ts) {
-        okmask = 0;
-#pragma unroll
-        for (int e = 0; e < NPG; ++e) {
-            const int tp = ts + 16 * e;
-            const int page = tp < t1 ? spg[(tp - t0) >> 4] : -1;
-            const bool ok = page >= 0 && page < n_pages;
-            const size_t ofs = ((size_t)(ok ? page : 0) * nkv + kvh) * page_elems;
-            okmask |= (ok ? 1u : 0u) << e;
-#pragma unroll
-            for (int u = 0; u < PPP; ++u) {
-                const int qq = tid + u * NT;
-                pf[e * PPP + u] = ld16((qq < 256 ? kpool : vpool) + ofs + (qq & 255) * 8);
-            }
-        }
-    };
-    // piece qq of page slot e into LDS: K row-major, V^T (piece q2 = slots 8 h .. 8 h + 7 of row d, groups 2 h
-    // and 2 h + 1) into the interleaved value rows
-    auto put = [&](int e, int qq, u32x4 v) {
-        if (qq < 256) {
-            *(u32x4*)(sk + (e * 16 + (qq >> 4)) * TA_KLD + (qq & 15) * 8) = v;
-        } else {
-            const int q2 = qq - 256, half = q2 & 1;
-            bf16_t* row = sv + ((e >> 1) * D + (q2 >> 1)) * TA_SVLD + (e & 1) * 4;
-            *(u32x2*)(row + (2 * half) * 8) = u32x2{v[0], v[1]};
-            *(u32x2*)(row + (2 * half + 1) * 8) = u32x2{v[2], v[3]};
-        }
-    };
-    auto stash = [&](int ts) {
-        okmask = __builtin_amdgcn_readfirstlane(okmask);
-        if (okmask == (1u << NPG) - 1 && ts + TA_SUB <= t1) {  // every page mapped and full (scalar branch)
-#pragma unroll
-            for (int e = 0; e < NPG; ++e)
-#pragma unroll
-                for (int u = 0; u < PPP; ++u) put(e, tid + u * NT, pf[e * PPP + u]);
-            return;
-        }
-#pragma unroll
-        for (int e = 0; e < NPG; ++e) {
-            const bool ok = (okmask >> e) & 1u;
-            const int nvalid = t1 - (ts + 16 * e);
-#pragma unroll
-            for (int u = 0; u < PPP; ++u) {
-                const int qq = tid + u * NT;
-                u32x4 v = pf[e * PPP + u];
-                if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-                if (qq >= 256 && nvalid < 16) {  // values of slots past the last key may hold anything: zero them
-                    const int half = (qq - 256) & 1;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int s0 = half * 8 + 2 * j;
-                        const uint32_t m = (s0 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
-                        v[j] &= m;
-                    }
-                }
-                put(e, qq, v);
-            }
-        }
-    };
-
-    // Q^T operands: lane supplies query row r of each tile (token tile * 16 + r), 8 d-values per k-step
-    u32x4 qf[QT][4];
-#pragma unroll
-    for (int qi = 0; qi < QT; ++qi) {
-        const bool ok = tile0 + qi < tiles;
-        const bf16_t* qp = qr + (((size_t)b * Tpad + (ok ? tile0 + qi : 0) * 16 + r) * nq + h) * D + g * 8;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) qf[qi][s] = ok ? ld16(qp + s * 32) : u32x4{0u, 0u, 0u, 0u};
-    }
-    // o[qi][0..7]: O^T for the eight 16-row d-tiles; o[qi][8]: the same product against an all-ones V^T,
-    // i.e. the row sums l of the bfloat16 P that weighted O (every lane ends with its token's sum).
-    f32x4 o[QT][9];
-    float m_run[QT];
-#pragma unroll
-    for (int qi = 0; qi < QT; ++qi) {
-#pragma unroll
-        for (int dt = 0; dt < 9; ++dt) o[qi][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run[qi] = -INFINITY;
-    }
-    const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bfloat16 1.0 x 8
-
-    __syncthreads();  // page ids in LDS
-    for (int j = tid; j < chunk_tokens / 16 && t0 + 16 * j < t1; j += NT) {
-        if ((t0 >> 4) + j >= max_pages) set_err(err, DFLASH_DEVERR_POS);
-        else if (spg[j] < 0 || spg[j] >= n_pages) set_err(err, DFLASH_DEVERR_PAGE);
-    }
-    // One 64-key round starting at ts.  TAIL: the round runs past the chunk's last key (masked scores, slices
-    // past the end skipped); the full rounds carry no masking code.
-    //
-    // Softmax in the log2 domain against a running reference m: p = 2^(s * scale - m).  The reference is raised
-    // (and O, l rescaled by 2^(m_old - m_new)) only when some row's maximum exceeds it by more than
-    // TA_RESCALE; otherwise p may reach 2^TA_RESCALE, which float32 sums and the bfloat16 P hold at the same
-    // relative precision.  The (m, l, O) partials are exact for any reference, so the merge is unchanged.
-    auto round = [&](int ts, auto tail_tag) {
-        constexpr bool TAIL = decltype(tail_tag)::value;
-        __syncthreads();
-        stash(ts);
-        __syncthreads();
-        if (ts + TA_SUB < t1) prefetch(ts + TA_SUB);
-        f32x4 sa[QT][NPG];
-#pragma unroll
-        for (int qi = 0; qi < QT; ++qi)
-#pragma unroll
-            for (int e = 0; e < NPG; ++e) sa[qi][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
+        u32x4 pf[PPT];
+        uint32_t okmask = 0;
+        auto prefetch = [&](int ts) {
+            okmask = 0;
 #pragma unroll
             for (int e = 0; e < NPG; ++e) {
-                const u32x4 kf = ld16(sk + (e * 16 + r) * TA_KLD + g * 8 + s * 32);
+                const int tp = ts + 16 * e;
+                const int page = tp < t1 ? spg[(tp - t0) >> 4] : -1;
+                const bool ok = page >= 0 && page < n_pages;
+                const size_t ofs = ((size_t)(ok ? page : 0) * nkv + kvh) * page_elems;
+                okmask |= (ok ? 1u : 0u) << e;
 #pragma unroll
-                for (int qi = 0; qi < QT; ++qi) sa[qi][e] = mfma16(kf, qf[qi][s], sa[qi][e]);
+                for (int u = 0; u < PPP; ++u) {
+                    const int qq = tid + u * NT;
+                    pf[e * PPP + u] = ld16((qq < 256 ? kpool : vpool) + ofs + (qq & 255) * 8);
+                }
             }
-        u32x4 pb[QT][NPG / 2];
-#pragma unroll
-        for (int qi = 0; qi < QT; ++qi) {
-            if (TAIL) {
-                const int nk = t1 - ts;
+        };
+        // piece qq of page slot e into LDS: K row-major, V^T (piece q2 = slots 8 h .. 8 h + 7 of row d, groups 2 h
+        // and 2 h + 1) into the interleaved value rows
+        auto put = [&](int e, int qq, u32x4 v) {
+            if (qq < 256) {
+                *(u32x4*)(sk + (e * 16 + (qq >> 4)) * TA_KLD + (qq & 15) * 8) = v;
+            } else {
+                const int q2 = qq - 256, half = q2 & 1;
+                bf16_t* row = sv + ((e >> 1) * D + (q2 >> 1)) * TA_SVLD + (e & 1) * 4;
+                *(u32x2*)(row + (2 * half) * 8) = u32x2{v[0], v[1]};
+                *(u32x2*)(row + (2 * half + 1) * 8) = u32x2{v[2], v[3]};
+            }
+        };
+        auto stash = [&](int ts) {
+            okmask = __builtin_amdgcn_readfirstlane(okmask);
+            if (okmask == (1u << NPG) - 1 && ts + TA_SUB <= t1) {  // every page mapped and full (scalar branch)
 #pragma unroll
                 for (int e = 0; e < NPG; ++e)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sa[qi][e][i] = 16 * e + 4 * g + i < nk ? sa[qi][e][i] : -INFINITY;
+                    for (int u = 0; u < PPP; ++u) put(e, tid + u * NT, pf[e * PPP + u]);
+                return;
             }
-            // row maximum of the raw scores (scale_log2 > 0 keeps the order)
-            float mx = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < NPG; ++e)
+            for (int e = 0; e < NPG; ++e) {
+                const bool ok = (okmask >> e) & 1u;
+                const int nvalid = t1 - (ts + 16 * e);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sa[qi][e][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mxs = mx * scale_log2;
-            if (__any(mxs > m_run[qi] + TA_RESCALE)) {
-                const float m_new = fmaxf(m_run[qi], mxs);
-                const float alpha = __builtin_amdgcn_exp2f(m_run[qi] - (m_new == -INFINITY ? 0.f : m_new));
-                m_run[qi] = m_new;
+                for (int u = 0; u < PPP; ++u) {
+                    const int qq = tid + u * NT;
+                    u32x4 v = pf[e * PPP + u];
+                    if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+                    if (qq >= 256 && nvalid < 16) {  // values of slots past the last key may hold anything: zero them
+                        const int half = (qq - 256) & 1;
 #pragma unroll
-                for (int dt = 0; dt < 9; ++dt) {
-                    o[qi][dt][0] *= alpha; o[qi][dt][1] *= alpha; o[qi][dt][2] *= alpha; o[qi][dt][3] *= alpha;
+                        for (int j = 0; j < 4; ++j) {
+                            const int s0 = half * 8 + 2 * j;
+                            const uint32_t m = (s0 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
+                            v[j] &= m;
+                        }
+                    }
+                    put(e, qq, v);
                 }
             }
-            const float neg_m = m_run[qi] == -INFINITY ? 0.f : -m_run[qi];
-            float p[NPG][4];
+        };
+
+        // Q^T operands: lane supplies query row r of each tile (token tile * 16 + r), 8 d-values per k-step
+        u32x4 qf[QT][4];
 #pragma unroll
-            for (int e = 0; e < NPG; ++e)
+        for (int qi = 0; qi < QT; ++qi) {
+            const bool ok = tile0 + qi < tiles;
+            const bf16_t* qp = qr + (((size_t)b * Tpad + (ok ? tile0 + qi : 0) * 16 + r) * nq + h) * D + g * 8;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p[e][i] = __builtin_amdgcn_exp2f(fmaf(sa[qi][e][i], scale_log2, neg_m));
-#pragma unroll
-            for (int hk = 0; hk < NPG / 2; ++hk)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    pb[qi][hk][j] = f2bf2(p[2 * hk + (j >> 1)][2 * (j & 1)], p[2 * hk + (j >> 1)][2 * (j & 1) + 1]);
+            for (int s = 0; s < 4; ++s) qf[qi][s] = ok ? ld16(qp + s * 32) : u32x4{0u, 0u, 0u, 0u};
         }
-        // O^T += V^T P^T over 32-key slices, P as bfloat16; each V^T fragment feeds every tile, and the
-        // all-ones operand accumulates the row sums from the same P
+        // o[qi][0..7]: O^T for the eight 16-row d-tiles; o[qi][8]: the same product against an all-ones V^T,
+        // i.e. the row sums l of the bfloat16 P that weighted O (every lane ends with its token's sum).
+        f32x4 o[QT][9];
+        float m_run[QT];
 #pragma unroll
-        for (int hk = 0; hk < NPG / 2; ++hk) {
-            if (TAIL && ts + 32 * hk >= t1) break;
+        for (int qi = 0; qi < QT; ++qi) {
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const u32x4 vf = ld16(sv + (hk * D + dt * 16 + r) * TA_SVLD + g * 8);
+            for (int dt = 0; dt < 9; ++dt) o[qi][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m_run[qi] = -INFINITY;
+        }
+        const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bfloat16 1.0 x 8
+
+        __syncthreads();  // page ids in LDS
+        for (int j = tid; j < npg && t0 + 16 * j < t1; j += NT) {
+            if ((t0 >> 4) + j >= max_pages) set_err(err, DFLASH_DEVERR_POS);
+            else if (spg[j] < 0 || spg[j] >= n_pages) set_err(err, DFLASH_DEVERR_PAGE);
+        }
+        // One 64-key round starting at ts.  TAIL: the round runs past the chunk's last key (masked scores, slices
+        // past the end skipped); the full rounds carry no masking code.
+        //
+        // Softmax in the log2 domain against a running reference m: p = 2^(s * scale - m).  The reference is raised
+        // (and O, l rescaled by 2^(m_old - m_new)) only when some row's maximum exceeds it by more than
+        // TA_RESCALE; otherwise p may reach 2^TA_RESCALE, which float32 sums and the bfloat16 P hold at the same
+        // relative precision.  The (m, l, O) partials are exact for any reference, so the merge is unchanged.
+        auto round = [&](int ts, auto tail_tag) {
+            constexpr bool TAIL = decltype(tail_tag)::value;
+            __syncthreads();
+            stash(ts);
+            __syncthreads();
+            if (ts + TA_SUB < t1) prefetch(ts + TA_SUB);
+            f32x4 sa[QT][NPG];
 #pragma unroll
-                for (int qi = 0; qi < QT; ++qi) o[qi][dt] = mfma16(vf, pb[qi][hk], o[qi][dt]);
+            for (int qi = 0; qi < QT; ++qi)
+#pragma unroll
+                for (int e = 0; e < NPG; ++e) sa[qi][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int e = 0; e < NPG; ++e) {
+                    const u32x4 kf = ld16(sk + (e * 16 + r) * TA_KLD + g * 8 + s * 32);
+#pragma unroll
+                    for (int qi = 0; qi < QT; ++qi) sa[qi][e] = mfma16(kf, qf[qi][s], sa[qi][e]);
+                }
+            u32x4 pb[QT][NPG / 2];
+#pragma unroll
+            for (int qi = 0; qi < QT; ++qi) {
+                if (TAIL) {
+                    const int nk = t1 - ts;
+#pragma unroll
+                    for (int e = 0; e < NPG; ++e)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sa[qi][e][i] = 16 * e + 4 * g + i < nk ? sa[qi][e][i] : -INFINITY;
+                }
+                // row maximum of the raw scores (scale_log2 > 0 keeps the order)
+                float mx = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < NPG; ++e)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sa[qi][e][i]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float mxs = mx * scale_log2;
+                if (__any(mxs > m_run[qi] + TA_RESCALE)) {
+                    const float m_new = fmaxf(m_run[qi], mxs);
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[qi] - (m_new == -INFINITY ? 0.f : m_new));
+                    m_run[qi] = m_new;
+#pragma unroll
+                    for (int dt = 0; dt < 9; ++dt) {
+                        o[qi][dt][0] *= alpha; o[qi][dt][1] *= alpha; o[qi][dt][2] *= alpha; o[qi][dt][3] *= alpha;
+                    }
+                }
+                const float neg_m = m_run[qi] == -INFINITY ? 0.f : -m_run[qi];
+                float p[NPG][4];
+#pragma unroll
+                for (int e = 0; e < NPG; ++e)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) p[e][i] = __builtin_amdgcn_exp2f(fmaf(sa[qi][e][i], scale_log2, neg_m));
+#pragma unroll
+                for (int hk = 0; hk < NPG / 2; ++hk)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pb[qi][hk][j] = f2bf2(p[2 * hk + (j >> 1)][2 * (j & 1)], p[2 * hk + (j >> 1)][2 * (j & 1) + 1]);
             }
+            // O^T += V^T P^T over 32-key slices, P as bfloat16; each V^T fragment feeds every tile, and the
+            // all-ones operand accumulates the row sums from the same P
 #pragma unroll
-            for (int qi = 0; qi < QT; ++qi) o[qi][8] = mfma16(ones, pb[qi][hk], o[qi][8]);
+            for (int hk = 0; hk < NPG / 2; ++hk) {
+                if (TAIL && ts + 32 * hk >= t1) break;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) {
+                    const u32x4 vf = ld16(sv + (hk * D + dt * 16 + r) * TA_SVLD + g * 8);
+#pragma unroll
+                    for (int qi = 0; qi < QT; ++qi) o[qi][dt] = mfma16(vf, pb[qi][hk], o[qi][dt]);
+                }
+#pragma unroll
+                for (int qi = 0; qi < QT; ++qi) o[qi][8] = mfma16(ones, pb[qi][hk], o[qi][8]);
+            }
+        };
+        if (t0 < t1) prefetch(t0);
+        int ts = t0;
+        for (; ts + TA_SUB <= t1; ts += TA_SUB) round(ts, std::false_type{});
+        if (ts < t1) round(ts, std::true_type{});
+#pragma unroll
+        for (int qi = 0; qi < QT; ++qi) {
+            const int tile = tile0 + qi;
+            if (tile >= tiles) continue;
+            const size_t base = ((((size_t)b * tiles + tile) * nq + h) * n_slots + slot) * 16 + r;
+            float* op = opart + base * D;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                *(float4*)(op + dt * 16 + 4 * g) = make_float4(o[qi][dt][0], o[qi][dt][1], o[qi][dt][2], o[qi][dt][3]);
+            if (g == 0) {
+                mlpart[base * 2 + 0] = m_run[qi];
+                mlpart[base * 2 + 1] = o[qi][8][0];
+            }
         }
-    };
-    if (t0 < t1) prefetch(t0);
-    int ts = t0;
-    for (; ts + TA_SUB <= t1; ts += TA_SUB) round(ts, std::false_type{});
-    if (ts < t1) round(ts, std::true_type{});
-#pragma unroll
-    for (int qi = 0; qi < QT; ++qi) {
-        const int tile = tile0 + qi;
-        if (tile >= tiles) continue;
-        const size_t base = ((((size_t)b * tiles + tile) * nq + h) * n_chunks + c) * 16 + r;
-        float* op = opart + base * D;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-            *(float4*)(op + dt * 16 + 4 * g) = make_float4(o[qi][dt][0], o[qi][dt][1], o[qi][dt][2], o[qi][dt][3]);
-        if (g == 0) {
-            mlpart[base * 2 + 0] = m_run[qi];
-            mlpart[base * 2 + 1] = o[qi][8][0];
-        }
-    }
+    }  // segment
 }
 
 // ------------------------------------------------------------------------------------------------------
@@ -465,7 +508,8 @@ __global__ __launch_bounds__(256) void tree_merge(int T, int Tpad, int tiles, in
                                                   const bf16_t* __restrict__ qr, const bf16_t* __restrict__ kr,
                                                   const bf16_t* __restrict__ v, const int32_t* __restrict__ anc,
                                                   const float* __restrict__ opart, const float* __restrict__ mlpart,
-                                                  int n_chunks, bf16_t* __restrict__ out) {
+                                                  int rpu, FastDiv div_rpw, int tw_log2, int n_slots,
+                                                  bf16_t* __restrict__ out) {
     const int b = blockIdx.y;
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, KV head)
     const int lane = threadIdx.x & 63;
@@ -481,6 +525,11 @@ __global__ __launch_bounds__(256) void tree_merge(int T, int Tpad, int tiles, in
     const int my_anc = lane <= depth ? anc_e : 0;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)TA_D);
     const int tile = i >> 4, row = i & 15;
+    // the context partials of this token's unit: one per workgroup its rounds met (none without a context)
+    // (tiles per context workgroup: 2^tw_log2; u0 < 2^31, bounded by the API)
+    const int u0 = (b * ((tiles + (1 << tw_log2) - 1) >> tw_log2) + (tile >> tw_log2)) * rpu;
+    const int n_chunks =
+        __builtin_amdgcn_readfirstlane(n_slots > 0 ? fdiv(u0 + rpu - 1, div_rpw) - fdiv(u0, div_rpw) + 1 : 0);
     for (int hg = 0; hg < G; hg += 4) {
         const int hq = hg + hs;
         const bool live = hq < G;
@@ -499,7 +548,7 @@ __global__ __launch_bounds__(256) void tree_merge(int T, int Tpad, int tiles, in
         float m = -INFINITY, l = 0.f, acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-        const size_t cbase = (((size_t)b * tiles + tile) * nq + h) * n_chunks;
+        const size_t cbase = (((size_t)b * tiles + tile) * nq + h) * n_slots;
         for (int c0 = 0; c0 < n_chunks; c0 += TM_BATCH) {  // TM_BATCH chunks' loads in flight at a time
             float2 mlc[TM_BATCH];
             float4 oc0[TM_BATCH], oc1[TM_BATCH];
@@ -583,13 +632,14 @@ hipError_t launch_tree_attention(const TreePlan& p, int batch, int T, const int3
     hipLaunchKernelGGL(tree_prep, dim3(p.tiles, batch, (nq + nkv + TP_HEADS - 1) / TP_HEADS), dim3(256), 0, st, T,
                        n_tokens, parent, nq, nkv,
                        (const bf16_t*)q, (const bf16_t*)k, ctx_len, max_ctx, rf, qr, kr, anc, Tpad, err);
-    if (p.chunks > 0) {
-        const dim3 grid(nkv * p.stiles * p.chunks * batch);
+    if (p.slots > 0) {
+        const dim3 grid(nkv * p.wgs);
         const int G = nq / nkv;
 #define TA_LAUNCH(GG)                                                                                          \
     hipLaunchKernelGGL((tree_ctx_bf16<GG>), grid, dim3(64 * TA_WAVES), 0, st, qr, Tpad, p.tiles, nq, nkv,        \
                        (const bf16_t*)kpool, (const bf16_t*)vpool, n_pages, pt, max_pages, ctx_len, max_ctx,    \
-                       p.chunk_tokens, p.chunks, opart, ml, err)
+                       batch * p.stiles, p.rpu, p.rpw, fast_div(p.rpu), fast_div(p.rpw), fast_div(p.stiles),    \
+                       p.slots, opart, ml, err)
         if (G == 1) TA_LAUNCH(1);
         else if (G == 2) TA_LAUNCH(2);
         else if (G == 4) TA_LAUNCH(4);
@@ -597,7 +647,9 @@ hipError_t launch_tree_attention(const TreePlan& p, int batch, int T, const int3
 #undef TA_LAUNCH
     }
     hipLaunchKernelGGL(tree_merge, dim3((T * nkv + 3) / 4, batch), dim3(256), 0, st, T, Tpad, p.tiles, nq, nkv,
-                       n_tokens, qr, kr, (const bf16_t*)v, anc, opart, ml, p.chunks, (bf16_t*)out);
+                       n_tokens, qr, kr, (const bf16_t*)v, anc, opart, ml, p.rpu,
+                       fast_div(p.slots > 0 ? p.rpw : 1), __builtin_ctz((unsigned)(TA_WAVES / (nq / nkv) * TA_QT)),
+                       p.slots, (bf16_t*)out);
     return hipGetLastError();
 }
 

@@ -317,7 +317,8 @@ int dflash_ddtree_walk(int batch, int budget, int max_accept, const int32_t *nod
  *   rope_theta   rotary base (0: no rotation); q and k are rotated in float32 and rounded to bfloat16
  *   out          device bfloat16 [batch][max_tokens][n_q_heads][128]
  * Query head h reads KV head h / (n_q_heads / n_kv_heads); that ratio is 1, 2, 4 or 8; head_dim 128;
- * max_tokens <= 2048.  q, k, v, out and the pages 16-byte aligned; ws 256-byte aligned, at least
+ * max_tokens <= 2048; batch * ceil(max_tokens / 16) * (ceil(max_ctx / 64) + 64) < 2^31 (else
+ * DFLASH_E_UNSUPPORTED).  q, k, v, out and the pages 16-byte aligned; ws 256-byte aligned, at least
  * dflash_tree_attention_workspace_bytes(...) bytes; its first 4 bytes are the device error word
  * (DFLASH_DEVERR_PAGE / _POS / _TREE), cleared by every call.                                             */
 size_t dflash_tree_attention_workspace_bytes(int batch, int max_tokens, int n_q_heads, int n_kv_heads,

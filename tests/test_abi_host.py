@@ -338,6 +338,9 @@ def test_tree_attention_workspace_size(D):
     assert D.dflash_tree_attention_workspace_bytes(1, 16, 32, 8, 64, 100) == 0
     assert D.dflash_tree_attention_workspace_bytes(1, 16, 24, 8, 128, 100) == 0
     assert D.dflash_tree_attention_workspace_bytes(0, 16, 32, 8, 128, 100) == 0
+    # the context rounds of every (request, token tile) are indexed in 32 bits
+    assert D.dflash_tree_attention_workspace_bytes(1, 2048, 32, 8, 128, 1 << 20) > 0
+    assert D.dflash_tree_attention_workspace_bytes(65535, 2048, 32, 8, 128, 1 << 20) == 0
 
 
 @pytest.mark.parametrize("over,code", [

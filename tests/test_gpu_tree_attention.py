@@ -61,7 +61,8 @@ def _to_dev(a, dtype=None):
     return t.cuda()
 
 
-def _run(rng, n_tokens, parents, ctx, nq, nkv, theta=THETA, qscale=1.5, max_tokens=None, oracle=True):
+def _run(rng, n_tokens, parents, ctx, nq, nkv, theta=THETA, qscale=1.5, max_tokens=None, oracle=True,
+         bad_page=None):
     """Build the synthetic layer, run the kernel, return (gpu out [B, T, nq, d] fp64, oracle outs, max |v|, err)."""
     import torch
     from block_diffusion_drafter_forward_amd import dflash as D
@@ -91,6 +92,8 @@ def _run(rng, n_tokens, parents, ctx, nq, nkv, theta=THETA, qscale=1.5, max_toke
         for p in range(ctx[b]):
             kpool[pt[b, p // 16], :, p % 16, :] = kc[p]
             vpool[pt[b, p // 16], :, :, p % 16] = vc[p]
+    if bad_page is not None:  # (request, page slot): an id past the pool
+        pt[bad_page] = n_pages + 7
     out = torch.zeros((B, T, nq, d), dtype=torch.bfloat16, device="cuda")
     nbytes = D.dflash_tree_attention_workspace_bytes(B, T, nq, nkv, d, max_ctx)
     assert nbytes > 0
@@ -169,6 +172,17 @@ def test_tree_attention_rows_past_n_tokens_untouched():
     assert err == 0
     _check(got, refs, vmax, [10, 3])
     assert np.all(got[0, 10:] == 0) and np.all(got[1, 3:] == 0)
+
+
+def test_tree_attention_flags_bad_page_ids():
+    """A page id past the pool, in the last workgroup's rounds of a long context, is flagged in the device error
+    word (its keys are read from page 0 instead)."""
+    from block_diffusion_drafter_forward_amd import dflash as D
+    rng = np.random.default_rng(8)
+    n = [300, 90]
+    par = [_random_parents(rng, 300), _random_parents(rng, 90)]
+    _, _, _, err = _run(rng, n, par, [4096, 2500], 32, 8, oracle=False, bad_page=(1, 150))
+    assert err == D.DEVERR_PAGE
 
 
 def test_tree_attention_flags_bad_parent_links():
