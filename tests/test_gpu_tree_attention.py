@@ -140,6 +140,10 @@ def _check(got, refs, vmax, n_tokens):
     dict(n=[64, 50], ctx=[300, 77], nq=16, nkv=8, tree="random"),
     dict(n=[40, 33], ctx=[130, 0], nq=64, nkv=8, tree="random"),
     dict(n=[2048], ctx=[16], nq=32, nkv=8, tree="random"),
+    # streamed context splits in which a workgroup's rounds run from one request's last token tiles into the
+    # next request's first, with ragged contexts
+    dict(n=[321, 200, 290], ctx=[1024, 700, 1000], nq=32, nkv=8, tree="ddtree"),
+    dict(n=[129, 100, 64], ctx=[4096, 4000, 1500], nq=32, nkv=8, tree="random"),
 ])
 def test_tree_attention_matches_oracle(case):
     rng = np.random.default_rng(sum(case["n"]) * 7 + sum(case["ctx"]) + case["nq"])
