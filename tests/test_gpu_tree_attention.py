@@ -144,6 +144,8 @@ def _check(got, refs, vmax, n_tokens):
     # next request's first, with ragged contexts
     dict(n=[321, 200, 290], ctx=[1024, 700, 1000], nq=32, nkv=8, tree="ddtree"),
     dict(n=[129, 100, 64], ctx=[4096, 4000, 1500], nq=32, nkv=8, tree="random"),
+    dict(n=[513], ctx=[1024], nq=64, nkv=8, tree="ddtree"),                              # streamed, 8 heads per KV head
+    dict(n=[257, 180, 97], ctx=[1536, 900, 1400], nq=16, nkv=16, tree="random"),      # streamed across requests, MHA
 ])
 def test_tree_attention_matches_oracle(case):
     rng = np.random.default_rng(sum(case["n"]) * 7 + sum(case["ctx"]) + case["nq"])
